@@ -68,6 +68,15 @@ def _take(a, idx) -> np.ndarray:
     return np.asarray(a)[idx].astype(np.float64)
 
 
+def _take_col(a, idx, col: int) -> np.ndarray:
+    """float64 entries a[idx, col] of a numpy array or CPU torch tensor."""
+    idx = np.asarray(idx, dtype=np.int64)
+    if hasattr(a, "detach"):
+        import torch
+        return a[:, col].index_select(0, torch.from_numpy(idx)).double().numpy()
+    return np.asarray(a)[idx, col].astype(np.float64)
+
+
 def validate(coords: np.ndarray, shape) -> None:
     """Raise ValueError for coordinates outside [0, B) x [0, X) x [0, Y) x [0, Z)."""
     coords = np.asarray(coords)
@@ -363,5 +372,5 @@ def wgrad_entries(feats, dout, nmap, entries) -> np.ndarray:
             cache[k] = pairs(nmap, k)
         I, J = cache[k]
         if I.size:
-            out[t] = float(np.dot(_take(feats, J)[:, a], _take(dout, I)[:, c]))
+            out[t] = float(np.dot(_take_col(feats, J, a), _take_col(dout, I, c)))
     return out

@@ -1,0 +1,227 @@
+"""Thin ctypes binding of libssc (include/ssc.h): argument marshalling only.
+
+Every step of the convolution runs in the HIP library.  torch supplies device
+memory and the current stream; nothing here computes on the host or falls back
+to another implementation.  If libssc.so is missing the calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libssc.so")
+_lib = None
+
+SSC_OK = 0
+STATUS_NAMES = {0: "SSC_OK", 1: "SSC_ERR_INVALID_ARG", 2: "SSC_ERR_UNSUPPORTED", 3: "SSC_ERR_WORKSPACE",
+                4: "SSC_ERR_HIP", 5: "SSC_ERR_COORD_RANGE", 6: "SSC_ERR_DUPLICATE", 7: "SSC_ERR_HASH_FULL"}
+DTYPE_CODE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+
+_VP, _I64, _I32, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+SIGNATURES = {
+    "ssc_plan_bytes": (_SZ, [_I64, _I32, _I32, _I32, _I32, _I32]),
+    "ssc_build_neighbor_map": (ctypes.c_int, [_VP, _I64, _I32, _I32, _I32, _I32, _I32, _VP, _VP, _VP, _SZ, _VP]),
+    "ssc_plan_status": (ctypes.c_int, [_VP, _VP, ctypes.POINTER(_I32)]),
+    "ssc_plan_pair_counts": (ctypes.c_int, [_VP, _VP, ctypes.POINTER(_I64)]),
+    "ssc_conv_workspace_bytes": (_SZ, [_I64, _I32, _I32, _I32]),
+    "ssc_subm_conv3d_fwd": (ctypes.c_int, [_VP, _VP, _VP, _I64, _I32, _I32, _I32, _VP, _VP, _VP, _VP, _VP, _SZ, _VP]),
+    "ssc_subm_conv3d_bwd": (ctypes.c_int, [_VP, _VP, _VP, _I64, _I32, _I32, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                                           _SZ, _VP]),
+    "ssc_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+}
+
+
+class SSCError(RuntimeError):
+    def __init__(self, func: str, code: int):
+        self.code = code
+        super().__init__(f"{func} failed: {STATUS_NAMES.get(code, code)} ({status_string(code)})")
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libssc; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"libssc.so not built at {_LIB_PATH}: run __graft_entry__.build()")
+        l = ctypes.CDLL(_LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            f = getattr(l, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = l
+    return _lib
+
+
+def status_string(code: int) -> str:
+    return lib().ssc_status_string(int(code)).decode()
+
+
+def _check(func: str, code: int) -> None:
+    if code != SSC_OK:
+        raise SSCError(func, code)
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype: torch.dtype, shape: tuple, device: torch.device) -> None:
+    if t.dtype != dtype or tuple(t.shape) != tuple(shape) or t.device != device or not t.is_contiguous():
+        raise ValueError(f"{name}: expected contiguous {dtype} {tuple(shape)} on {device}, "
+                         f"got {t.dtype} {tuple(t.shape)} on {t.device}")
+
+
+# ---------------------------------------------------------------------------
+# plan
+# ---------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class Plan:
+    """Neighbour map, permutation and neighbour cache of one coordinate set."""
+    nmap: torch.Tensor      # [n, 27] uint32 (stored as int32 bits)
+    perm: torch.Tensor      # [n] int32
+    buf: torch.Tensor       # plan buffer (uint8)
+    n: int
+    shape: tuple
+    key_bits: int
+
+    @property
+    def device(self) -> torch.device:
+        return self.buf.device
+
+
+def plan_bytes(n: int, shape, key_bits: int = 0) -> int:
+    B, X, Y, Z = (int(s) for s in shape)
+    return int(lib().ssc_plan_bytes(int(n), B, X, Y, Z, int(key_bits)))
+
+
+def build_neighbor_map(coords: torch.Tensor, shape, key_bits: int = 0, check: bool = True) -> Plan:
+    """ssc_build_neighbor_map on a device int32 [n, 4] coordinate tensor; raises on any error."""
+    dev = coords.device
+    n = int(coords.shape[0])
+    _need(coords, "coords", torch.int32, (n, 4), dev)
+    nbytes = plan_bytes(n, shape, key_bits)
+    if nbytes == 0:
+        raise SSCError("ssc_plan_bytes", 1)
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    nmap = torch.empty((n, 27), dtype=torch.int32, device=dev)
+    perm = torch.empty((n,), dtype=torch.int32, device=dev)
+    B, X, Y, Z = (int(s) for s in shape)
+    _check("ssc_build_neighbor_map",
+           lib().ssc_build_neighbor_map(_ptr(coords), n, B, X, Y, Z, int(key_bits), _ptr(nmap), _ptr(perm),
+                                        _ptr(buf), nbytes, _stream(dev)))
+    plan = Plan(nmap, perm, buf, n, tuple(int(s) for s in shape), int(key_bits))
+    if check:
+        st = plan_status(plan)
+        if st != SSC_OK:
+            raise SSCError("ssc_build_neighbor_map (device)", st)
+    return plan
+
+
+def plan_status(plan: Plan) -> int:
+    out = ctypes.c_int32(-1)
+    _check("ssc_plan_status", lib().ssc_plan_status(_ptr(plan.buf), _stream(plan.device), ctypes.byref(out)))
+    return int(out.value)
+
+
+def plan_pair_counts(plan: Plan) -> list[int]:
+    arr = (ctypes.c_int64 * 27)()
+    _check("ssc_plan_pair_counts", lib().ssc_plan_pair_counts(_ptr(plan.buf), _stream(plan.device), arr))
+    return [int(v) for v in arr]
+
+
+# ---------------------------------------------------------------------------
+# convolution
+# ---------------------------------------------------------------------------
+
+def conv_workspace_bytes(n: int, ci: int, co: int, dtype: torch.dtype) -> int:
+    return int(lib().ssc_conv_workspace_bytes(int(n), int(ci), int(co), DTYPE_CODE[dtype]))
+
+
+def workspace(plan: Plan, ci: int, co: int, dtype: torch.dtype) -> torch.Tensor:
+    nbytes = conv_workspace_bytes(plan.n, ci, co, dtype)
+    if nbytes == 0:
+        raise SSCError("ssc_conv_workspace_bytes", 2)
+    return torch.empty(nbytes, dtype=torch.uint8, device=plan.device)
+
+
+def subm_conv3d_fwd(plan: Plan, feats: torch.Tensor, weight: torch.Tensor, bias: torch.Tensor | None = None,
+                    out: torch.Tensor | None = None, ws: torch.Tensor | None = None) -> torch.Tensor:
+    dev, dt, n = plan.device, feats.dtype, plan.n
+    ci, co = int(weight.shape[1]), int(weight.shape[2])
+    _need(feats, "feats", dt, (n, ci), dev)
+    _need(weight, "weight", dt, (27, ci, co), dev)
+    if bias is not None:
+        _need(bias, "bias", dt, (co,), dev)
+    if out is None:
+        out = torch.empty((n, co), dtype=dt, device=dev)
+    _need(out, "out", dt, (n, co), dev)
+    if ws is None:
+        ws = workspace(plan, ci, co, dt)
+    if dt not in DTYPE_CODE:
+        raise SSCError("ssc_subm_conv3d_fwd", 2)
+    _check("ssc_subm_conv3d_fwd",
+           lib().ssc_subm_conv3d_fwd(_ptr(plan.buf), _ptr(plan.nmap), _ptr(plan.perm), n, ci, co, DTYPE_CODE[dt],
+                                     _ptr(feats), _ptr(weight), _ptr(bias), _ptr(out), _ptr(ws), ws.numel(),
+                                     _stream(dev)))
+    return out
+
+
+def subm_conv3d_bwd(plan: Plan, feats: torch.Tensor, weight: torch.Tensor, dout: torch.Tensor,
+                    need_dfeats: bool = True, need_dweight: bool = True, need_dbias: bool = True,
+                    ws: torch.Tensor | None = None, outs: tuple | None = None):
+    """Returns (dfeats, dweight, dbias); entries not asked for are None."""
+    dev, dt, n = plan.device, dout.dtype, plan.n
+    ci, co = int(weight.shape[1]), int(weight.shape[2])
+    _need(feats, "feats", dt, (n, ci), dev)
+    _need(weight, "weight", dt, (27, ci, co), dev)
+    _need(dout, "dout", dt, (n, co), dev)
+    if outs is not None:
+        dX, dW, db = outs
+    else:
+        dX = torch.empty((n, ci), dtype=dt, device=dev) if need_dfeats else None
+        dW = torch.empty((27, ci, co), dtype=dt, device=dev) if need_dweight else None
+        db = torch.empty((co,), dtype=dt, device=dev) if need_dbias else None
+    if ws is None:
+        ws = workspace(plan, ci, co, dt)
+    _check("ssc_subm_conv3d_bwd",
+           lib().ssc_subm_conv3d_bwd(_ptr(plan.buf), _ptr(plan.nmap), _ptr(plan.perm), n, ci, co, DTYPE_CODE[dt],
+                                     _ptr(feats), _ptr(weight), _ptr(dout), _ptr(dX), _ptr(dW), _ptr(db),
+                                     _ptr(ws), ws.numel(), _stream(dev)))
+    return dX, dW, db
+
+
+class SubmConv3dFunction(torch.autograd.Function):
+    """autograd wrapper: forward = ssc_subm_conv3d_fwd, backward = ssc_subm_conv3d_bwd."""
+
+    @staticmethod
+    def forward(ctx, feats, weight, bias, plan):
+        ctx.plan = plan
+        ctx.has_bias = bias is not None
+        ctx.save_for_backward(feats, weight)
+        return subm_conv3d_fwd(plan, feats.contiguous(), weight.contiguous(),
+                               None if bias is None else bias.contiguous())
+
+    @staticmethod
+    def backward(ctx, dout):
+        feats, weight = ctx.saved_tensors
+        dX, dW, db = subm_conv3d_bwd(ctx.plan, feats, weight, dout.contiguous(),
+                                     need_dfeats=ctx.needs_input_grad[0], need_dweight=ctx.needs_input_grad[1],
+                                     need_dbias=ctx.has_bias and ctx.needs_input_grad[2])
+        return dX, dW, db, None
+
+
+def subm_conv3d(feats: torch.Tensor, plan: Plan, weight: torch.Tensor, bias: torch.Tensor | None = None):
+    """Differentiable submanifold convolution over a built plan."""
+    return SubmConv3dFunction.apply(feats, weight, bias, plan)

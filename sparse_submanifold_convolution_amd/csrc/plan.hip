@@ -1,0 +1,612 @@
+// Neighbour-cache build for the 3x3x3 submanifold convolution on gfx950.
+//
+// What the FlexGEMM pages name for this stage (contributor report, section
+// two: the kernels.cuda.hash, kernels.cuda.serialize and kernels.cuda.spconv
+// rows of the module table, and "how one call flows through the modules"):
+// a coordinate hashmap (insert, then lookup), the submanifold neighbour map,
+// z-order codes, and the masked-implicit-GEMM preprocessing that orders rows
+// (sorted_idx) so that tiles of rows share their valid offsets.
+//
+// Kernels, in launch order:
+//   plan_init       header fields, status word, pair counters
+//   fill_u32/u64    empty hash slots (all ones)
+//   hash_insert     coordinate check, key packing, open-addressing insert with
+//                   atomicCAS on 32- or 64-bit keys; value = row index
+//   probe           27 lookups per voxel (bounds checked per axis before a key
+//                   is packed, so no off-grid neighbour can alias a real one);
+//                   writes nmap rows through LDS so the stores coalesce, and the
+//                   64-bit sort key (mask << zbits) | zorder
+//   radix_hist /    stable LSD radix sort, 8 bits a pass, wave64 ballots rank
+//   radix_scatter   equal digits; the last pass writes perm and sorted masks
+//   pair_count /    per-offset lists of (i, nmap[i][k]) in increasing i, built
+//   pair_scatter    with block counts, a device-wide scan and a stable scatter
+//   scan_*          device-wide exclusive scan of uint32 (three kernels)
+
+#include <hip/hip_runtime.h>
+
+#include "ssc_internal.h"
+
+namespace ssc {
+
+// ---------------------------------------------------------------------------
+// small device helpers
+// ---------------------------------------------------------------------------
+
+// MurmurHash3 finalisers (Austin Appleby, public domain): full avalanche of the
+// packed coordinate key before it is masked to a table slot.
+__device__ __forceinline__ uint32_t mix_hash(uint32_t h) {
+  h ^= h >> 16;
+  h *= 0x85ebca6bu;
+  h ^= h >> 13;
+  h *= 0xc2b2ae35u;
+  h ^= h >> 16;
+  return h;
+}
+__device__ __forceinline__ uint32_t mix_hash(uint64_t k) {
+  k ^= k >> 33;
+  k *= 0xff51afd7ed558ccdull;
+  k ^= k >> 33;
+  k *= 0xc4ceb9fe1a85ec53ull;
+  k ^= k >> 33;
+  return uint32_t(k);
+}
+
+template <typename KeyT>
+__device__ __forceinline__ KeyT empty_key() {
+  return KeyT(~KeyT(0));
+}
+
+__device__ __forceinline__ uint64_t lanemask_lt() {
+  const unsigned lane = __lane_id();
+  return lane == 0 ? 0ull : (~0ull >> (64 - lane));
+}
+
+__device__ __forceinline__ bool coord_ok(int b, int x, int y, int z, int B, int X, int Y, int Z) {
+  return b >= 0 && b < B && x >= 0 && x < X && y >= 0 && y < Y && z >= 0 && z < Z;
+}
+
+__device__ __forceinline__ uint64_t pack_key(int b, int x, int y, int z, int X, int Y, int Z) {
+  return ((uint64_t(b) * uint64_t(X) + uint64_t(x)) * uint64_t(Y) + uint64_t(y)) * uint64_t(Z) +
+         uint64_t(z);
+}
+
+// interleave the low `bits` bits of x, y, z: triplet (x, y, z) per bit, x highest
+__device__ __forceinline__ uint64_t zorder(uint32_t x, uint32_t y, uint32_t z, int bits) {
+  uint64_t code = 0;
+  for (int b = 0; b < bits; ++b) {
+    code |= uint64_t((x >> b) & 1u) << (3 * b + 2);
+    code |= uint64_t((y >> b) & 1u) << (3 * b + 1);
+    code |= uint64_t((z >> b) & 1u) << (3 * b);
+  }
+  return code;
+}
+
+// ---------------------------------------------------------------------------
+// device-wide exclusive scan of uint32
+// ---------------------------------------------------------------------------
+
+// exclusive scan of one value per thread across the workgroup; returns the total
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* lds_waves,
+                                                         uint32_t* out_excl) {
+  const int lane = __lane_id();
+  const int wave = threadIdx.x / 64;
+  const int nwaves = blockDim.x / 64;
+  uint32_t incl = v;
+  for (int d = 1; d < 64; d <<= 1) {
+    uint32_t t = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += t;
+  }
+  if (lane == 63) lds_waves[wave] = incl;
+  __syncthreads();
+  uint32_t before = 0, total = 0;
+  for (int w = 0; w < nwaves; ++w) {
+    uint32_t c = lds_waves[w];
+    if (w < wave) before += c;
+    total += c;
+  }
+  *out_excl = before + incl - v;
+  __syncthreads();
+  return total;
+}
+
+__global__ void __launch_bounds__(kScanThreads) scan_reduce(const uint32_t* __restrict__ data,
+                                                            int64_t len, uint32_t* __restrict__ tmp) {
+  __shared__ uint32_t waves[kScanThreads / 64];
+  const int64_t base = int64_t(blockIdx.x) * kScanBlock;
+  uint32_t s = 0;
+  for (int e = 0; e < kScanItems; ++e) {
+    int64_t idx = base + int64_t(e) * kScanThreads + threadIdx.x;
+    if (idx < len) s += data[idx];
+  }
+  uint32_t excl;
+  uint32_t total = block_exclusive_scan(s, waves, &excl);
+  if (threadIdx.x == 0) tmp[blockIdx.x] = total;
+}
+
+// one workgroup: exclusive scan of the block sums, in chunks with a carry
+__global__ void __launch_bounds__(kScanThreads) scan_top(uint32_t* __restrict__ tmp, int64_t nb) {
+  __shared__ uint32_t waves[kScanThreads / 64];
+  uint32_t carry = 0;
+  for (int64_t c0 = 0; c0 < nb; c0 += kScanThreads) {
+    int64_t idx = c0 + threadIdx.x;
+    uint32_t v = idx < nb ? tmp[idx] : 0u;
+    uint32_t excl;
+    uint32_t total = block_exclusive_scan(v, waves, &excl);
+    if (idx < nb) tmp[idx] = carry + excl;
+    carry += total;
+  }
+}
+
+__global__ void __launch_bounds__(kScanThreads) scan_apply(uint32_t* __restrict__ data, int64_t len,
+                                                           const uint32_t* __restrict__ tmp) {
+  __shared__ uint32_t waves[kScanThreads / 64];
+  const int64_t base = int64_t(blockIdx.x) * kScanBlock + int64_t(threadIdx.x) * kScanItems;
+  uint32_t v[kScanItems];
+  uint32_t s = 0;
+#pragma unroll
+  for (int e = 0; e < kScanItems; ++e) {
+    int64_t idx = base + e;
+    v[e] = idx < len ? data[idx] : 0u;
+    s += v[e];
+  }
+  uint32_t excl;
+  block_exclusive_scan(s, waves, &excl);
+  uint32_t run = tmp[blockIdx.x] + excl;
+#pragma unroll
+  for (int e = 0; e < kScanItems; ++e) {
+    int64_t idx = base + e;
+    if (idx < len) data[idx] = run;
+    run += v[e];
+  }
+}
+
+static void launch_scan(uint32_t* data, int64_t len, uint32_t* tmp, hipStream_t s) {
+  if (len <= 0) return;
+  const int64_t nb = (len + kScanBlock - 1) / kScanBlock;
+  scan_reduce<<<dim3(unsigned(nb)), dim3(kScanThreads), 0, s>>>(data, len, tmp);
+  scan_top<<<dim3(1), dim3(kScanThreads), 0, s>>>(tmp, nb);
+  scan_apply<<<dim3(unsigned(nb)), dim3(kScanThreads), 0, s>>>(data, len, tmp);
+}
+
+// ---------------------------------------------------------------------------
+// header, fills, hash insert, probe
+// ---------------------------------------------------------------------------
+
+__global__ void plan_init(PlanHeader* h, int64_t n, int B, int X, int Y, int Z, int key_bits,
+                          int zbits, uint64_t capacity) {
+  if (threadIdx.x == 0) {
+    h->magic = kPlanMagic;
+    h->status_bits = 0;
+    h->n = n;
+    h->dims[0] = B;
+    h->dims[1] = X;
+    h->dims[2] = Y;
+    h->dims[3] = Z;
+    h->key_bits = key_bits;
+    h->zbits = zbits;
+    h->capacity = capacity;
+  }
+  if (threadIdx.x < 32) {
+    h->pair_count[threadIdx.x] = 0;
+    h->pair_off[threadIdx.x] = 0;
+  }
+}
+
+template <typename T>
+__global__ void fill_kernel(T* __restrict__ p, int64_t count, T v) {
+  int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t stride = int64_t(gridDim.x) * blockDim.x;
+  for (; i < count; i += stride) p[i] = v;
+}
+
+template <typename KeyT>
+__global__ void __launch_bounds__(256) hash_insert(const int4* __restrict__ coords, int64_t n,
+                                                   int B, int X, int Y, int Z,
+                                                   KeyT* __restrict__ keys, uint32_t* __restrict__ vals,
+                                                   uint64_t capacity, uint32_t* __restrict__ status) {
+  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const int4 c = coords[i];
+  if (!coord_ok(c.x, c.y, c.z, c.w, B, X, Y, Z)) {
+    atomicOr(status, kBitCoordRange);
+    return;
+  }
+  const KeyT key = KeyT(pack_key(c.x, c.y, c.z, c.w, X, Y, Z));
+  const uint64_t mask = capacity - 1;
+  uint64_t slot = mix_hash(key) & mask;
+  for (uint64_t probe = 0; probe < capacity; ++probe) {
+    KeyT prev = atomicCAS(&keys[slot], empty_key<KeyT>(), key);
+    if (prev == empty_key<KeyT>()) {
+      vals[slot] = uint32_t(i);
+      return;
+    }
+    if (prev == key) {
+      atomicOr(status, kBitDuplicate);
+      return;
+    }
+    slot = (slot + 1) & mask;
+  }
+  atomicOr(status, kBitHashFull);
+}
+
+template <typename KeyT>
+__device__ __forceinline__ uint32_t hash_lookup(const KeyT* __restrict__ keys,
+                                                const uint32_t* __restrict__ vals, uint64_t capacity,
+                                                KeyT key) {
+  const uint64_t mask = capacity - 1;
+  uint64_t slot = mix_hash(key) & mask;
+  for (uint64_t probe = 0; probe < capacity; ++probe) {
+    const KeyT k = keys[slot];
+    if (k == key) return vals[slot];
+    if (k == empty_key<KeyT>()) return kSentinel;
+    slot = (slot + 1) & mask;
+  }
+  return kSentinel;
+}
+
+// One thread per voxel: 27 probes, the neighbour mask, and the sort key.
+template <typename KeyT>
+__global__ void __launch_bounds__(256) probe(const int4* __restrict__ coords, int64_t n, int B, int X,
+                                             int Y, int Z, const KeyT* __restrict__ keys,
+                                             const uint32_t* __restrict__ vals, uint64_t capacity,
+                                             uint32_t* __restrict__ nmap, uint64_t* __restrict__ sort_key,
+                                             int axis_bits, int zbits) {
+  __shared__ uint32_t rows[256 * kV];
+  const int64_t row0 = int64_t(blockIdx.x) * 256;
+  const int64_t i = row0 + threadIdx.x;
+  if (i < n) {
+    const int4 c = coords[i];
+    const bool ok = coord_ok(c.x, c.y, c.z, c.w, B, X, Y, Z);
+    uint32_t mask = 0;
+#pragma unroll 1
+    for (int k = 0; k < kV; ++k) {
+      const int px = c.y + k / 9 - 1;
+      const int py = c.z + (k / 3) % 3 - 1;
+      const int pz = c.w + k % 3 - 1;
+      uint32_t j = kSentinel;
+      if (ok && px >= 0 && px < X && py >= 0 && py < Y && pz >= 0 && pz < Z) {
+        j = hash_lookup<KeyT>(keys, vals, capacity, KeyT(pack_key(c.x, px, py, pz, X, Y, Z)));
+      }
+      rows[threadIdx.x * kV + k] = j;
+      if (j != kSentinel) mask |= 1u << k;
+    }
+    uint64_t key = 0;
+    if (ok) {
+      const uint64_t z = (uint64_t(uint32_t(c.x)) << (3 * axis_bits)) |
+                         zorder(uint32_t(c.y), uint32_t(c.z), uint32_t(c.w), axis_bits);
+      key = (uint64_t(mask) << zbits) | z;
+    }
+    sort_key[i] = key;
+  }
+  __syncthreads();
+  const int64_t rows_here = (n - row0) < 256 ? (n - row0) : 256;
+  const int64_t words = rows_here * kV;
+  uint32_t* dst = nmap + row0 * kV;
+  for (int64_t e = threadIdx.x; e < words; e += 256) dst[e] = rows[e];
+}
+
+// ---------------------------------------------------------------------------
+// stable LSD radix sort of 64-bit keys with a 32-bit payload
+// ---------------------------------------------------------------------------
+
+__global__ void __launch_bounds__(kSortThreads) radix_hist(const uint64_t* __restrict__ keys, int64_t n,
+                                                           int shift, uint32_t* __restrict__ hist,
+                                                           int64_t nblk) {
+  __shared__ uint32_t cnt[256];
+  cnt[threadIdx.x] = 0;
+  __syncthreads();
+  const int64_t base = int64_t(blockIdx.x) * kSortBlockKeys;
+  for (int q = 0; q < kSortItems; ++q) {
+    const int64_t idx = base + int64_t(q) * kSortThreads + threadIdx.x;
+    if (idx < n) atomicAdd(&cnt[(keys[idx] >> shift) & 255u], 1u);
+  }
+  __syncthreads();
+  hist[int64_t(threadIdx.x) * nblk + blockIdx.x] = cnt[threadIdx.x];
+  if (blockIdx.x == 0 && threadIdx.x == 0) hist[256 * nblk] = 0;
+}
+
+// Keys of one workgroup are taken in rounds of 256 in index order; inside a
+// round, lanes with equal digits are ranked by a 64-lane ballot match and waves
+// are ranked by their counts, so equal digits keep their input order.
+__global__ void __launch_bounds__(kSortThreads)
+    radix_scatter(const uint64_t* __restrict__ keys_in, const uint32_t* __restrict__ vals_in,
+                  uint64_t* __restrict__ keys_out, uint32_t* __restrict__ vals_out, int64_t n, int shift,
+                  const uint32_t* __restrict__ offsets, int64_t nblk, int first, int last,
+                  int32_t* __restrict__ perm, uint32_t* __restrict__ smask, int zbits) {
+  __shared__ uint32_t base[256];
+  __shared__ uint32_t wcnt[kSortThreads / 64][256];
+  const int tid = threadIdx.x;
+  const int wave = tid / 64;
+  base[tid] = offsets[int64_t(tid) * nblk + blockIdx.x];
+  const int64_t blk0 = int64_t(blockIdx.x) * kSortBlockKeys;
+  for (int q = 0; q < kSortItems; ++q) {
+    const int64_t idx = blk0 + int64_t(q) * kSortThreads + tid;
+    const bool valid = idx < n;
+    const uint64_t key = valid ? keys_in[idx] : 0ull;
+    const uint32_t val = valid ? (first ? uint32_t(idx) : vals_in[idx]) : 0u;
+    const uint32_t d = uint32_t(key >> shift) & 255u;
+#pragma unroll
+    for (int w = 0; w < kSortThreads / 64; ++w) wcnt[w][tid] = 0;
+    __syncthreads();
+    uint64_t peers = __ballot(valid);
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      const bool bit = (d >> b) & 1u;
+      const uint64_t ones = __ballot(bit);
+      peers &= bit ? ones : ~ones;
+    }
+    const uint32_t rank = __popcll(peers & lanemask_lt());
+    if (valid && rank == 0) wcnt[wave][d] = __popcll(peers);
+    __syncthreads();
+    if (valid) {
+      uint32_t pos = base[d] + rank;
+      for (int w = 0; w < wave; ++w) pos += wcnt[w][d];
+      if (last) {
+        perm[pos] = int32_t(val);
+        smask[pos] = uint32_t(key >> zbits);
+      } else {
+        keys_out[pos] = key;
+        vals_out[pos] = val;
+      }
+    }
+    __syncthreads();
+    uint32_t add = 0;
+#pragma unroll
+    for (int w = 0; w < kSortThreads / 64; ++w) add += wcnt[w][tid];
+    base[tid] += add;
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// per-offset pair lists
+// ---------------------------------------------------------------------------
+
+__global__ void __launch_bounds__(256) pair_count(const uint32_t* __restrict__ nmap, int64_t n,
+                                                  uint32_t* __restrict__ pcnt, int64_t pblk) {
+  __shared__ uint32_t cnt[32];
+  if (threadIdx.x < 32) cnt[threadIdx.x] = 0;
+  __syncthreads();
+  const int64_t row0 = int64_t(blockIdx.x) * kPairRows;
+  uint32_t local[kV];
+#pragma unroll
+  for (int k = 0; k < kV; ++k) local[k] = 0;
+  for (int q = 0; q < kPairRows / 256; ++q) {
+    const int64_t row = row0 + q * 256 + threadIdx.x;
+    if (row < n) {
+      const uint32_t* r = nmap + row * kV;
+#pragma unroll
+      for (int k = 0; k < kV; ++k) local[k] += r[k] != kSentinel ? 1u : 0u;
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < kV; ++k) {
+    uint32_t v = local[k];
+    for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
+    if (__lane_id() == 0) atomicAdd(&cnt[k], v);
+  }
+  __syncthreads();
+  if (threadIdx.x < kV) pcnt[int64_t(threadIdx.x) * pblk + blockIdx.x] = cnt[threadIdx.x];
+  if (blockIdx.x == 0 && threadIdx.x == 0) pcnt[kV * pblk] = 0;
+}
+
+__global__ void pair_offsets(const uint32_t* __restrict__ pcnt, int64_t pblk, PlanHeader* h) {
+  const int k = threadIdx.x;
+  if (k <= kV) h->pair_off[k] = pcnt[int64_t(k) * pblk];
+  if (k < kV) h->pair_count[k] = pcnt[int64_t(k + 1) * pblk] - pcnt[int64_t(k) * pblk];
+}
+
+__global__ void __launch_bounds__(256) pair_scatter(const uint32_t* __restrict__ nmap, int64_t n,
+                                                    const uint32_t* __restrict__ pcnt, int64_t pblk,
+                                                    uint32_t* __restrict__ pair_i,
+                                                    uint32_t* __restrict__ pair_j) {
+  __shared__ uint32_t base[32];
+  __shared__ uint32_t wc[kV][4];
+  const int tid = threadIdx.x;
+  const int wave = tid / 64;
+  if (tid < kV) base[tid] = pcnt[int64_t(tid) * pblk + blockIdx.x];
+  __syncthreads();
+  const int64_t row0 = int64_t(blockIdx.x) * kPairRows;
+  for (int q = 0; q < kPairRows / 256; ++q) {
+    const int64_t row = row0 + q * 256 + tid;
+    const bool in = row < n;
+    uint32_t j[kV];
+    uint32_t rank[kV];
+#pragma unroll
+    for (int k = 0; k < kV; ++k) {
+      j[k] = in ? nmap[row * kV + k] : kSentinel;
+      const uint64_t b = __ballot(j[k] != kSentinel);
+      rank[k] = __popcll(b & lanemask_lt());
+      if (__lane_id() == 0) wc[k][wave] = __popcll(b);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kV; ++k) {
+      if (j[k] != kSentinel) {
+        uint32_t pos = base[k] + rank[k];
+        for (int w = 0; w < wave; ++w) pos += wc[k][w];
+        pair_i[pos] = uint32_t(row);
+        pair_j[pos] = j[k];
+      }
+    }
+    __syncthreads();
+    if (tid < kV) base[tid] += wc[tid][0] + wc[tid][1] + wc[tid][2] + wc[tid][3];
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+
+static bool grid_ok(int32_t B, int32_t X, int32_t Y, int32_t Z) {
+  return B >= 1 && X >= 1 && Y >= 1 && Z >= 1 && X <= (1 << 20) && Y <= (1 << 20) &&
+         Z <= (1 << 20) && B <= (1 << 20);
+}
+
+static int effective_key_bits(int32_t B, int32_t X, int32_t Y, int32_t Z, int32_t key_bits) {
+  const unsigned __int128 vol = (unsigned __int128)(uint64_t)B * (uint64_t)X * (uint64_t)Y * (uint64_t)Z;
+  const bool fits32 = vol <= (unsigned __int128)0xFFFFFFFFu;
+  if (key_bits == 0) return fits32 ? 32 : 64;
+  if (key_bits == 32) return fits32 ? 32 : -1;
+  if (key_bits == 64) return vol < ((unsigned __int128)1 << 64) ? 64 : -1;
+  return -1;
+}
+
+static void sort_key_bits(int32_t B, int32_t X, int32_t Y, int32_t Z, int* axis_bits, int* zbits) {
+  int m = X;
+  if (Y > m) m = Y;
+  if (Z > m) m = Z;
+  *axis_bits = ceil_log2_u64(uint64_t(m));
+  *zbits = 3 * *axis_bits + ceil_log2_u64(uint64_t(B));
+}
+
+static inline unsigned grid1d(int64_t work, int threads) {
+  int64_t b = (work + threads - 1) / threads;
+  return unsigned(b < 1 ? 1 : b);
+}
+
+}  // namespace ssc
+
+using namespace ssc;
+
+extern "C" size_t ssc_plan_bytes(int64_t n, int32_t B, int32_t X, int32_t Y, int32_t Z,
+                                 int32_t key_bits) {
+  if (n < 0 || n > SSC_MAX_VOXELS || !grid_ok(B, X, Y, Z)) return 0;
+  const int kb = effective_key_bits(B, X, Y, Z, key_bits);
+  if (kb < 0) return 0;
+  int axis_bits, zbits;
+  sort_key_bits(B, X, Y, Z, &axis_bits, &zbits);
+  if (kV + zbits > 64) return 0;
+  return plan_layout(n, kb).total;
+}
+
+extern "C" int ssc_build_neighbor_map(const int32_t* coords, int64_t n, int32_t B, int32_t X, int32_t Y,
+                                      int32_t Z, int32_t key_bits, uint32_t* nmap, int32_t* perm,
+                                      void* plan, size_t plan_bytes, void* stream) {
+  if (n < 0 || n > SSC_MAX_VOXELS || !plan) return SSC_ERR_INVALID_ARG;
+  if (n > 0 && (!coords || !nmap || !perm)) return SSC_ERR_INVALID_ARG;
+  if (!aligned16(plan) || (n > 0 && (!aligned16(coords) || !aligned16(nmap) || !aligned16(perm))))
+    return SSC_ERR_INVALID_ARG;
+  if (!grid_ok(B, X, Y, Z)) return SSC_ERR_INVALID_ARG;
+  if (key_bits != 0 && key_bits != 32 && key_bits != 64) return SSC_ERR_INVALID_ARG;
+  const int kb = effective_key_bits(B, X, Y, Z, key_bits);
+  if (kb < 0) return SSC_ERR_UNSUPPORTED;
+  int axis_bits, zbits;
+  sort_key_bits(B, X, Y, Z, &axis_bits, &zbits);
+  if (kV + zbits > 64) return SSC_ERR_UNSUPPORTED;
+  const PlanLayout L = plan_layout(n, kb);
+  if (plan_bytes < L.total) return SSC_ERR_WORKSPACE;
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* base = static_cast<char*>(plan);
+  PlanHeader* h = reinterpret_cast<PlanHeader*>(base + L.header);
+  (void)hipGetLastError();
+  plan_init<<<1, 64, 0, s>>>(h, n, B, X, Y, Z, kb, zbits, L.capacity);
+  if (n == 0) return hipGetLastError() == hipSuccess ? SSC_OK : SSC_ERR_HIP;
+
+  uint32_t* smask = reinterpret_cast<uint32_t*>(base + L.smask);
+  uint32_t* pair_i = reinterpret_cast<uint32_t*>(base + L.pair_i);
+  uint32_t* pair_j = reinterpret_cast<uint32_t*>(base + L.pair_j);
+  uint32_t* hvals = reinterpret_cast<uint32_t*>(base + L.hvals);
+  uint64_t* key0 = reinterpret_cast<uint64_t*>(base + L.key0);
+  uint64_t* key1 = reinterpret_cast<uint64_t*>(base + L.key1);
+  uint32_t* val0 = reinterpret_cast<uint32_t*>(base + L.val0);
+  uint32_t* val1 = reinterpret_cast<uint32_t*>(base + L.val1);
+  uint32_t* hist = reinterpret_cast<uint32_t*>(base + L.hist);
+  uint32_t* pcnt = reinterpret_cast<uint32_t*>(base + L.pcnt);
+  uint32_t* scan_tmp = reinterpret_cast<uint32_t*>(base + L.scan_tmp);
+  const int4* c4 = reinterpret_cast<const int4*>(coords);
+
+  const unsigned fill_blocks = 1024;
+  if (kb == 64) {
+    uint64_t* hkeys = reinterpret_cast<uint64_t*>(base + L.hkeys);
+    fill_kernel<uint64_t><<<fill_blocks, 256, 0, s>>>(hkeys, int64_t(L.capacity), ~0ull);
+    hash_insert<uint64_t><<<grid1d(n, 256), 256, 0, s>>>(c4, n, B, X, Y, Z, hkeys, hvals, L.capacity,
+                                                         &h->status_bits);
+    probe<uint64_t><<<grid1d(n, 256), 256, 0, s>>>(c4, n, B, X, Y, Z, hkeys, hvals, L.capacity, nmap, key0,
+                                                   axis_bits, zbits);
+  } else {
+    uint32_t* hkeys = reinterpret_cast<uint32_t*>(base + L.hkeys);
+    fill_kernel<uint32_t><<<fill_blocks, 256, 0, s>>>(hkeys, int64_t(L.capacity), ~0u);
+    hash_insert<uint32_t><<<grid1d(n, 256), 256, 0, s>>>(c4, n, B, X, Y, Z, hkeys, hvals, L.capacity,
+                                                         &h->status_bits);
+    probe<uint32_t><<<grid1d(n, 256), 256, 0, s>>>(c4, n, B, X, Y, Z, hkeys, hvals, L.capacity, nmap, key0,
+                                                   axis_bits, zbits);
+  }
+
+  // radix sort over the key's kV + zbits low bits
+  const int bits = kV + zbits;
+  const int passes = (bits + 7) / 8;
+  const int64_t nblk = L.sort_blocks;
+  const uint64_t* kin = key0;
+  const uint32_t* vin = val0;
+  uint64_t* kout = key1;
+  uint32_t* vout = val1;
+  for (int p = 0; p < passes; ++p) {
+    const int shift = 8 * p;
+    radix_hist<<<unsigned(nblk), kSortThreads, 0, s>>>(kin, n, shift, hist, nblk);
+    launch_scan(hist, nblk * 256 + 1, scan_tmp, s);
+    radix_scatter<<<unsigned(nblk), kSortThreads, 0, s>>>(kin, vin, kout, vout, n, shift, hist, nblk,
+                                                           p == 0 ? 1 : 0, p == passes - 1 ? 1 : 0, perm,
+                                                           smask, zbits);
+    const uint64_t* tk = kout;
+    const uint32_t* tv = vout;
+    kout = const_cast<uint64_t*>(kin);
+    vout = const_cast<uint32_t*>(vin);
+    kin = tk;
+    vin = tv;
+  }
+
+  // per-offset pair lists
+  const int64_t pblk = L.pair_blocks;
+  pair_count<<<unsigned(pblk), 256, 0, s>>>(nmap, n, pcnt, pblk);
+  launch_scan(pcnt, pblk * kV + 1, scan_tmp, s);
+  pair_offsets<<<1, 64, 0, s>>>(pcnt, pblk, h);
+  pair_scatter<<<unsigned(pblk), 256, 0, s>>>(nmap, n, pcnt, pblk, pair_i, pair_j);
+
+  return hipGetLastError() == hipSuccess ? SSC_OK : SSC_ERR_HIP;
+}
+
+extern "C" int ssc_plan_status(const void* plan, void* stream, int32_t* status_host) {
+  if (!plan || !status_host) return SSC_ERR_INVALID_ARG;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  PlanHeader h;
+  if (hipStreamSynchronize(s) != hipSuccess) return SSC_ERR_HIP;
+  if (hipMemcpy(&h, plan, sizeof(h), hipMemcpyDeviceToHost) != hipSuccess) return SSC_ERR_HIP;
+  if (h.magic != kPlanMagic) return SSC_ERR_INVALID_ARG;
+  int32_t st = SSC_OK;
+  if (h.status_bits & kBitCoordRange)
+    st = SSC_ERR_COORD_RANGE;
+  else if (h.status_bits & kBitDuplicate)
+    st = SSC_ERR_DUPLICATE;
+  else if (h.status_bits & kBitHashFull)
+    st = SSC_ERR_HASH_FULL;
+  *status_host = st;
+  return SSC_OK;
+}
+
+extern "C" int ssc_plan_pair_counts(const void* plan, void* stream, int64_t* counts_host) {
+  if (!plan || !counts_host) return SSC_ERR_INVALID_ARG;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  PlanHeader h;
+  if (hipStreamSynchronize(s) != hipSuccess) return SSC_ERR_HIP;
+  if (hipMemcpy(&h, plan, sizeof(h), hipMemcpyDeviceToHost) != hipSuccess) return SSC_ERR_HIP;
+  if (h.magic != kPlanMagic) return SSC_ERR_INVALID_ARG;
+  for (int k = 0; k < kV; ++k) counts_host[k] = h.pair_count[k];
+  return SSC_OK;
+}
+
+extern "C" const char* ssc_status_string(int status) {
+  switch (status) {
+    case SSC_OK: return "ok";
+    case SSC_ERR_INVALID_ARG: return "invalid argument";
+    case SSC_ERR_UNSUPPORTED: return "unsupported dtype, channel count or grid";
+    case SSC_ERR_WORKSPACE: return "plan or workspace buffer too small";
+    case SSC_ERR_HIP: return "HIP runtime error";
+    case SSC_ERR_COORD_RANGE: return "coordinate out of range";
+    case SSC_ERR_DUPLICATE: return "duplicate coordinate";
+    case SSC_ERR_HASH_FULL: return "hash table full";
+    default: return "unknown status";
+  }
+}

@@ -1,0 +1,118 @@
+// Internal declarations shared by the libssc translation units: plan layout,
+// constants and small device helpers.  Not part of the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "ssc.h"
+
+namespace ssc {
+
+constexpr uint32_t kSentinel = 0xFFFFFFFFu;
+constexpr int kV = 27;
+constexpr int kCentre = 13;
+constexpr uint32_t kPlanMagic = 0x50435353u;  // "SSCP"
+
+// status bits the device sets in the plan header
+constexpr uint32_t kBitCoordRange = 1u;
+constexpr uint32_t kBitDuplicate = 2u;
+constexpr uint32_t kBitHashFull = 4u;
+
+// radix sort: keys per workgroup of the histogram / scatter kernels
+constexpr int kSortThreads = 256;
+constexpr int kSortItems = 8;
+constexpr int kSortBlockKeys = kSortThreads * kSortItems;
+// pair-list build: rows per workgroup
+constexpr int kPairRows = 1024;
+// device-wide scan: elements per workgroup
+constexpr int kScanThreads = 256;
+constexpr int kScanItems = 16;
+constexpr int kScanBlock = kScanThreads * kScanItems;
+
+struct PlanHeader {
+  uint32_t magic;
+  uint32_t status_bits;
+  int64_t n;
+  int32_t dims[4];
+  int32_t key_bits;
+  int32_t zbits;  // bits of the z-order key (batch + interleaved coordinates)
+  uint64_t capacity;
+  uint32_t pair_count[32];  // [27] used: valid pairs per offset
+  uint32_t pair_off[32];    // [28] used: start of each offset's pair list
+};
+static_assert(sizeof(PlanHeader) <= 4096, "plan header too large");
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+inline int ceil_log2_u64(uint64_t v) {
+  int e = 0;
+  while ((uint64_t(1) << e) < v) ++e;
+  return e;
+}
+
+// Offsets (bytes from the plan base) of every plan region.  The regions the
+// convolution calls read depend on n only and come first.
+struct PlanLayout {
+  size_t header = 0;
+  size_t smask = 0;   // [n] u32: neighbour mask of the row at each sorted position
+  size_t pair_i = 0;  // [27n] u32: pair lists, output row i
+  size_t pair_j = 0;  // [27n] u32: pair lists, input row j = nmap[i][k]
+  // build-only scratch
+  size_t hkeys = 0, hvals = 0, key0 = 0, key1 = 0, val0 = 0, val1 = 0, hist = 0, pcnt = 0,
+         scan_tmp = 0;
+  size_t total = 0;
+  uint64_t capacity = 0;
+  int key_bytes = 4;
+  int64_t sort_blocks = 0;
+  int64_t pair_blocks = 0;
+};
+
+inline PlanLayout conv_layout(int64_t n) {
+  PlanLayout L;
+  size_t off = 4096;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align_up(off + bytes, 256);
+    return o;
+  };
+  L.header = 0;
+  L.smask = take(size_t(n) * 4);
+  L.pair_i = take(size_t(n) * kV * 4);
+  L.pair_j = take(size_t(n) * kV * 4);
+  L.total = off;
+  return L;
+}
+
+inline PlanLayout plan_layout(int64_t n, int key_bits) {
+  PlanLayout L = conv_layout(n);
+  size_t off = L.total;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align_up(off + bytes, 256);
+    return o;
+  };
+  uint64_t want = uint64_t(n) * 2 < 1024 ? 1024 : uint64_t(n) * 2;
+  L.capacity = uint64_t(1) << ceil_log2_u64(want);
+  L.key_bytes = key_bits == 64 ? 8 : 4;
+  L.sort_blocks = (n + kSortBlockKeys - 1) / kSortBlockKeys;
+  L.pair_blocks = (n + kPairRows - 1) / kPairRows;
+  L.hkeys = take(L.capacity * L.key_bytes);
+  L.hvals = take(L.capacity * 4);
+  L.key0 = take(size_t(n) * 8);
+  L.key1 = take(size_t(n) * 8);
+  L.val0 = take(size_t(n) * 4);
+  L.val1 = take(size_t(n) * 4);
+  L.hist = take((size_t(L.sort_blocks) * 256 + 1) * 4);
+  L.pcnt = take((size_t(L.pair_blocks) * kV + 1) * 4);
+  size_t scan_len = size_t(L.sort_blocks) * 256 + 1;
+  if (size_t(L.pair_blocks) * kV + 1 > scan_len) scan_len = size_t(L.pair_blocks) * kV + 1;
+  L.scan_tmp = take(((scan_len + kScanBlock - 1) / kScanBlock + 1) * 4);
+  L.total = off;
+  return L;
+}
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace ssc

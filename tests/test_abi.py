@@ -1,0 +1,102 @@
+"""libssc loads, exports every call include/ssc.h declares, and rejects bad arguments on the host.
+
+No call here reaches the GPU: each one returns before any HIP runtime call.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssc.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    import sparse_submanifold_convolution_amd as ssc
+    return ssc.lib()
+
+
+def declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ssc_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared()
+    for n in ["ssc_build_neighbor_map", "ssc_subm_conv3d_fwd", "ssc_subm_conv3d_bwd", "ssc_plan_bytes",
+              "ssc_plan_status", "ssc_conv_workspace_bytes", "ssc_status_string"]:
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(L):
+    from sparse_submanifold_convolution_amd.binding import SIGNATURES
+    for name in declared():
+        assert hasattr(L, name), name
+        assert name in SIGNATURES, f"binding has no signature for {name}"
+
+
+def test_status_strings(L):
+    for code in range(8):
+        assert L.ssc_status_string(code)
+    assert L.ssc_status_string(99) == b"unknown status"
+
+
+def test_plan_bytes_validation(L):
+    assert L.ssc_plan_bytes(100, 1, 32, 32, 32, 0) > 0
+    assert L.ssc_plan_bytes(-1, 1, 32, 32, 32, 0) == 0
+    assert L.ssc_plan_bytes(100, 0, 32, 32, 32, 0) == 0
+    assert L.ssc_plan_bytes(100, 1, 32, 32, 32, 17) == 0
+    assert L.ssc_plan_bytes((1 << 26) + 1, 1, 32, 32, 32, 0) == 0
+    # 32-bit keys cannot hold a 2 x 2048^3 volume; 64-bit can
+    assert L.ssc_plan_bytes(100, 2, 2048, 2048, 2048, 32) == 0
+    assert L.ssc_plan_bytes(100, 2, 2048, 2048, 2048, 0) > 0
+    assert L.ssc_plan_bytes(100, 1, 1024, 1024, 1024, 64) > L.ssc_plan_bytes(100, 1, 1024, 1024, 1024, 32)
+    assert L.ssc_plan_bytes(0, 1, 1, 1, 1, 0) > 0
+
+
+def test_workspace_bytes_validation(L):
+    assert L.ssc_conv_workspace_bytes(1000, 64, 64, 1) > 0
+    assert L.ssc_conv_workspace_bytes(1000, 24, 64, 1) == 0     # not a multiple of 16
+    assert L.ssc_conv_workspace_bytes(1000, 64, 8, 0) == 0
+    assert L.ssc_conv_workspace_bytes(1000, 64, 64, 3) == 0     # unknown dtype
+    assert L.ssc_conv_workspace_bytes(1000, 8192, 64, 2) == 0   # too wide
+
+
+FAKE = ctypes.c_void_p(0x10000)   # aligned, never dereferenced: every call below fails its host checks first
+
+
+def test_build_rejects_on_host(L):
+    out = L.ssc_build_neighbor_map(None, 10, 1, 8, 8, 8, 0, FAKE, FAKE, FAKE, 1 << 30, None)
+    assert out == 1
+    out = L.ssc_build_neighbor_map(FAKE, 10, 1, 8, 8, 8, 0, FAKE, FAKE, FAKE, 16, None)
+    assert out == 3                                   # plan buffer too small
+    out = L.ssc_build_neighbor_map(FAKE, 10, 1, 8, 8, 8, 48, FAKE, FAKE, FAKE, 1 << 30, None)
+    assert out == 1                                   # key_bits must be 0, 32 or 64
+    out = L.ssc_build_neighbor_map(ctypes.c_void_p(0x10004), 10, 1, 8, 8, 8, 0, FAKE, FAKE, FAKE, 1 << 30, None)
+    assert out == 1                                   # misaligned coords
+    out = L.ssc_build_neighbor_map(FAKE, 10, 2, 2048, 2048, 2048, 32, FAKE, FAKE, FAKE, 1 << 30, None)
+    assert out == 2                                   # volume does not fit 32-bit keys
+
+
+def test_conv_rejects_on_host(L):
+    f = L.ssc_subm_conv3d_fwd
+    assert f(FAKE, FAKE, FAKE, 100, 32, 32, 5, FAKE, FAKE, None, FAKE, FAKE, 1 << 30, None) == 2   # dtype
+    assert f(FAKE, FAKE, FAKE, 100, 20, 32, 0, FAKE, FAKE, None, FAKE, FAKE, 1 << 30, None) == 2   # Ci % 16
+    assert f(FAKE, FAKE, FAKE, 100, 32, 32, 0, FAKE, FAKE, None, FAKE, FAKE, 64, None) == 3        # workspace
+    assert f(FAKE, FAKE, FAKE, 100, 32, 32, 0, None, FAKE, None, FAKE, FAKE, 1 << 30, None) == 1   # feats NULL
+    assert f(FAKE, FAKE, FAKE, -1, 32, 32, 0, FAKE, FAKE, None, FAKE, FAKE, 1 << 30, None) == 1
+    b = L.ssc_subm_conv3d_bwd
+    assert b(FAKE, FAKE, FAKE, 100, 32, 32, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 64, None) == 3
+    assert b(FAKE, FAKE, FAKE, 100, 32, 32, 0, None, FAKE, FAKE, None, FAKE, None, FAKE, 1 << 30, None) == 1
+    assert b(FAKE, FAKE, FAKE, 100, 32, 40, 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == 2
+
+
+def test_binding_raises_without_library(monkeypatch):
+    from sparse_submanifold_convolution_amd import binding
+    monkeypatch.setattr(binding, "_lib", None)
+    monkeypatch.setattr(binding, "_LIB_PATH", "/nonexistent/libssc.so")
+    with pytest.raises(RuntimeError):
+        binding.lib()
