@@ -1,0 +1,249 @@
+"""Benchmark: 3x3x3 submanifold convolution, neighbour-cache build + forward + both backward passes, one GPU.
+
+One step runs the whole path over one resident batch: build_neighbor_map
+(hash insert, probes, mask/z-order sort, pair lists), the forward masked
+implicit GEMM, the input-gradient GEMM and the Split-K weight gradient with
+dbias.  The headline value is effective TFLOP/s counting valid-neighbour MACs
+only (3 passes x 2 P Ci Co flops per step); voxels/s is reported beside it.
+
+The roofline object covers the dominant kernel (the masked implicit GEMM,
+timed on its input-gradient launch, which is that kernel alone on the
+stream) or, when the workload's arithmetic intensity sits below the ridge,
+against HBM bandwidth with algorithmic bytes.  The oracle (CPU, float64) is
+timed on the host on the same workload as a reported baseline.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "effective TFLOP/s (valid MACs) + voxels/s, subm conv3d fwd+bwd, 1 MI355X"
+PEAK_HBM_GBS = 8000.0
+PEAK_TFLOPS = {"f32": 157.3, "f16": 2500.0, "bf16": 2500.0}
+DEFAULT_CONFIG = 2
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--config", type=int, default=DEFAULT_CONFIG, choices=[1, 2, 3, 4, 5])
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-budget-s", type=float, default=20.0)
+    p.add_argument("--copy-calib", type=int, default=0,
+                   help="only run a device copy of this many MiB (HBM counter calibration)")
+    return p.parse_args()
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "sparse_submanifold_convolution_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode())
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed counter summary, if it matches the current sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    rec = data.get(f"{kernel}|{workload}")
+    if not rec or rec.get("source_hash") != source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def copy_calibration(mib: int) -> None:
+    import torch
+    a = torch.empty(mib << 20, dtype=torch.uint8, device="cuda:0")
+    a.fill_(1)
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_mib": mib, "launches": 5, "bytes_read_per_launch": mib << 20,
+                      "bytes_written_per_launch": mib << 20}), flush=True)
+
+
+def cpu_baseline(w, budget_s: float) -> dict:
+    """The oracle as it stands (float64, numpy + BLAS) on the same workload, on the host."""
+    import numpy as np
+    from oracle import subm as O
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [t for t in threadpool_info() if t.get("user_api") == "blas"]
+        cores = int(blas[0]["num_threads"]) if blas else 1
+    except Exception:  # threadpoolctl missing: report the affinity set
+        cores = len(os.sched_getaffinity(0))
+    reps, t_total, flops = 0, 0.0, 0.0
+    t_stage = {"nmap": 0.0, "perm": 0.0, "fwd": 0.0, "dgrad": 0.0, "wgrad": 0.0}
+    while reps == 0 or (t_total < budget_s / 2 and reps < 5):
+        t0 = time.perf_counter()
+        nm = O.neighbor_map(w.coords, w.shape)
+        t1 = time.perf_counter()
+        O.sort_perm(w.coords, nm, w.shape)
+        t2 = time.perf_counter()
+        O.fwd(w.feats, w.weight, w.bias, nm)
+        t3 = time.perf_counter()
+        O.dgrad(w.dout, w.weight, nm)
+        t4 = time.perf_counter()
+        O.wgrad(w.feats, w.dout, nm)
+        O.dbias(w.dout)
+        t5 = time.perf_counter()
+        for k, v in zip(t_stage, (t1 - t0, t2 - t1, t3 - t2, t4 - t3, t5 - t4)):
+            t_stage[k] += v
+        t_total += t5 - t0
+        reps += 1
+        P = int((nm != O.SENTINEL).sum())
+        flops = 3 * 2.0 * P * w.ci * w.co
+    sec = t_total / reps
+    return {"value": flops / sec / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"whole workload (same {w.n} voxels, all three passes plus map and sort), "
+                      f"{reps} repetition(s), float64 numpy/BLAS",
+            "seconds_per_step": sec, "voxels_per_s": w.n / sec,
+            "stage_seconds": {k: v / reps for k, v in t_stage.items()}}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(the design for sharding is described in DESIGN.md). Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calib:
+        copy_calibration(args.copy_calib)
+        return
+
+    import numpy as np
+    import torch
+    import sparse_submanifold_convolution_amd as ssc
+    from sparse_submanifold_convolution_amd import workloads as WL
+
+    dev = torch.device("cuda:0")
+    ssc.lib()
+    w = WL.make_workload(args.config)
+    print(f"[bench] workload {args.config}: {w.desc}, n={w.n}", file=sys.stderr, flush=True)
+    coords = torch.from_numpy(w.coords).to(dev)
+    X, W, b, dY = (t.to(dev) for t in (w.feats, w.weight, w.bias, w.dout))
+    n, ci, co = w.n, w.ci, w.co
+
+    # buffers allocated once; a step only enqueues kernels
+    B_, Xd, Yd, Zd = w.shape
+    pbytes = ssc.plan_bytes(n, w.shape, w.key_bits)
+    plan = ssc.Plan(torch.empty((n, 27), dtype=torch.int32, device=dev), torch.empty(n, dtype=torch.int32, device=dev),
+                    torch.empty(pbytes, dtype=torch.uint8, device=dev), n, tuple(w.shape), w.key_bits)
+    ws = ssc.workspace(plan, ci, co, X.dtype)
+    out = torch.empty((n, co), dtype=X.dtype, device=dev)
+    dX = torch.empty((n, ci), dtype=X.dtype, device=dev)
+    dW = torch.empty((27, ci, co), dtype=X.dtype, device=dev)
+    db = torch.empty((co,), dtype=X.dtype, device=dev)
+    L = ssc.lib()
+    stream = torch.cuda.current_stream(dev)
+    sp = ssc.binding._stream(dev)
+    P_ = ssc.binding._ptr
+
+    def build():
+        r = L.ssc_build_neighbor_map(P_(coords), n, B_, Xd, Yd, Zd, w.key_bits, P_(plan.nmap), P_(plan.perm),
+                                     P_(plan.buf), pbytes, sp)
+        if r:
+            raise ssc.SSCError("ssc_build_neighbor_map", r)
+
+    def fwd():
+        ssc.subm_conv3d_fwd(plan, X, W, b, out=out, ws=ws)
+
+    def dgrad():
+        ssc.subm_conv3d_bwd(plan, X, W, dY, ws=ws, outs=(dX, None, None))
+
+    def wgrad():
+        ssc.subm_conv3d_bwd(plan, X, W, dY, ws=ws, outs=(None, dW, db))
+
+    parts = [("plan", build), ("fwd", fwd), ("dgrad", dgrad), ("wgrad", wgrad)]
+    build()
+    st = ssc.plan_status(plan)
+    if st:
+        raise ssc.SSCError("plan", st)
+    counts = ssc.plan_pair_counts(plan)
+    P = sum(counts)
+    flops_pass = 2.0 * P * ci * co
+
+    for _ in range(args.warmup):
+        for _, f in parts:
+            f()
+    torch.cuda.synchronize()
+
+    ev = {k: [] for k, _ in parts}
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        for name, f in parts:
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            f()
+            e1.record(stream)
+            ev[name].append((e0, e1))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = {k: float(np.mean([a.elapsed_time(c) for a, c in v])) for k, v in ev.items()}
+    ms_step = wall * 1e3 / args.steps
+
+    value = 3 * flops_pass / (ms_step * 1e-3) / 1e12
+    esize = X.element_size()
+    # dominant kernel: the masked implicit GEMM, timed on its input-gradient launch (one kernel per call)
+    kernel = "igemm"
+    alg_bytes = 4.0 * P + esize * n * (ci + co) + esize * 27 * ci * co
+    ai = flops_pass / alg_bytes
+    peak_f = PEAK_TFLOPS[w.dtype]
+    ridge = peak_f * 1e12 / (PEAK_HBM_GBS * 1e9)
+    t_k = ms["dgrad"] * 1e-3
+    wl_name = f"cfg{args.config}"
+    traffic = measured_traffic(kernel, wl_name)
+    if ai >= ridge:
+        ach = flops_pass / t_k / 1e12
+        roof = {"bound": "mfma", "achieved": ach, "peak": peak_f, "unit": "TFLOP/s", "frac": ach / peak_f,
+                "traffic": traffic}
+    else:
+        ach = alg_bytes / t_k / 1e9
+        roof = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": ach / PEAK_HBM_GBS,
+                "traffic": traffic}
+    roof.update({"kernel": f"{kernel} (masked implicit GEMM, input-gradient launch)",
+                 "avg_launch_ms": ms["dgrad"], "flops_per_launch": flops_pass, "alg_bytes_per_launch": alg_bytes,
+                 "arith_intensity": ai, "ridge": ridge})
+
+    line = {
+        "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": f"config {args.config}: {w.desc}", "voxels": n, "valid_pairs": P, "ci": ci, "co": co,
+                   "key_bits": w.key_bits or 32, "step": "neighbour-cache build + fwd + dgrad + wgrad + dbias",
+                   "parallelism": "single GPU"},
+        "voxels_per_s": n / (ms_step * 1e-3),
+        "conv_only_tflops": 3 * flops_pass / ((ms["fwd"] + ms["dgrad"] + ms["wgrad"]) * 1e-3) / 1e12,
+        "breakdown_ms": ms,
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_budget_s)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
