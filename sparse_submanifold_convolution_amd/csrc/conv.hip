@@ -13,10 +13,11 @@
 //                  rows of the sorted order and BN output channels.  It ORs
 //                  the rows' neighbour masks into the tile's offset set, reads
 //                  the tile's gather indices into LDS, then walks (offset,
-//                  K-slice) stages: gathered A rows and the offset's weight
-//                  slice go through double-buffered LDS into 32x32 MFMA tiles
-//                  with fp32 accumulators.  The epilogue adds bias, rounds once
-//                  and writes each row at its original index perm[r].
+//                  K-slice) stages: each wave gathers its own rows straight into
+//                  registers, the offset's weight slice goes through
+//                  double-buffered LDS, and 32x32 MFMAs accumulate in fp32.
+//                  The epilogue adds bias, rounds once and writes each row at
+//                  its original index perm[r].
 //                  Forward: A = X, B[k] = W[k]^T.  Input gradient: A = dY and
 //                  B[k] = W[26-k] as stored, because nmap[i][k] = j exactly
 //                  when nmap[j][26-k] = i.
@@ -96,35 +97,69 @@ __device__ __forceinline__ int acc_row(int lane, int i) { return (i >> 2) * 8 + 
 // ---------------------------------------------------------------------------
 // masked implicit GEMM (forward and input gradient)
 // ---------------------------------------------------------------------------
+//
+// A workgroup of NW waves owns a tile of BM = NW * FM * 32 consecutive rows in
+// sorted order and BN = FN * 32 output channels.  Wave w owns rows
+// [w*FM*32, (w+1)*FM*32) of the tile and every channel of it, so the rows it
+// gathers are its own: each lane loads its row's K-slice straight from global
+// memory into registers in MFMA operand order, DEPTH stages ahead, and no A
+// data passes through LDS.  The weight slice of the stage (dense, shared by
+// all waves) is staged through a double-buffered LDS tile.
+//
+// Inside a stage of BK reduction elements, lane half h (lanes 32h..32h+31)
+// covers the contiguous run [h*BK/2, (h+1)*BK/2): MFMA step s takes its
+// elements s*kFrag..s*kFrag+kFrag-1 of that run, for both operands.  Any
+// one-to-one assignment of reduction indices to (step, half, element) slots
+// gives the same sum, and this one makes every lane's gather one contiguous
+// run of its row.
 
-template <typename T, int BM, int BN, int BK, int WM, int WN>
+template <typename T, int FM, int FN, int BK, int NW>
 struct IgemmCfg {
-  static constexpr int kThreads = 64 * WM * WN;
-  static constexpr int kVec = 16 / int(sizeof(T));          // elements per 16-byte load
-  static constexpr int kPad = kVec;                         // LDS row padding (elements)
-  static constexpr int kLd = BK + kPad;                     // LDS row stride (elements)
-  static constexpr int kTM = BM / WM, kTN = BN / WN;        // per-wave tile
-  static constexpr int kFM = kTM / 32, kFN = kTN / 32;      // MFMA blocks per wave
-  static constexpr int kVpr = BK / kVec;                    // 16-byte vectors per tile row
-  static constexpr int kAV = (BM * kVpr + kThreads - 1) / kThreads;
-  static constexpr int kBV = (BN * kVpr + kThreads - 1) / kThreads;
-  static constexpr size_t kLdsA = size_t(BM) * kLd * sizeof(T);
-  static constexpr size_t kLdsB = size_t(BN) * kLd * sizeof(T);
-  static_assert(kTM % 32 == 0 && kTN % 32 == 0, "wave tile must be whole 32x32 MFMA blocks");
-  static_assert(BK % Elt<T>::kStep == 0 && BK % kVec == 0, "bad BK");
+  static constexpr int kThreads = 64 * NW;
+  static constexpr int kBM = NW * FM * 32;
+  static constexpr int kBN = FN * 32;
+  static constexpr int kVec = 16 / int(sizeof(T));                 // elements per 16-byte load
+  static constexpr int kLd = BK + kVec;                            // LDS row stride of B (elements)
+  static constexpr int kNV = (BK / 2) * int(sizeof(T)) / 16;       // 16-byte loads per lane per row block
+  static constexpr int kSteps = BK / Elt<T>::kStep;                // MFMAs per stage per block
+  static constexpr int kBV = (kBN * BK / kVec + kThreads - 1) / kThreads;  // B vectors per thread
+  static constexpr size_t kLdsB = size_t(kBN) * kLd * sizeof(T);
+  static_assert(kNV >= 1, "BK too small for 16-byte gathers");
+  static_assert(BK % Elt<T>::kStep == 0, "bad BK");
 };
 
-template <typename T, int BM, int BN, int BK, int WM, int WN>
-__global__ void __launch_bounds__(64 * WM * WN)
+template <typename T, int NV>
+__device__ __forceinline__ typename Elt<T>::frag_t a_frag(const uint4 (&v)[NV], int s) {
+  if constexpr (sizeof(T) == 4) {
+    const float* f = reinterpret_cast<const float*>(&v[0]);
+    return f[s];
+  } else {
+    return __builtin_bit_cast(typename Elt<T>::frag_t, v[s]);
+  }
+}
+
+template <typename T, int FM, int FN, int BK, int NW, int DEPTH, int KMAP>
+__global__ void __launch_bounds__(64 * NW)
     igemm(const T* __restrict__ A, const T* __restrict__ Bt, const T* __restrict__ bias, T* __restrict__ out,
           const uint32_t* __restrict__ nmap, const int32_t* __restrict__ perm,
-          const uint32_t* __restrict__ smask, int64_t n, int K, int N, int flip) {
-  using C = IgemmCfg<T, BM, BN, BK, WM, WN>;
+          const uint32_t* __restrict__ smask, int64_t n, int K, int N, int flip, int ntiles, int nblk_n) {
+  using C = IgemmCfg<T, FM, FN, BK, NW>;
   using E = Elt<T>;
   using frag_t = typename E::frag_t;
   constexpr int NT = C::kThreads;
+  constexpr int BM = C::kBM, BN = C::kBN, NV = C::kNV;
+  static_assert(KMAP == 0 || sizeof(T) == 2, "the natural order needs one 16-byte load per MFMA fragment");
 
-  __shared__ __align__(16) char lds_a[2 * C::kLdsA];
+  // XCD-aware order: hardware hands workgroup ids to the 8 XCDs round-robin;
+  // give each XCD a contiguous run of (tile, column block) work so that the
+  // column blocks of one row tile share that XCD's L2.
+  const int nwork = ntiles * nblk_n;
+  const int per = (nwork + 7) / 8;
+  const int work = int(blockIdx.x % 8u) * per + int(blockIdx.x / 8u);
+  if (work >= nwork) return;
+  const int tile = work / nblk_n;
+  const int n0 = (work % nblk_n) * BN;
+
   __shared__ __align__(16) char lds_b[2 * C::kLdsB];
   __shared__ uint32_t jtab[kV][BM];
   __shared__ int32_t prow[BM];
@@ -133,11 +168,10 @@ __global__ void __launch_bounds__(64 * WM * WN)
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave / WN, wn = wave % WN;
-  const int64_t row0 = int64_t(blockIdx.x) * BM;
-  const int n0 = blockIdx.y * BN;
+  const int half = lane >> 5;
+  const int64_t row0 = int64_t(tile) * BM;
 
-  // ---- prologue: rows, tile offset set, gather indices ----
+  // ---- prologue: rows, the tile's offset set, gather indices ----
   if (tid == 0) tile_union = 0;
   __syncthreads();
   for (int r = tid; r < BM; r += NT) {
@@ -160,119 +194,135 @@ __global__ void __launch_bounds__(64 * WM * WN)
       jtab[k][r] = p >= 0 ? nmap[int64_t(p) * kV + k] : kSentinel;
     }
   }
+  __syncthreads();
 
-  f32x16 acc[C::kFM][C::kFN];
+  f32x16 acc[FM][FN];
 #pragma unroll
-  for (int i = 0; i < C::kFM; ++i)
+  for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < C::kFN; ++j)
+    for (int j = 0; j < FN; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
   const int kslices = K / BK;
   const int nstages = __popc(uni) * kslices;
-  uint4 ra[C::kAV], rb[C::kBV];
-  __syncthreads();  // jtab ready
 
-  uint32_t rem = uni;
-  int kcur = rem ? __ffs(rem) - 1 : 0;
-  int kslice = 0;
-
-  auto load_stage = [&](int k, int ks) {
-    const int kb = flip ? (kV - 1 - k) : k;
-    const int c0 = ks * BK;
-#pragma unroll
-    for (int v = 0; v < C::kAV; ++v) {
-      const int idx = tid + v * NT;
-      uint4 val = make_uint4(0, 0, 0, 0);
-      if (idx < BM * C::kVpr) {
-        const int r = idx / C::kVpr, cv = idx % C::kVpr;
-        const uint32_t j = jtab[k][r];
-        if (j != kSentinel)
-          val = *reinterpret_cast<const uint4*>(A + int64_t(j) * K + c0 + cv * C::kVec);
-      }
-      ra[v] = val;
+  // stage cursors: A runs DEPTH stages ahead, B one stage ahead
+  uint32_t a_rem = uni, b_rem = uni;
+  int a_k = a_rem ? __ffs(a_rem) - 1 : 0, a_ks = 0;
+  int b_k = a_k, b_ks = 0;
+  auto advance = [&](uint32_t& rem, int& k, int& ks) {
+    if (++ks == kslices) {
+      ks = 0;
+      rem &= rem - 1;
+      k = rem ? __ffs(rem) - 1 : 0;
     }
-    const T* bbase = Bt + int64_t(kb) * N * K;
+  };
+
+  uint4 abuf[DEPTH][FM][NV];
+  uint4 rb[C::kBV];
+
+  // KMAP 0: lane half h reads the run [h*BK/2, (h+1)*BK/2) of the stage, one
+  // contiguous piece per lane.  KMAP 1 (16-bit only): the natural MFMA order,
+  // load v of half h reads 16 bytes at element (2v + h) * 8, so each load
+  // instruction covers 32 contiguous bytes of every row.
+  auto load_a = [&](uint4 (&dst)[FM][NV]) {
+    const int c0 = a_ks * BK + (KMAP == 0 ? half * (BK / 2) : half * C::kVec);
+    constexpr int vstride = KMAP == 0 ? 1 : 2;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const uint32_t j = jtab[a_k][wave * FM * 32 + i * 32 + (lane & 31)];
+      if (j != kSentinel) {
+        const uint4* src = reinterpret_cast<const uint4*>(A + int64_t(j) * K + c0);
+#pragma unroll
+        for (int v = 0; v < NV; ++v) dst[i][v] = src[v * vstride];
+      } else {
+#pragma unroll
+        for (int v = 0; v < NV; ++v) dst[i][v] = make_uint4(0, 0, 0, 0);
+      }
+    }
+    advance(a_rem, a_k, a_ks);
+  };
+  auto load_b = [&]() {
+    const int kb = flip ? (kV - 1 - b_k) : b_k;
+    const T* base = Bt + int64_t(kb) * N * K + b_ks * BK;
+    constexpr int VPR = BK / C::kVec;
 #pragma unroll
     for (int v = 0; v < C::kBV; ++v) {
       const int idx = tid + v * NT;
       uint4 val = make_uint4(0, 0, 0, 0);
-      if (idx < BN * C::kVpr) {
-        const int r = idx / C::kVpr, cv = idx % C::kVpr;
-        if (n0 + r < N) val = *reinterpret_cast<const uint4*>(bbase + int64_t(n0 + r) * K + c0 + cv * C::kVec);
+      if (idx < BN * VPR) {
+        const int r = idx / VPR, cv = idx % VPR;
+        if (n0 + r < N) val = *reinterpret_cast<const uint4*>(base + int64_t(n0 + r) * K + cv * C::kVec);
       }
       rb[v] = val;
     }
+    advance(b_rem, b_k, b_ks);
   };
-  auto store_stage = [&](int buf) {
-    T* sa = reinterpret_cast<T*>(lds_a + buf * C::kLdsA);
+  auto store_b = [&](int buf) {
     T* sb = reinterpret_cast<T*>(lds_b + buf * C::kLdsB);
-#pragma unroll
-    for (int v = 0; v < C::kAV; ++v) {
-      const int idx = tid + v * NT;
-      if (idx < BM * C::kVpr) {
-        const int r = idx / C::kVpr, cv = idx % C::kVpr;
-        *reinterpret_cast<uint4*>(sa + r * C::kLd + cv * C::kVec) = ra[v];
-      }
-    }
+    constexpr int VPR = BK / C::kVec;
 #pragma unroll
     for (int v = 0; v < C::kBV; ++v) {
       const int idx = tid + v * NT;
-      if (idx < BN * C::kVpr) {
-        const int r = idx / C::kVpr, cv = idx % C::kVpr;
+      if (idx < BN * VPR) {
+        const int r = idx / VPR, cv = idx % VPR;
         *reinterpret_cast<uint4*>(sb + r * C::kLd + cv * C::kVec) = rb[v];
       }
     }
   };
-
-  if (nstages > 0) load_stage(kcur, 0);
-  for (int s = 0; s < nstages; ++s) {
-    const int buf = s & 1;
-    store_stage(buf);
-    __syncthreads();
-    if (s + 1 < nstages) {
-      if (++kslice == kslices) {
-        kslice = 0;
-        rem &= rem - 1;
-        kcur = __ffs(rem) - 1;
-      }
-      load_stage(kcur, kslice);
-    }
-    const T* sa = reinterpret_cast<const T*>(lds_a + buf * C::kLdsA);
+  auto compute = [&](const uint4 (&a)[FM][NV], int buf) {
     const T* sb = reinterpret_cast<const T*>(lds_b + buf * C::kLdsB);
-    const int koff = (lane >> 5) * E::kFrag;
 #pragma unroll
-    for (int kk = 0; kk < BK; kk += E::kStep) {
-      frag_t af[C::kFM], bfr[C::kFN];
+    for (int s = 0; s < C::kSteps; ++s) {
+      frag_t bfr[FN];
 #pragma unroll
-      for (int i = 0; i < C::kFM; ++i) {
-        const int r = wm * C::kTM + i * 32 + (lane & 31);
-        af[i] = *reinterpret_cast<const frag_t*>(sa + r * C::kLd + kk + koff);
+      for (int j = 0; j < FN; ++j) {
+        const int c = j * 32 + (lane & 31);
+        const int kofs = KMAP == 0 ? half * (BK / 2) + s * E::kFrag : (2 * s + half) * E::kFrag;
+        bfr[j] = *reinterpret_cast<const frag_t*>(sb + c * C::kLd + kofs);
       }
 #pragma unroll
-      for (int j = 0; j < C::kFN; ++j) {
-        const int c = wn * C::kTN + j * 32 + (lane & 31);
-        bfr[j] = *reinterpret_cast<const frag_t*>(sb + c * C::kLd + kk + koff);
+      for (int i = 0; i < FM; ++i) {
+        const frag_t af = a_frag<T, NV>(a[i], s);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = E::mfma(af, bfr[j], acc[i][j]);
       }
+    }
+  };
+
+  // prologue loads
 #pragma unroll
-      for (int i = 0; i < C::kFM; ++i)
+  for (int d = 0; d < DEPTH; ++d)
+    if (d < nstages) load_a(abuf[d]);
+  if (nstages > 0) load_b();
+
+  for (int s0 = 0; s0 < nstages; s0 += DEPTH) {
 #pragma unroll
-        for (int j = 0; j < C::kFN; ++j) acc[i][j] = E::mfma(af[i], bfr[j], acc[i][j]);
+    for (int d = 0; d < DEPTH; ++d) {
+      const int s = s0 + d;
+      if (s < nstages) {
+        const int buf = s & 1;
+        store_b(buf);
+        __syncthreads();
+        if (s + 1 < nstages) load_b();
+        compute(abuf[d], buf);
+        if (s + DEPTH < nstages) load_a(abuf[d]);
+      }
     }
   }
 
   // ---- epilogue: bias, round once, scatter rows to perm ----
 #pragma unroll
-  for (int j = 0; j < C::kFN; ++j) {
-    const int c = n0 + wn * C::kTN + j * 32 + (lane & 31);
+  for (int j = 0; j < FN; ++j) {
+    const int c = n0 + j * 32 + (lane & 31);
     if (c >= N) continue;
     const float bv = bias ? E::load(bias[c]) : 0.f;
 #pragma unroll
-    for (int i = 0; i < C::kFM; ++i) {
+    for (int i = 0; i < FM; ++i) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int r = wm * C::kTM + i * 32 + acc_row(lane, e);
+        const int r = wave * FM * 32 + i * 32 + acc_row(lane, e);
         const int32_t p = prow[r];
         if (p >= 0) out[int64_t(p) * N + c] = E::store(acc[i][j][e] + bv);
       }
@@ -464,6 +514,223 @@ __global__ void __launch_bounds__(64 * WM * WN)
   }
 }
 
+// Weight gradient for 16-bit types, built on the gfx950 LDS transpose read.
+// Gathered X rows (by j) and dY rows (by i) are stored in LDS as they sit in
+// memory: row = pair, columns = channels, plain 16-byte writes.  The MFMA
+// operands need 8 consecutive pairs of one channel per lane; the transpose
+// read delivers them: within each 16-lane group, lane i receives element
+// (i mod 4) of the 64-bit pieces addressed by lanes i/4, i/4+4, i/4+8 and
+// i/4+12, so pointing lane j at pair row j/4, channels 4*(j mod 4)..+3 hands
+// lane i channel i of four consecutive pairs.  Two such reads make one
+// fragment.  Row strides are 64 bytes past a multiple of 256 so the four
+// rows of a read fall in different bank groups.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+
+template <int C>
+struct TrPad {
+  // smallest padding (elements) giving a row of 2*(C+pad) bytes = 64 mod 256
+  static constexpr int v = ((2 * C) % 256 == 64) ? 0 : ((64 - (2 * C) % 256 + 256) % 256) / 2;
+};
+
+template <typename T, int FM, int FN, int NWM, int NWN, int BKP>
+struct WgradTrCfg {
+  static constexpr int kThreads = 64 * NWM * NWN;
+  static constexpr int kBM = NWM * FM * 32, kBN = NWN * FN * 32;
+  static constexpr int kLdA = kBM + TrPad<kBM>::v, kLdB = kBN + TrPad<kBN>::v;
+  static constexpr size_t kLdsA = size_t(BKP) * kLdA * 2, kLdsB = size_t(BKP) * kLdB * 2;
+  static constexpr int kItemsA = BKP * kBM / 8, kItemsB = BKP * kBN / 8;
+  static constexpr int kIA = (kItemsA + kThreads - 1) / kThreads, kIB = (kItemsB + kThreads - 1) / kThreads;
+  // pair indices are staged through LDS in groups of kGP pairs, one group ahead
+  static constexpr int kGP = 512;
+  static constexpr int kSG = kGP / BKP;                 // stages per group
+  static constexpr int kPI = kGP / kThreads;            // index pairs each thread fetches per group
+  static_assert((2 * kLdA) % 256 == 64 && (2 * kLdB) % 256 == 64, "row stride must be 64 mod 256 bytes");
+  static_assert(BKP % 16 == 0 && kGP % BKP == 0 && kGP % kThreads == 0, "bad staging sizes");
+};
+
+__device__ __forceinline__ s16x4 lds_tr16(const void* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(const_cast<void*>(p)));
+}
+
+// Pipeline: pair indices for group g+1 are written to LDS at the first stage
+// of group g (fetched one group earlier into registers); row gathers for stage
+// s+DEPTH are issued during stage s from indices already in LDS; the stage's
+// rows go through double-buffered LDS into transpose reads and MFMAs.
+template <typename T, int FM, int FN, int NWM, int NWN, int BKP, int DEPTH>
+__global__ void __launch_bounds__(64 * NWM * NWN)
+    wgrad_tr(const T* __restrict__ X, const T* __restrict__ dY, const uint32_t* __restrict__ pair_i,
+             const uint32_t* __restrict__ pair_j, const PlanHeader* __restrict__ hdr, float* __restrict__ partial,
+             int Ci, int Co, int64_t chunk_len, int max_chunks, int ntiles_n) {
+  using C = WgradTrCfg<T, FM, FN, NWM, NWN, BKP>;
+  using E = Elt<T>;
+  using frag_t = typename E::frag_t;
+  constexpr int NT = C::kThreads, BM = C::kBM, BN = C::kBN, SG = C::kSG, GP = C::kGP;
+  static_assert(DEPTH >= 1 && DEPTH < C::kSG, "prefetch depth must stay inside one index group");
+
+  const int chunk = blockIdx.x;
+  const int k = blockIdx.y;
+  const int64_t pk = hdr->pair_count[k];
+  const int64_t start = int64_t(chunk) * chunk_len;
+  if (start >= pk) return;
+  const int64_t end = (start + chunk_len < pk) ? start + chunk_len : pk;
+  const int64_t off = hdr->pair_off[k];
+  const int64_t pbeg = off + start, pend = off + end;
+  const int m0 = (blockIdx.z / ntiles_n) * BM;
+  const int c0 = (blockIdx.z % ntiles_n) * BN;
+
+  __shared__ __align__(16) char lds_a[2 * C::kLdsA];
+  __shared__ __align__(16) char lds_b[2 * C::kLdsB];
+  __shared__ uint32_t pidx[2][GP][2];  // (i, j) per pair; sentinel past the chunk
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave / NWN, wn = wave % NWN;
+  const int grp = lane >> 4, src = lane & 15;
+  const int tr_row = (grp >> 1) * 8 + (src >> 2);
+  const int tr_col = (grp & 1) * 16 + (src & 3) * 4;
+
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  const int nstages = int((end - start + BKP - 1) / BKP);
+
+  uint32_t ri[C::kPI], rj[C::kPI];
+  auto fetch_idx = [&](int g) {
+#pragma unroll
+    for (int q = 0; q < C::kPI; ++q) {
+      const int64_t p = pbeg + int64_t(g) * GP + q * NT + tid;
+      ri[q] = p < pend ? pair_i[p] : kSentinel;
+      rj[q] = p < pend ? pair_j[p] : kSentinel;
+    }
+  };
+  auto put_idx = [&](int g) {
+#pragma unroll
+    for (int q = 0; q < C::kPI; ++q) {
+      pidx[g & 1][q * NT + tid][0] = ri[q];
+      pidx[g & 1][q * NT + tid][1] = rj[q];
+    }
+  };
+
+  uint4 ra[DEPTH][C::kIA], rb[DEPTH][C::kIB];
+  auto load_stage = [&](int s, uint4 (&da)[C::kIA], uint4 (&db)[C::kIB]) {
+    const uint32_t(*pi)[2] = pidx[(s / SG) & 1];
+    const int r0 = (s % SG) * BKP;
+#pragma unroll
+    for (int v = 0; v < C::kIA; ++v) {
+      const int idx = tid + v * NT;
+      const int r = idx / (BM / 8), cv = idx % (BM / 8);
+      uint4 val = make_uint4(0, 0, 0, 0);
+      if (idx < C::kItemsA) {
+        const uint32_t j = pi[r0 + r][1];
+        if (j != kSentinel && m0 + cv * 8 < Ci) val = *reinterpret_cast<const uint4*>(X + int64_t(j) * Ci + m0 + cv * 8);
+      }
+      da[v] = val;
+    }
+#pragma unroll
+    for (int v = 0; v < C::kIB; ++v) {
+      const int idx = tid + v * NT;
+      const int r = idx / (BN / 8), cv = idx % (BN / 8);
+      uint4 val = make_uint4(0, 0, 0, 0);
+      if (idx < C::kItemsB) {
+        const uint32_t i = pi[r0 + r][0];
+        if (i != kSentinel && c0 + cv * 8 < Co) val = *reinterpret_cast<const uint4*>(dY + int64_t(i) * Co + c0 + cv * 8);
+      }
+      db[v] = val;
+    }
+  };
+  auto store_stage = [&](int buf, const uint4 (&da)[C::kIA], const uint4 (&db)[C::kIB]) {
+    char* sa = lds_a + buf * C::kLdsA;
+    char* sb = lds_b + buf * C::kLdsB;
+#pragma unroll
+    for (int v = 0; v < C::kIA; ++v) {
+      const int idx = tid + v * NT;
+      if (idx < C::kItemsA) {
+        const int r = idx / (BM / 8), cv = idx % (BM / 8);
+        *reinterpret_cast<uint4*>(sa + (size_t(r) * C::kLdA + cv * 8) * 2) = da[v];
+      }
+    }
+#pragma unroll
+    for (int v = 0; v < C::kIB; ++v) {
+      const int idx = tid + v * NT;
+      if (idx < C::kItemsB) {
+        const int r = idx / (BN / 8), cv = idx % (BN / 8);
+        *reinterpret_cast<uint4*>(sb + (size_t(r) * C::kLdB + cv * 8) * 2) = db[v];
+      }
+    }
+  };
+  auto frag = [&](const char* base, int ld, int row0, int col0) {
+    const char* p = base + (size_t(row0 + tr_row) * ld + col0 + tr_col) * 2;
+    const s16x4 lo = lds_tr16(p);
+    const s16x4 hi = lds_tr16(p + size_t(4) * ld * 2);
+    const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(frag_t, v);
+  };
+  auto compute = [&](int buf) {
+    const char* sa = lds_a + buf * C::kLdsA;
+    const char* sb = lds_b + buf * C::kLdsB;
+#pragma unroll
+    for (int kk = 0; kk < BKP; kk += 16) {
+      frag_t af[FM], bfr[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) af[i] = frag(sa, C::kLdA, kk, wm * FM * 32 + i * 32);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) bfr[j] = frag(sb, C::kLdB, kk, wn * FN * 32 + j * 32);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = E::mfma(af[i], bfr[j], acc[i][j]);
+    }
+  };
+
+  // prologue: indices of groups 0 (to LDS) and 1 (registers), first DEPTH stages of rows
+  fetch_idx(0);
+  put_idx(0);
+  fetch_idx(1);
+  __syncthreads();
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d)
+    if (d < nstages) load_stage(d, ra[d], rb[d]);
+
+  for (int s0 = 0; s0 < nstages; s0 += DEPTH) {
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) {
+      const int s = s0 + d;
+      if (s < nstages) {
+        if (s % SG == 0) {
+          put_idx(s / SG + 1);
+          fetch_idx(s / SG + 2);
+        }
+        store_stage(s & 1, ra[d], rb[d]);
+        __syncthreads();
+        if (s + DEPTH < nstages) load_stage(s + DEPTH, ra[d], rb[d]);
+        compute(s & 1);
+      }
+    }
+  }
+
+  float* dst = partial + (int64_t(k) * max_chunks + chunk) * int64_t(Ci) * Co;
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    const int c = c0 + wn * FN * 32 + j * 32 + (lane & 31);
+    if (c >= Co) continue;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int m = m0 + wm * FM * 32 + i * 32 + acc_row(lane, e);
+        if (m < Ci) dst[int64_t(m) * Co + c] = acc[i][j][e];
+      }
+  }
+}
+
 template <typename T>
 __global__ void __launch_bounds__(256) wgrad_reduce(const float* __restrict__ partial,
                                                     const PlanHeader* __restrict__ hdr, T* __restrict__ dW,
@@ -479,16 +746,41 @@ __global__ void __launch_bounds__(256) wgrad_reduce(const float* __restrict__ pa
   dW[int64_t(k) * cico + e] = Elt<T>::store(s);
 }
 
-// dbias stage 1: block b sums rows [b*rows, (b+1)*rows) of every column
+// dbias stage 1: block (b, y) sums rows [b*rows, (b+1)*rows) of the 256
+// columns of chunk y.  Threads are 32 column vectors of 8 x 8 row phases; each
+// loads 16 bytes a row and the phases are added in a fixed order.
 template <typename T>
 __global__ void __launch_bounds__(256) colsum_partial(const T* __restrict__ dY, int64_t n, int Co,
                                                       int64_t rows, float* __restrict__ part) {
+  __shared__ float red[8][256];
+  const int cv = threadIdx.x & 31, ph = threadIdx.x >> 5;
+  const int col = blockIdx.y * 256 + cv * 8;
   const int64_t r0 = int64_t(blockIdx.x) * rows;
   const int64_t r1 = (r0 + rows < n) ? r0 + rows : n;
-  for (int c = threadIdx.x; c < Co; c += 256) {
-    float s = 0.f;
-    for (int64_t r = r0; r < r1; ++r) s += Elt<T>::load(dY[r * Co + c]);
-    part[int64_t(blockIdx.x) * Co + c] = s;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (col < Co) {
+    for (int64_t r = r0 + ph; r < r1; r += 8) {
+      const uint4 v = *reinterpret_cast<const uint4*>(dY + r * Co + col);
+      const T* e = reinterpret_cast<const T*>(&v);
+#pragma unroll
+      for (int q = 0; q < 16 / int(sizeof(T)); ++q) acc[q] += Elt<T>::load(e[q]);
+      if constexpr (sizeof(T) == 4) {
+        const uint4 w = *reinterpret_cast<const uint4*>(dY + r * Co + col + 4);
+        const T* f = reinterpret_cast<const T*>(&w);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[4 + q] += Elt<T>::load(f[q]);
+      }
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < 8; ++q) red[ph][cv * 8 + q] = acc[q];
+  __syncthreads();
+  const int c = blockIdx.y * 256 + threadIdx.x;
+  if (c < Co) {
+    float sum = 0.f;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) sum += red[q][threadIdx.x];
+    part[int64_t(blockIdx.x) * Co + c] = sum;
   }
 }
 
@@ -513,8 +805,12 @@ __global__ void zero_kernel(T* __restrict__ p, int64_t count) {
 // host-side configuration
 // ---------------------------------------------------------------------------
 
-// Weight-gradient tile edge for a channel count.
-static int wgrad_tile(int c) { return c >= 128 ? 128 : (c > 32 ? 64 : 32); }
+// Weight-gradient tile edge for a channel count: fp32 uses the LDS-transposing
+// kernel (up to 128), 16-bit types the transpose-read kernel (up to 256).
+static int wgrad_tile(int c, int esize) {
+  if (esize == 2 && c >= 256) return 256;
+  return c >= 128 ? 128 : (c > 32 ? 64 : 32);
+}
 
 struct BwdShape {
   int bm = 0, bn = 0, mt = 0, nt = 0;
@@ -524,14 +820,20 @@ struct BwdShape {
   int bias_blocks = 0;
 };
 
-static BwdShape bwd_shape(int64_t n, int Ci, int Co) {
+static BwdShape bwd_shape(int64_t n, int Ci, int Co, int esize) {
   BwdShape s;
-  s.bm = wgrad_tile(Ci);
-  s.bn = wgrad_tile(Co);
+  if (esize == 2) {
+    // square tiles of the narrower side
+    const int t = wgrad_tile(Ci < Co ? Ci : Co, 2);
+    s.bm = s.bn = t;
+  } else {
+    s.bm = wgrad_tile(Ci, 4);
+    s.bn = wgrad_tile(Co, 4);
+  }
   s.mt = (Ci + s.bm - 1) / s.bm;
   s.nt = (Co + s.bn - 1) / s.bn;
-  // aim for about 4096 workgroups at P ~ 14 n valid pairs
-  int64_t len = (14 * n * int64_t(s.mt) * s.nt + 4095) / 4096;
+  // aim for about 2048 workgroups at P ~ 14 n valid pairs
+  int64_t len = (14 * n * int64_t(s.mt) * s.nt + 2047) / 2048;
   len = (len + 255) / 256 * 256;
   if (len < 1024) len = 1024;
   if (len > (int64_t(1) << 20)) len = int64_t(1) << 20;
@@ -549,7 +851,7 @@ struct WsLayout {
 
 static WsLayout ws_layout(int64_t n, int Ci, int Co, int esize) {
   WsLayout w;
-  const BwdShape b = bwd_shape(n, Ci, Co);
+  const BwdShape b = bwd_shape(n, Ci, Co, esize);
   size_t off = 0;
   w.wt = off;
   off = align_up(off + size_t(kV) * Ci * Co * esize, 256);
@@ -567,40 +869,72 @@ static bool channels_ok(int Ci, int Co) {
   return Ci > 0 && Co > 0 && Ci % 16 == 0 && Co % 16 == 0 && Ci <= 4096 && Co <= 4096;
 }
 
+template <typename T, int FM, int FN, int BK, int NW, int DEPTH, int KMAP>
+static void igemm_go(const T* A, const T* Bt, const T* bias, T* out, const uint32_t* nmap, const int32_t* perm,
+                     const uint32_t* smask, int64_t n, int K, int N, int flip, hipStream_t s) {
+  constexpr int BM = NW * FM * 32, BN = FN * 32;
+  const int ntiles = int((n + BM - 1) / BM);
+  const int nblk = (N + BN - 1) / BN;
+  const int nwork = ntiles * nblk;
+  const unsigned grid = unsigned((nwork + 7) / 8 * 8);
+  igemm<T, FM, FN, BK, NW, DEPTH, KMAP><<<grid, 64 * NW, 0, s>>>(A, Bt, bias, out, nmap, perm, smask, n, K, N,
+                                                                flip, ntiles, nblk);
+}
+
+// Tile choice (measured on MI355X, see the tuning notes): every wave owns 32
+// rows; the workgroup spans as many output channels as the layer has, up to
+// 256, so the gathered rows are fetched once per channel block; 8 waves share
+// one weight tile when there are enough rows to fill the chip, fewer waves
+// (more, smaller workgroups) otherwise.
+template <typename T, int FN>
+static void igemm_pick_rows(const T* A, const T* Bt, const T* bias, T* out, const uint32_t* nmap,
+                            const int32_t* perm, const uint32_t* smask, int64_t n, int K, int N, int flip,
+                            hipStream_t s) {
+  const int64_t nblk = (N + FN * 32 - 1) / (FN * 32);
+  const int64_t wg256 = (n + 255) / 256 * nblk, wg128 = (n + 127) / 128 * nblk;
+#define SSC_GO(NW, BK, DEPTH, KMAP) \
+  igemm_go<T, 1, FN, BK, NW, DEPTH, KMAP>(A, Bt, bias, out, nmap, perm, smask, n, K, N, flip, s)
+#define SSC_BK(NW, DEPTH)                                                 \
+  do {                                                                    \
+    if constexpr (sizeof(T) == 4) {                                       \
+      SSC_GO(NW, 16, 2, 0);                                               \
+    } else {                                                              \
+      if (K % 64 == 0) SSC_GO(NW, 64, DEPTH, 1);                          \
+      else if (K % 32 == 0) SSC_GO(NW, 32, DEPTH, 1);                     \
+      else SSC_GO(NW, 16, DEPTH, 1);                                      \
+    }                                                                     \
+  } while (0)
+  if (FN >= 4 && wg256 >= 512) SSC_BK(8, 3);
+  else if (wg128 >= 256) SSC_BK(4, 4);
+  else SSC_BK(2, 4);
+#undef SSC_BK
+#undef SSC_GO
+}
+
 template <typename T>
 static void launch_igemm(const T* A, const T* Bt, const T* bias, T* out, const uint32_t* nmap,
                          const int32_t* perm, const uint32_t* smask, int64_t n, int K, int N, int flip,
                          hipStream_t s) {
-  const unsigned tiles = unsigned((n + 127) / 128);
-  constexpr bool f32 = sizeof(T) == 4;
-  // BK: the largest of 32/16 that divides K (16-bit MFMA reduces 16 at a time; fp32 takes 2)
-  const bool bk32 = K % 32 == 0;
-  if (N >= 128) {
-    dim3 grid(tiles, unsigned((N + 127) / 128));
-    if (bk32)
-      igemm<T, 128, 128, 32, 2, 2><<<grid, 256, 0, s>>>(A, Bt, bias, out, nmap, perm, smask, n, K, N, flip);
-    else
-      igemm<T, 128, 128, 16, 2, 2><<<grid, 256, 0, s>>>(A, Bt, bias, out, nmap, perm, smask, n, K, N, flip);
-  } else if (N > 32) {
-    dim3 grid(tiles, unsigned((N + 63) / 64));
-    if (bk32)
-      igemm<T, 128, 64, 32, 4, 1><<<grid, 256, 0, s>>>(A, Bt, bias, out, nmap, perm, smask, n, K, N, flip);
-    else
-      igemm<T, 128, 64, 16, 4, 1><<<grid, 256, 0, s>>>(A, Bt, bias, out, nmap, perm, smask, n, K, N, flip);
-  } else {
-    dim3 grid(tiles, 1);
-    if (bk32)
-      igemm<T, 128, 32, 32, 4, 1><<<grid, 256, 0, s>>>(A, Bt, bias, out, nmap, perm, smask, n, K, N, flip);
-    else
-      igemm<T, 128, 32, 16, 4, 1><<<grid, 256, 0, s>>>(A, Bt, bias, out, nmap, perm, smask, n, K, N, flip);
-  }
-  (void)f32;
+  if (N > 128) igemm_pick_rows<T, 8>(A, Bt, bias, out, nmap, perm, smask, n, K, N, flip, s);
+  else if (N > 64) igemm_pick_rows<T, 4>(A, Bt, bias, out, nmap, perm, smask, n, K, N, flip, s);
+  else if (N > 32) igemm_pick_rows<T, 2>(A, Bt, bias, out, nmap, perm, smask, n, K, N, flip, s);
+  else igemm_pick_rows<T, 1>(A, Bt, bias, out, nmap, perm, smask, n, K, N, flip, s);
 }
 
 template <typename T>
 static void launch_wgrad(const T* X, const T* dY, const uint32_t* pi, const uint32_t* pj, const PlanHeader* h,
                          float* partial, int Ci, int Co, const BwdShape& b, hipStream_t s) {
   dim3 grid(unsigned(b.max_chunks), kV, unsigned(b.mt * b.nt));
+  if constexpr (sizeof(T) == 2) {
+#define SSC_WTR(FM, FN, NWM, NWN)                                                                      \
+  wgrad_tr<T, FM, FN, NWM, NWN, 32, 2><<<grid, 64 * NWM * NWN, 0, s>>>(X, dY, pi, pj, h, partial, Ci, Co, \
+                                                                      b.chunk_len, b.max_chunks, b.nt)
+    if (b.bm == 256) SSC_WTR(2, 4, 4, 2);
+    else if (b.bm == 128) SSC_WTR(2, 2, 2, 2);
+    else if (b.bm == 64) SSC_WTR(1, 1, 2, 2);
+    else SSC_WTR(1, 1, 1, 1);
+#undef SSC_WTR
+  } else {
   if (b.bm == 128 && b.bn == 128)
     wgrad<T, 128, 128, 32, 2, 2><<<grid, 256, 0, s>>>(X, dY, pi, pj, h, partial, Ci, Co, b.chunk_len,
                                                        b.max_chunks, b.nt);
@@ -628,6 +962,7 @@ static void launch_wgrad(const T* X, const T* dY, const uint32_t* pi, const uint
   else
     wgrad<T, 128, 32, 32, 2, 1><<<grid, 128, 0, s>>>(X, dY, pi, pj, h, partial, Ci, Co, b.chunk_len,
                                                       b.max_chunks, b.nt);
+  }
 }
 
 template <typename T>
@@ -650,7 +985,7 @@ static int run_bwd(const char* plan, const uint32_t* nmap, const int32_t* perm, 
                    void* dbias, char* ws, hipStream_t s) {
   const PlanLayout L = conv_layout(n);
   const WsLayout W = ws_layout(n, Ci, Co, sizeof(T));
-  const BwdShape b = bwd_shape(n, Ci, Co);
+  const BwdShape b = bwd_shape(n, Ci, Co, int(sizeof(T)));
   const PlanHeader* h = reinterpret_cast<const PlanHeader*>(plan + L.header);
   const T* dY = static_cast<const T*>(dout);
   if (dfeats) {
@@ -668,7 +1003,7 @@ static int run_bwd(const char* plan, const uint32_t* nmap, const int32_t* perm, 
   }
   if (dbias) {
     float* part = reinterpret_cast<float*>(ws + W.bias);
-    colsum_partial<T><<<unsigned(b.bias_blocks), 256, 0, s>>>(dY, n, Co, b.bias_rows, part);
+    colsum_partial<T><<<dim3(unsigned(b.bias_blocks), unsigned((Co + 255) / 256)), 256, 0, s>>>(dY, n, Co, b.bias_rows, part);
     colsum_final<T><<<unsigned((Co + 255) / 256), 256, 0, s>>>(part, b.bias_blocks, Co, static_cast<T*>(dbias));
   }
   return SSC_OK;
