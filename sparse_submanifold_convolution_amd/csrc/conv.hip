@@ -104,7 +104,8 @@ __device__ __forceinline__ int acc_row(int lane, int i) { return (i >> 2) * 8 + 
 // gathers are its own: each lane loads its row's K-slice straight from global
 // memory into registers in MFMA operand order, DEPTH stages ahead, and no A
 // data passes through LDS.  The weight slice of the stage (dense, shared by
-// all waves) is staged through a double-buffered LDS tile.
+// all waves) is fetched DEPTH stages ahead too and staged through a
+// double-buffered LDS tile.
 //
 // Inside a stage of BK reduction elements, lane half h (lanes 32h..32h+31)
 // covers the contiguous run [h*BK/2, (h+1)*BK/2): MFMA step s takes its
@@ -207,7 +208,7 @@ __global__ void __launch_bounds__(64 * NW)
   const int kslices = K / BK;
   const int nstages = __popc(uni) * kslices;
 
-  // stage cursors: A runs DEPTH stages ahead, B one stage ahead
+  // stage cursors: A and B both run DEPTH stages ahead
   uint32_t a_rem = uni, b_rem = uni;
   int a_k = a_rem ? __ffs(a_rem) - 1 : 0, a_ks = 0;
   int b_k = a_k, b_ks = 0;
@@ -220,7 +221,7 @@ __global__ void __launch_bounds__(64 * NW)
   };
 
   uint4 abuf[DEPTH][FM][NV];
-  uint4 rb[C::kBV];
+  uint4 bbuf[DEPTH][C::kBV];
 
   // KMAP 0: lane half h reads the run [h*BK/2, (h+1)*BK/2) of the stage, one
   // contiguous piece per lane.  KMAP 1 (16-bit only): the natural MFMA order,
@@ -243,7 +244,7 @@ __global__ void __launch_bounds__(64 * NW)
     }
     advance(a_rem, a_k, a_ks);
   };
-  auto load_b = [&]() {
+  auto load_b = [&](uint4 (&rb)[C::kBV]) {
     const int kb = flip ? (kV - 1 - b_k) : b_k;
     const T* base = Bt + int64_t(kb) * N * K + b_ks * BK;
     constexpr int VPR = BK / C::kVec;
@@ -259,7 +260,7 @@ __global__ void __launch_bounds__(64 * NW)
     }
     advance(b_rem, b_k, b_ks);
   };
-  auto store_b = [&](int buf) {
+  auto store_b = [&](int buf, const uint4 (&rb)[C::kBV]) {
     T* sb = reinterpret_cast<T*>(lds_b + buf * C::kLdsB);
     constexpr int VPR = BK / C::kVec;
 #pragma unroll
@@ -291,11 +292,13 @@ __global__ void __launch_bounds__(64 * NW)
     }
   };
 
-  // prologue loads
+  // prologue loads: both operands DEPTH stages deep
 #pragma unroll
   for (int d = 0; d < DEPTH; ++d)
-    if (d < nstages) load_a(abuf[d]);
-  if (nstages > 0) load_b();
+    if (d < nstages) {
+      load_a(abuf[d]);
+      load_b(bbuf[d]);
+    }
 
   for (int s0 = 0; s0 < nstages; s0 += DEPTH) {
 #pragma unroll
@@ -303,9 +306,9 @@ __global__ void __launch_bounds__(64 * NW)
       const int s = s0 + d;
       if (s < nstages) {
         const int buf = s & 1;
-        store_b(buf);
+        store_b(buf, bbuf[d]);
         __syncthreads();
-        if (s + 1 < nstages) load_b();
+        if (s + DEPTH < nstages) load_b(bbuf[d]);
         compute(abuf[d], buf);
         if (s + DEPTH < nstages) load_a(abuf[d]);
       }
@@ -784,14 +787,20 @@ __global__ void __launch_bounds__(256) colsum_partial(const T* __restrict__ dY, 
   }
 }
 
+// dbias stage 2: 64 columns per workgroup, 4 phases each adding every 4th
+// partial, then the phases in a fixed order.
 template <typename T>
 __global__ void __launch_bounds__(256) colsum_final(const float* __restrict__ part, int nb, int Co,
                                                     T* __restrict__ dbias) {
-  const int c = blockIdx.x * 256 + threadIdx.x;
-  if (c >= Co) return;
+  __shared__ float red[4][64];
+  const int cl = threadIdx.x & 63, ph = threadIdx.x >> 6;
+  const int c = blockIdx.x * 64 + cl;
   float s = 0.f;
-  for (int b = 0; b < nb; ++b) s += part[int64_t(b) * Co + c];
-  dbias[c] = Elt<T>::store(s);
+  if (c < Co)
+    for (int b = ph; b < nb; b += 4) s += part[int64_t(b) * Co + c];
+  red[ph][cl] = s;
+  __syncthreads();
+  if (ph == 0 && c < Co) dbias[c] = Elt<T>::store(((red[0][cl] + red[1][cl]) + red[2][cl]) + red[3][cl]);
 }
 
 template <typename T>
@@ -904,9 +913,11 @@ static void igemm_pick_rows(const T* A, const T* Bt, const T* bias, T* out, cons
       else SSC_GO(NW, 16, DEPTH, 1);                                      \
     }                                                                     \
   } while (0)
-  if (FN >= 4 && wg256 >= 512) SSC_BK(8, 3);
-  else if (wg128 >= 256) SSC_BK(4, 4);
-  else SSC_BK(2, 4);
+  // prefetch depth: as deep as the registers allow without spilling
+  constexpr int D8 = FN >= 8 ? 2 : 3, D4 = FN >= 8 ? 3 : 4;
+  if (FN >= 4 && wg256 >= 512) SSC_BK(8, D8);
+  else if (wg128 >= 256) SSC_BK(4, D4);
+  else SSC_BK(2, D4);
 #undef SSC_BK
 #undef SSC_GO
 }
@@ -1004,7 +1015,7 @@ static int run_bwd(const char* plan, const uint32_t* nmap, const int32_t* perm, 
   if (dbias) {
     float* part = reinterpret_cast<float*>(ws + W.bias);
     colsum_partial<T><<<dim3(unsigned(b.bias_blocks), unsigned((Co + 255) / 256)), 256, 0, s>>>(dY, n, Co, b.bias_rows, part);
-    colsum_final<T><<<unsigned((Co + 255) / 256), 256, 0, s>>>(part, b.bias_blocks, Co, static_cast<T*>(dbias));
+    colsum_final<T><<<unsigned((Co + 63) / 64), 256, 0, s>>>(part, b.bias_blocks, Co, static_cast<T*>(dbias));
   }
   return SSC_OK;
 }

@@ -12,14 +12,18 @@
 //   fill_u32/u64    empty hash slots (all ones)
 //   hash_insert     coordinate check, key packing, open-addressing insert with
 //                   atomicCAS on 32- or 64-bit keys; value = row index
-//   probe           27 lookups per voxel (bounds checked per axis before a key
-//                   is packed, so no off-grid neighbour can alias a real one);
-//                   writes nmap rows through LDS so the stores coalesce, and the
-//                   64-bit sort key (mask << zbits) | zorder
+//   probe_half      one lookup per (voxel, offset k < 13), bounds checked per
+//                   axis before a key is packed (no off-grid neighbour can alias
+//                   a real one); a hit j fills nmap[i][k] and its mirror
+//                   nmap[j][26-k]; the centre entry is the row itself
+//   row_scan        per row: neighbour mask and 64-bit sort key
+//                   (mask << zbits) | zorder; per block: pair-list histogram
 //   radix_hist /    stable LSD radix sort, 8 bits a pass, wave64 ballots rank
-//   radix_scatter   equal digits; the last pass writes perm and sorted masks
-//   pair_count /    per-offset lists of (i, nmap[i][k]) in increasing i, built
-//   pair_scatter    with block counts, a device-wide scan and a stable scatter
+//   radix_scatter   equal digits; the last pass writes perm and sorted masks;
+//                   with few blocks the scatter sums the block histograms itself
+//                   instead of a device-wide scan
+//   pair_scatter    per-offset lists of (i, nmap[i][k]) in increasing i, from the
+//                   row_scan histogram, a device-wide scan and a stable scatter
 //   scan_*          device-wide exclusive scan of uint32 (three kernels)
 
 #include <hip/hip_runtime.h>
@@ -244,45 +248,82 @@ __device__ __forceinline__ uint32_t hash_lookup(const KeyT* __restrict__ keys,
   return kSentinel;
 }
 
-// One thread per voxel: 27 probes, the neighbour mask, and the sort key.
+// One thread per (voxel i, offset k < 13).  nmap[i][k] = j exactly when
+// nmap[j][26-k] = i, so each unordered neighbour pair is looked up once, from
+// the voxel for which its offset lies in the lower half, and both entries are
+// written; every entry no thread writes keeps the sentinel it was filled
+// with.  The centre entry is the row itself.
 template <typename KeyT>
-__global__ void __launch_bounds__(256) probe(const int4* __restrict__ coords, int64_t n, int B, int X,
-                                             int Y, int Z, const KeyT* __restrict__ keys,
-                                             const uint32_t* __restrict__ vals, uint64_t capacity,
-                                             uint32_t* __restrict__ nmap, uint64_t* __restrict__ sort_key,
-                                             int axis_bits, int zbits) {
+__global__ void __launch_bounds__(256) probe_half(const int4* __restrict__ coords, int64_t n, int B, int X,
+                                                  int Y, int Z, const KeyT* __restrict__ keys,
+                                                  const uint32_t* __restrict__ vals, uint64_t capacity,
+                                                  uint32_t* __restrict__ nmap) {
+  const int64_t g = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (g >= n * kCentre) return;
+  const int64_t i = g / kCentre;
+  const int k = int(g - i * kCentre);
+  const int4 c = coords[i];
+  if (!coord_ok(c.x, c.y, c.z, c.w, B, X, Y, Z)) return;
+  if (k == 0) nmap[i * kV + kCentre] = uint32_t(i);
+  const int px = c.y + k / 9 - 1;
+  const int py = c.z + (k / 3) % 3 - 1;
+  const int pz = c.w + k % 3 - 1;
+  if (px < 0 || px >= X || py < 0 || py >= Y || pz < 0 || pz >= Z) return;
+  const uint32_t j = hash_lookup<KeyT>(keys, vals, capacity, KeyT(pack_key(c.x, px, py, pz, X, Y, Z)));
+  if (j == kSentinel) return;
+  nmap[i * kV + k] = j;
+  nmap[int64_t(j) * kV + (kV - 1 - k)] = uint32_t(i);
+}
+
+// Rows of nmap in blocks of kPairRows, read cooperatively through LDS so the
+// loads coalesce.  Per row: the neighbour mask and the 64-bit sort key
+// (mask << zbits) | (b << 3*axis_bits) | zorder(x, y, z).  Per block: the
+// number of valid entries of each offset (the pair-list histogram).
+__global__ void __launch_bounds__(256) row_scan(const int4* __restrict__ coords, const uint32_t* __restrict__ nmap,
+                                                int64_t n, int B, int X, int Y, int Z, int axis_bits, int zbits,
+                                                uint64_t* __restrict__ sort_key, uint32_t* __restrict__ pcnt,
+                                                int64_t pblk) {
   __shared__ uint32_t rows[256 * kV];
-  const int64_t row0 = int64_t(blockIdx.x) * 256;
-  const int64_t i = row0 + threadIdx.x;
-  if (i < n) {
-    const int4 c = coords[i];
-    const bool ok = coord_ok(c.x, c.y, c.z, c.w, B, X, Y, Z);
-    uint32_t mask = 0;
-#pragma unroll 1
-    for (int k = 0; k < kV; ++k) {
-      const int px = c.y + k / 9 - 1;
-      const int py = c.z + (k / 3) % 3 - 1;
-      const int pz = c.w + k % 3 - 1;
-      uint32_t j = kSentinel;
-      if (ok && px >= 0 && px < X && py >= 0 && py < Y && pz >= 0 && pz < Z) {
-        j = hash_lookup<KeyT>(keys, vals, capacity, KeyT(pack_key(c.x, px, py, pz, X, Y, Z)));
+  __shared__ uint32_t cnt[32];
+  if (threadIdx.x < 32) cnt[threadIdx.x] = 0;
+  uint32_t local[kV];
+#pragma unroll
+  for (int k = 0; k < kV; ++k) local[k] = 0;
+  for (int q = 0; q < kPairRows / 256; ++q) {
+    const int64_t row0 = int64_t(blockIdx.x) * kPairRows + q * 256;
+    if (row0 >= n) break;
+    const int64_t here = (n - row0) < 256 ? (n - row0) : 256;
+    __syncthreads();
+    for (int64_t e = threadIdx.x; e < here * kV; e += 256) rows[e] = nmap[row0 * kV + e];
+    __syncthreads();
+    if (threadIdx.x < here) {
+      const int64_t i = row0 + threadIdx.x;
+      uint32_t mask = 0;
+#pragma unroll
+      for (int k = 0; k < kV; ++k) {
+        const bool v = rows[threadIdx.x * kV + k] != kSentinel;
+        mask |= uint32_t(v) << k;
+        local[k] += v ? 1u : 0u;
       }
-      rows[threadIdx.x * kV + k] = j;
-      if (j != kSentinel) mask |= 1u << k;
+      const int4 c = coords[i];
+      uint64_t key = 0;
+      if (coord_ok(c.x, c.y, c.z, c.w, B, X, Y, Z)) {
+        const uint64_t z = (uint64_t(uint32_t(c.x)) << (3 * axis_bits)) |
+                           zorder(uint32_t(c.y), uint32_t(c.z), uint32_t(c.w), axis_bits);
+        key = (uint64_t(mask) << zbits) | z;
+      }
+      sort_key[i] = key;
     }
-    uint64_t key = 0;
-    if (ok) {
-      const uint64_t z = (uint64_t(uint32_t(c.x)) << (3 * axis_bits)) |
-                         zorder(uint32_t(c.y), uint32_t(c.z), uint32_t(c.w), axis_bits);
-      key = (uint64_t(mask) << zbits) | z;
-    }
-    sort_key[i] = key;
+  }
+#pragma unroll
+  for (int k = 0; k < kV; ++k) {
+    uint32_t v = local[k];
+    for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
+    if (__lane_id() == 0) atomicAdd(&cnt[k], v);
   }
   __syncthreads();
-  const int64_t rows_here = (n - row0) < 256 ? (n - row0) : 256;
-  const int64_t words = rows_here * kV;
-  uint32_t* dst = nmap + row0 * kV;
-  for (int64_t e = threadIdx.x; e < words; e += 256) dst[e] = rows[e];
+  if (threadIdx.x < kV) pcnt[int64_t(threadIdx.x) * pblk + blockIdx.x] = cnt[threadIdx.x];
+  if (blockIdx.x == 0 && threadIdx.x == 0) pcnt[kV * pblk] = 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -312,12 +353,27 @@ __global__ void __launch_bounds__(kSortThreads)
     radix_scatter(const uint64_t* __restrict__ keys_in, const uint32_t* __restrict__ vals_in,
                   uint64_t* __restrict__ keys_out, uint32_t* __restrict__ vals_out, int64_t n, int shift,
                   const uint32_t* __restrict__ offsets, int64_t nblk, int first, int last,
-                  int32_t* __restrict__ perm, uint32_t* __restrict__ smask, int zbits) {
+                  int32_t* __restrict__ perm, uint32_t* __restrict__ smask, int zbits, int direct) {
   __shared__ uint32_t base[256];
   __shared__ uint32_t wcnt[kSortThreads / 64][256];
   const int tid = threadIdx.x;
   const int wave = tid / 64;
-  base[tid] = offsets[int64_t(tid) * nblk + blockIdx.x];
+  if (direct) {
+    // few blocks: this block's start for digit tid = (keys of smaller digits) +
+    // (keys of digit tid in earlier blocks), read straight from the histograms
+    __shared__ uint32_t waves_sum[kSortThreads / 64];
+    uint32_t tot = 0, before = 0;
+    for (int64_t b = 0; b < nblk; ++b) {
+      const uint32_t c = offsets[int64_t(tid) * nblk + b];
+      tot += c;
+      if (b < int64_t(blockIdx.x)) before += c;
+    }
+    uint32_t excl;
+    block_exclusive_scan(tot, waves_sum, &excl);
+    base[tid] = excl + before;
+  } else {
+    base[tid] = offsets[int64_t(tid) * nblk + blockIdx.x];
+  }
   const int64_t blk0 = int64_t(blockIdx.x) * kSortBlockKeys;
   for (int q = 0; q < kSortItems; ++q) {
     const int64_t idx = blk0 + int64_t(q) * kSortThreads + tid;
@@ -362,34 +418,6 @@ __global__ void __launch_bounds__(kSortThreads)
 // per-offset pair lists
 // ---------------------------------------------------------------------------
 
-__global__ void __launch_bounds__(256) pair_count(const uint32_t* __restrict__ nmap, int64_t n,
-                                                  uint32_t* __restrict__ pcnt, int64_t pblk) {
-  __shared__ uint32_t cnt[32];
-  if (threadIdx.x < 32) cnt[threadIdx.x] = 0;
-  __syncthreads();
-  const int64_t row0 = int64_t(blockIdx.x) * kPairRows;
-  uint32_t local[kV];
-#pragma unroll
-  for (int k = 0; k < kV; ++k) local[k] = 0;
-  for (int q = 0; q < kPairRows / 256; ++q) {
-    const int64_t row = row0 + q * 256 + threadIdx.x;
-    if (row < n) {
-      const uint32_t* r = nmap + row * kV;
-#pragma unroll
-      for (int k = 0; k < kV; ++k) local[k] += r[k] != kSentinel ? 1u : 0u;
-    }
-  }
-#pragma unroll
-  for (int k = 0; k < kV; ++k) {
-    uint32_t v = local[k];
-    for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
-    if (__lane_id() == 0) atomicAdd(&cnt[k], v);
-  }
-  __syncthreads();
-  if (threadIdx.x < kV) pcnt[int64_t(threadIdx.x) * pblk + blockIdx.x] = cnt[threadIdx.x];
-  if (blockIdx.x == 0 && threadIdx.x == 0) pcnt[kV * pblk] = 0;
-}
-
 __global__ void pair_offsets(const uint32_t* __restrict__ pcnt, int64_t pblk, PlanHeader* h) {
   const int k = threadIdx.x;
   if (k <= kV) h->pair_off[k] = pcnt[int64_t(k) * pblk];
@@ -406,15 +434,20 @@ __global__ void __launch_bounds__(256) pair_scatter(const uint32_t* __restrict__
   const int wave = tid / 64;
   if (tid < kV) base[tid] = pcnt[int64_t(tid) * pblk + blockIdx.x];
   __syncthreads();
-  const int64_t row0 = int64_t(blockIdx.x) * kPairRows;
+  __shared__ uint32_t rows[256 * kV];
   for (int q = 0; q < kPairRows / 256; ++q) {
-    const int64_t row = row0 + q * 256 + tid;
+    const int64_t rbase = int64_t(blockIdx.x) * kPairRows + q * 256;
+    if (rbase >= n) break;
+    const int64_t here = (n - rbase) < 256 ? (n - rbase) : 256;
+    for (int64_t e = tid; e < here * kV; e += 256) rows[e] = nmap[rbase * kV + e];
+    __syncthreads();
+    const int64_t row = rbase + tid;
     const bool in = row < n;
     uint32_t j[kV];
     uint32_t rank[kV];
 #pragma unroll
     for (int k = 0; k < kV; ++k) {
-      j[k] = in ? nmap[row * kV + k] : kSentinel;
+      j[k] = in ? rows[tid * kV + k] : kSentinel;
       const uint64_t b = __ballot(j[k] != kSentinel);
       rank[k] = __popcll(b & lanemask_lt());
       if (__lane_id() == 0) wc[k][wave] = __popcll(b);
@@ -519,21 +552,24 @@ extern "C" int ssc_build_neighbor_map(const int32_t* coords, int64_t n, int32_t 
   const int4* c4 = reinterpret_cast<const int4*>(coords);
 
   const unsigned fill_blocks = 1024;
+  const int64_t pblk = L.pair_blocks;
+  fill_kernel<uint32_t><<<fill_blocks, 256, 0, s>>>(nmap, n * kV, kSentinel);
   if (kb == 64) {
     uint64_t* hkeys = reinterpret_cast<uint64_t*>(base + L.hkeys);
     fill_kernel<uint64_t><<<fill_blocks, 256, 0, s>>>(hkeys, int64_t(L.capacity), ~0ull);
     hash_insert<uint64_t><<<grid1d(n, 256), 256, 0, s>>>(c4, n, B, X, Y, Z, hkeys, hvals, L.capacity,
                                                          &h->status_bits);
-    probe<uint64_t><<<grid1d(n, 256), 256, 0, s>>>(c4, n, B, X, Y, Z, hkeys, hvals, L.capacity, nmap, key0,
-                                                   axis_bits, zbits);
+    probe_half<uint64_t><<<grid1d(n * kCentre, 256), 256, 0, s>>>(c4, n, B, X, Y, Z, hkeys, hvals, L.capacity,
+                                                                  nmap);
   } else {
     uint32_t* hkeys = reinterpret_cast<uint32_t*>(base + L.hkeys);
     fill_kernel<uint32_t><<<fill_blocks, 256, 0, s>>>(hkeys, int64_t(L.capacity), ~0u);
     hash_insert<uint32_t><<<grid1d(n, 256), 256, 0, s>>>(c4, n, B, X, Y, Z, hkeys, hvals, L.capacity,
                                                          &h->status_bits);
-    probe<uint32_t><<<grid1d(n, 256), 256, 0, s>>>(c4, n, B, X, Y, Z, hkeys, hvals, L.capacity, nmap, key0,
-                                                   axis_bits, zbits);
+    probe_half<uint32_t><<<grid1d(n * kCentre, 256), 256, 0, s>>>(c4, n, B, X, Y, Z, hkeys, hvals, L.capacity,
+                                                                  nmap);
   }
+  row_scan<<<unsigned(pblk), 256, 0, s>>>(c4, nmap, n, B, X, Y, Z, axis_bits, zbits, key0, pcnt, pblk);
 
   // radix sort over the key's kV + zbits low bits
   const int bits = kV + zbits;
@@ -546,10 +582,11 @@ extern "C" int ssc_build_neighbor_map(const int32_t* coords, int64_t n, int32_t 
   for (int p = 0; p < passes; ++p) {
     const int shift = 8 * p;
     radix_hist<<<unsigned(nblk), kSortThreads, 0, s>>>(kin, n, shift, hist, nblk);
-    launch_scan(hist, nblk * 256 + 1, scan_tmp, s);
+    const int direct = nblk <= kSortDirectBlocks ? 1 : 0;
+    if (!direct) launch_scan(hist, nblk * 256 + 1, scan_tmp, s);
     radix_scatter<<<unsigned(nblk), kSortThreads, 0, s>>>(kin, vin, kout, vout, n, shift, hist, nblk,
                                                            p == 0 ? 1 : 0, p == passes - 1 ? 1 : 0, perm,
-                                                           smask, zbits);
+                                                           smask, zbits, direct);
     const uint64_t* tk = kout;
     const uint32_t* tv = vout;
     kout = const_cast<uint64_t*>(kin);
@@ -559,8 +596,6 @@ extern "C" int ssc_build_neighbor_map(const int32_t* coords, int64_t n, int32_t 
   }
 
   // per-offset pair lists
-  const int64_t pblk = L.pair_blocks;
-  pair_count<<<unsigned(pblk), 256, 0, s>>>(nmap, n, pcnt, pblk);
   launch_scan(pcnt, pblk * kV + 1, scan_tmp, s);
   pair_offsets<<<1, 64, 0, s>>>(pcnt, pblk, h);
   pair_scatter<<<unsigned(pblk), 256, 0, s>>>(nmap, n, pcnt, pblk, pair_i, pair_j);

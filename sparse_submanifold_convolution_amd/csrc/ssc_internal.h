@@ -24,8 +24,10 @@ constexpr uint32_t kBitHashFull = 4u;
 constexpr int kSortThreads = 256;
 constexpr int kSortItems = 8;
 constexpr int kSortBlockKeys = kSortThreads * kSortItems;
+// up to this many sort blocks, radix_scatter reads the histograms directly
+constexpr int kSortDirectBlocks = 64;
 // pair-list build: rows per workgroup
-constexpr int kPairRows = 1024;
+constexpr int kPairRows = 256;
 // device-wide scan: elements per workgroup
 constexpr int kScanThreads = 256;
 constexpr int kScanItems = 16;
