@@ -40,6 +40,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--config", type=int, default=DEFAULT_CONFIG, choices=[1, 2, 3, 4, 5])
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-graph", action="store_true",
+                   help="time eagerly launched steps instead of replaying one captured HIP graph per step")
     p.add_argument("--cpu-budget-s", type=float, default=20.0)
     p.add_argument("--copy-calib", type=int, default=0,
                    help="only run a device copy of this many MiB (HBM counter calibration)")
@@ -155,12 +157,12 @@ def main():
     db = torch.empty((co,), dtype=X.dtype, device=dev)
     L = ssc.lib()
     stream = torch.cuda.current_stream(dev)
-    sp = ssc.binding._stream(dev)
     P_ = ssc.binding._ptr
 
     def build():
+        # the current stream: the capturing stream while a graph is recorded
         r = L.ssc_build_neighbor_map(P_(coords), n, B_, Xd, Yd, Zd, w.key_bits, P_(plan.nmap), P_(plan.perm),
-                                     P_(plan.buf), pbytes, sp)
+                                     P_(plan.buf), pbytes, ssc.binding._stream(dev))
         if r:
             raise ssc.SSCError("ssc_build_neighbor_map", r)
 
@@ -182,11 +184,15 @@ def main():
     P = sum(counts)
     flops_pass = 2.0 * P * ci * co
 
-    for _ in range(args.warmup):
+    def step():
         for _, f in parts:
             f()
+
+    for _ in range(args.warmup):
+        step()
     torch.cuda.synchronize()
 
+    # per-call times of eagerly launched steps (HIP events on the stream the kernels run on)
     ev = {k: [] for k, _ in parts}
     t0 = time.perf_counter()
     for _ in range(args.steps):
@@ -198,9 +204,34 @@ def main():
             e1.record(stream)
             ev[name].append((e0, e1))
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    wall_eager = time.perf_counter() - t0
     ms = {k: float(np.mean([a.elapsed_time(c) for a, c in v])) for k, v in ev.items()}
-    ms_step = wall * 1e3 / args.steps
+    ms_step_eager = wall_eager * 1e3 / args.steps
+
+    if args.no_graph:
+        ms_step = ms_step_eager
+        mode = "eager launches"
+    else:
+        # the whole step (plan build + fwd + both gradients) captured once and replayed
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            step()
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+        mode = "one captured HIP graph per step"
+        stream = torch.cuda.current_stream(dev)
 
     value = 3 * flops_pass / (ms_step * 1e-3) / 1e12
     esize = X.element_size()
@@ -231,10 +262,11 @@ def main():
         "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": f"config {args.config}: {w.desc}", "voxels": n, "valid_pairs": P, "ci": ci, "co": co,
                    "key_bits": w.key_bits or 32, "step": "neighbour-cache build + fwd + dgrad + wgrad + dbias",
-                   "parallelism": "single GPU"},
+                   "launch": mode, "parallelism": "single GPU"},
         "voxels_per_s": n / (ms_step * 1e-3),
         "conv_only_tflops": 3 * flops_pass / ((ms["fwd"] + ms["dgrad"] + ms["wgrad"]) * 1e-3) / 1e12,
         "breakdown_ms": ms,
+        "ms_per_step_eager": ms_step_eager,
         "roofline": roof,
     }
     if not args.no_cpu_baseline:

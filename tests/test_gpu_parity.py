@@ -252,3 +252,51 @@ def test_config4_sampled(ssc):
 
 def test_config5_sampled(ssc):
     _sampled_parity(ssc, 5)
+
+
+def test_graph_replay_matches_eager(ssc):
+    """A captured step (build + fwd + bwd) replayed several times, with eager work in between, matches eager runs."""
+    w = WL.random_workload(41, 2, (14, 13, 12), 0.3, 64, 64, "f16", random_bias=True)
+    print(f"[case] graph replay n={w.n}", flush=True)
+    dev = DEV
+    coords = torch.from_numpy(w.coords).to(dev)
+    X, W, b, dY = (t.to(dev) for t in (w.feats, w.weight, w.bias, w.dout))
+    ref_plan = ssc.build_neighbor_map(coords, w.shape)
+    ref = [ssc.subm_conv3d_fwd(ref_plan, X, W, b), *ssc.subm_conv3d_bwd(ref_plan, X, W, dY)]
+    torch.cuda.synchronize()
+    B_, Xd, Yd, Zd = w.shape
+    nbytes = ssc.plan_bytes(w.n, w.shape)
+    plan = ssc.Plan(torch.empty((w.n, 27), dtype=torch.int32, device=dev), torch.empty(w.n, dtype=torch.int32, device=dev),
+                    torch.empty(nbytes, dtype=torch.uint8, device=dev), w.n, tuple(w.shape), 0)
+    ws = ssc.workspace(plan, w.ci, w.co, X.dtype)
+    out = torch.empty_like(ref[0]); dX = torch.empty_like(ref[1]); dW = torch.empty_like(ref[2]); db = torch.empty_like(ref[3])
+    L = ssc.lib()
+
+    def step():
+        st = ssc.binding._stream(dev)
+        r = L.ssc_build_neighbor_map(ssc.binding._ptr(coords), w.n, B_, Xd, Yd, Zd, 0, ssc.binding._ptr(plan.nmap),
+                                     ssc.binding._ptr(plan.perm), ssc.binding._ptr(plan.buf), nbytes, st)
+        assert r == 0
+        ssc.subm_conv3d_fwd(plan, X, W, b, out=out, ws=ws)
+        ssc.subm_conv3d_bwd(plan, X, W, dY, ws=ws, outs=(dX, dW, db))
+
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream(dev).wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(3):
+        for t in (out, dX, dW, db, plan.nmap, plan.perm):
+            t.zero_()
+        junk = (X.float() * 2).sum()          # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(plan.nmap, ref_plan.nmap) and torch.equal(plan.perm, ref_plan.perm)
+        for got, r in zip((out, dX, dW, db), ref):
+            assert torch.equal(got, r), f"replay {rep} differs"
+        del junk
