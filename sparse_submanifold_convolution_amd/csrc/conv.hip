@@ -139,11 +139,15 @@ __device__ __forceinline__ typename Elt<T>::frag_t a_frag(const uint4 (&v)[NV], 
   }
 }
 
+// Split-K (nsplit > 1): work item (tile, column block, part) takes the part-th
+// contiguous share of the tile's offset set and writes fp32 partial sums, in
+// sorted row order, to partial[part][row][N]; split_reduce finishes them.
 template <typename T, int FM, int FN, int BK, int NW, int DEPTH, int KMAP>
 __global__ void __launch_bounds__(64 * NW)
     igemm(const T* __restrict__ A, const T* __restrict__ Bt, const T* __restrict__ bias, T* __restrict__ out,
-          const uint32_t* __restrict__ nmap, const int32_t* __restrict__ perm,
-          const uint32_t* __restrict__ smask, int64_t n, int K, int N, int flip, int ntiles, int nblk_n) {
+          const uint32_t* __restrict__ snmap, const int32_t* __restrict__ perm,
+          const uint32_t* __restrict__ smask, int64_t n, int K, int N, int flip, int ntiles, int nblk_n,
+          int nsplit, float* __restrict__ partial) {
   using C = IgemmCfg<T, FM, FN, BK, NW>;
   using E = Elt<T>;
   using frag_t = typename E::frag_t;
@@ -154,15 +158,16 @@ __global__ void __launch_bounds__(64 * NW)
   // XCD-aware order: hardware hands workgroup ids to the 8 XCDs round-robin;
   // give each XCD a contiguous run of (tile, column block) work so that the
   // column blocks of one row tile share that XCD's L2.
-  const int nwork = ntiles * nblk_n;
+  const int nwork = ntiles * nblk_n * nsplit;
   const int per = (nwork + 7) / 8;
   const int work = int(blockIdx.x % 8u) * per + int(blockIdx.x / 8u);
   if (work >= nwork) return;
-  const int tile = work / nblk_n;
-  const int n0 = (work % nblk_n) * BN;
+  const int part = work % nsplit;
+  const int tile = (work / nsplit) / nblk_n;
+  const int n0 = ((work / nsplit) % nblk_n) * BN;
 
   __shared__ __align__(16) char lds_b[2 * C::kLdsB];
-  __shared__ uint32_t jtab[kV][BM];
+  __shared__ uint32_t jtab[BM * kV];  // [row][k]: this tile's rows of the sorted-order map
   __shared__ int32_t prow[BM];
   __shared__ uint32_t tile_union;
 
@@ -173,29 +178,49 @@ __global__ void __launch_bounds__(64 * NW)
   const int64_t row0 = int64_t(tile) * BM;
 
   // ---- prologue: rows, the tile's offset set, gather indices ----
+  // The tile's rows of the sorted-order map are one contiguous block; all of
+  // its loads are issued before any is stored, so the prologue costs one
+  // memory round trip, independent of perm.
+  constexpr int JV = (BM * kV + NT - 1) / NT;
+  uint32_t jv[JV];
+  const int64_t jbase = row0 * kV, jend = n * kV;
+#pragma unroll
+  for (int q = 0; q < JV; ++q) {
+    const int64_t e = jbase + q * NT + tid;
+    jv[q] = (q * NT + tid < BM * kV && e < jend) ? snmap[e] : kSentinel;
+  }
   if (tid == 0) tile_union = 0;
-  __syncthreads();
-  for (int r = tid; r < BM; r += NT) {
-    const int64_t g = row0 + r;
-    int32_t p = -1;
-    uint32_t m = 0;
+  int32_t pr = -1;
+  uint32_t msk = 0;
+  if (tid < BM) {
+    const int64_t g = row0 + tid;
     if (g < n) {
-      p = perm[g];
-      m = smask[g];
-    }
-    prow[r] = p;
-    if (m) atomicOr(&tile_union, m);
-  }
-  __syncthreads();
-  const uint32_t uni = tile_union;
-  for (int e = tid; e < kV * BM; e += NT) {
-    const int k = e / BM, r = e - k * BM;
-    if ((uni >> k) & 1u) {
-      const int32_t p = prow[r];
-      jtab[k][r] = p >= 0 ? nmap[int64_t(p) * kV + k] : kSentinel;
+      pr = perm[g];
+      msk = smask[g];
     }
   }
+#pragma unroll
+  for (int q = 0; q < JV; ++q)
+    if (q * NT + tid < BM * kV) jtab[q * NT + tid] = jv[q];
   __syncthreads();
+  if (tid < BM) {
+    prow[tid] = pr;
+    if (msk) atomicOr(&tile_union, msk);
+  }
+  __syncthreads();
+  uint32_t uni = tile_union;
+  if (nsplit > 1) {
+    // keep this part's contiguous share of the offsets (in increasing k)
+    const int cnt = __popc(uni);
+    const int lo = part * cnt / nsplit, hi = (part + 1) * cnt / nsplit;
+    uint32_t keep = 0, rest = uni;
+    for (int r = 0; rest; ++r) {
+      const uint32_t bit = rest & (0u - rest);
+      if (r >= lo && r < hi) keep |= bit;
+      rest ^= bit;
+    }
+    uni = keep;
+  }
 
   f32x16 acc[FM][FN];
 #pragma unroll
@@ -232,7 +257,7 @@ __global__ void __launch_bounds__(64 * NW)
     constexpr int vstride = KMAP == 0 ? 1 : 2;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
-      const uint32_t j = jtab[a_k][wave * FM * 32 + i * 32 + (lane & 31)];
+      const uint32_t j = jtab[(wave * FM * 32 + i * 32 + (lane & 31)) * kV + a_k];
       if (j != kSentinel) {
         const uint4* src = reinterpret_cast<const uint4*>(A + int64_t(j) * K + c0);
 #pragma unroll
@@ -315,6 +340,24 @@ __global__ void __launch_bounds__(64 * NW)
     }
   }
 
+  if (nsplit > 1) {
+    // fp32 partials in sorted row order; bias, rounding and perm come later
+    float* dst = partial + int64_t(part) * n * N;
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int c = n0 + j * 32 + (lane & 31);
+      if (c >= N) continue;
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int64_t g = row0 + wave * FM * 32 + i * 32 + acc_row(lane, e);
+          if (g < n) dst[g * N + c] = acc[i][j][e];
+        }
+    }
+    return;
+  }
+
   // ---- epilogue: bias, round once, scatter rows to perm ----
 #pragma unroll
   for (int j = 0; j < FN; ++j) {
@@ -347,6 +390,21 @@ __global__ void __launch_bounds__(256) transpose_w(const T* __restrict__ W, T* _
   __syncthreads();
   for (int r = ty; r < 32; r += 8)
     if (c0 + r < N && r0 + tx < K) dst[int64_t(c0 + r) * K + r0 + tx] = tile[tx][r];
+}
+
+// out[perm[r]][c] = bias[c] + sum over parts, in part order, of partial[part][r][c]
+template <typename T>
+__global__ void __launch_bounds__(256) split_reduce(const float* __restrict__ partial, int nsplit, int64_t n, int N,
+                                                    const T* __restrict__ bias, const int32_t* __restrict__ perm,
+                                                    T* __restrict__ out) {
+  const int64_t e = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (e >= n * N) return;
+  const int64_t r = e / N;
+  const int c = int(e - r * N);
+  float s = 0.f;
+  for (int p = 0; p < nsplit; ++p) s += partial[int64_t(p) * n * N + e];
+  if (bias) s += Elt<T>::load(bias[c]);
+  out[int64_t(perm[r]) * N + c] = Elt<T>::store(s);
 }
 
 // ---------------------------------------------------------------------------
@@ -814,6 +872,18 @@ __global__ void zero_kernel(T* __restrict__ p, int64_t count) {
 // host-side configuration
 // ---------------------------------------------------------------------------
 
+// Offset-set parts per tile: only tiny problems (fewer than 128 of the
+// smallest tiles) split each tile's offsets over up to 4 workgroups; measured
+// on MI355X, a 2k-voxel layer runs 1.9x faster split four ways while a
+// 24k-voxel layer (381 tiles) runs faster unsplit.
+static int split_parts(int64_t n, int N) {
+  const int64_t nblk = N > 128 ? (N + 255) / 256 : (N > 64 ? (N + 127) / 128 : (N > 32 ? (N + 63) / 64 : 1));
+  const int64_t wg = (n + 63) / 64 * nblk;  // the smallest-tile count igemm_pick_rows may launch
+  if (n == 0 || wg >= 128) return 1;
+  int64_t sp = (512 + wg - 1) / wg;
+  return int(sp > 4 ? 4 : sp);
+}
+
 // Weight-gradient tile edge for a channel count: fp32 uses the LDS-transposing
 // kernel (up to 128), 16-bit types the transpose-read kernel (up to 256).
 static int wgrad_tile(int c, int esize) {
@@ -855,7 +925,7 @@ static BwdShape bwd_shape(int64_t n, int Ci, int Co, int esize) {
 }
 
 struct WsLayout {
-  size_t wt = 0, partial = 0, bias = 0, total = 0;
+  size_t wt = 0, partial = 0, bias = 0, split = 0, total = 0;
 };
 
 static WsLayout ws_layout(int64_t n, int Ci, int Co, int esize) {
@@ -868,6 +938,12 @@ static WsLayout ws_layout(int64_t n, int Ci, int Co, int esize) {
   off = align_up(off + size_t(kV) * b.max_chunks * size_t(Ci) * Co * 4, 256);
   w.bias = off;
   off = align_up(off + size_t(b.bias_blocks) * Co * 4, 256);
+  // Split-K partials of the forward (N = Co) or input-gradient (N = Ci) GEMM
+  const int sf = split_parts(n, Co), sd = split_parts(n, Ci);
+  const size_t sbytes_f = sf > 1 ? size_t(sf) * size_t(n) * Co * 4 : 0;
+  const size_t sbytes_d = sd > 1 ? size_t(sd) * size_t(n) * Ci * 4 : 0;
+  w.split = off;
+  off = align_up(off + (sbytes_f > sbytes_d ? sbytes_f : sbytes_d), 256);
   w.total = off;
   return w;
 }
@@ -880,14 +956,17 @@ static bool channels_ok(int Ci, int Co) {
 
 template <typename T, int FM, int FN, int BK, int NW, int DEPTH, int KMAP>
 static void igemm_go(const T* A, const T* Bt, const T* bias, T* out, const uint32_t* nmap, const int32_t* perm,
-                     const uint32_t* smask, int64_t n, int K, int N, int flip, hipStream_t s) {
+                     const uint32_t* smask, int64_t n, int K, int N, int flip, float* partial, hipStream_t s) {
   constexpr int BM = NW * FM * 32, BN = FN * 32;
   const int ntiles = int((n + BM - 1) / BM);
   const int nblk = (N + BN - 1) / BN;
-  const int nwork = ntiles * nblk;
+  const int nsplit = split_parts(n, N);
+  const int nwork = ntiles * nblk * nsplit;
   const unsigned grid = unsigned((nwork + 7) / 8 * 8);
   igemm<T, FM, FN, BK, NW, DEPTH, KMAP><<<grid, 64 * NW, 0, s>>>(A, Bt, bias, out, nmap, perm, smask, n, K, N,
-                                                                flip, ntiles, nblk);
+                                                                flip, ntiles, nblk, nsplit, partial);
+  if (nsplit > 1)
+    split_reduce<T><<<unsigned((n * N + 255) / 256), 256, 0, s>>>(partial, nsplit, n, N, bias, perm, out);
 }
 
 // Tile choice (measured on MI355X, see the tuning notes): every wave owns 32
@@ -898,11 +977,11 @@ static void igemm_go(const T* A, const T* Bt, const T* bias, T* out, const uint3
 template <typename T, int FN>
 static void igemm_pick_rows(const T* A, const T* Bt, const T* bias, T* out, const uint32_t* nmap,
                             const int32_t* perm, const uint32_t* smask, int64_t n, int K, int N, int flip,
-                            hipStream_t s) {
+                            float* partial, hipStream_t s) {
   const int64_t nblk = (N + FN * 32 - 1) / (FN * 32);
   const int64_t wg256 = (n + 255) / 256 * nblk, wg128 = (n + 127) / 128 * nblk;
 #define SSC_GO(NW, BK, DEPTH, KMAP) \
-  igemm_go<T, 1, FN, BK, NW, DEPTH, KMAP>(A, Bt, bias, out, nmap, perm, smask, n, K, N, flip, s)
+  igemm_go<T, 1, FN, BK, NW, DEPTH, KMAP>(A, Bt, bias, out, nmap, perm, smask, n, K, N, flip, partial, s)
 #define SSC_BK(NW, DEPTH)                                                 \
   do {                                                                    \
     if constexpr (sizeof(T) == 4) {                                       \
@@ -925,11 +1004,11 @@ static void igemm_pick_rows(const T* A, const T* Bt, const T* bias, T* out, cons
 template <typename T>
 static void launch_igemm(const T* A, const T* Bt, const T* bias, T* out, const uint32_t* nmap,
                          const int32_t* perm, const uint32_t* smask, int64_t n, int K, int N, int flip,
-                         hipStream_t s) {
-  if (N > 128) igemm_pick_rows<T, 8>(A, Bt, bias, out, nmap, perm, smask, n, K, N, flip, s);
-  else if (N > 64) igemm_pick_rows<T, 4>(A, Bt, bias, out, nmap, perm, smask, n, K, N, flip, s);
-  else if (N > 32) igemm_pick_rows<T, 2>(A, Bt, bias, out, nmap, perm, smask, n, K, N, flip, s);
-  else igemm_pick_rows<T, 1>(A, Bt, bias, out, nmap, perm, smask, n, K, N, flip, s);
+                         float* partial, hipStream_t s) {
+  if (N > 128) igemm_pick_rows<T, 8>(A, Bt, bias, out, nmap, perm, smask, n, K, N, flip, partial, s);
+  else if (N > 64) igemm_pick_rows<T, 4>(A, Bt, bias, out, nmap, perm, smask, n, K, N, flip, partial, s);
+  else if (N > 32) igemm_pick_rows<T, 2>(A, Bt, bias, out, nmap, perm, smask, n, K, N, flip, partial, s);
+  else igemm_pick_rows<T, 1>(A, Bt, bias, out, nmap, perm, smask, n, K, N, flip, partial, s);
 }
 
 template <typename T>
@@ -985,8 +1064,10 @@ static int run_fwd(const char* plan, const uint32_t* nmap, const int32_t* perm, 
   T* wt = reinterpret_cast<T*>(ws + W.wt);
   dim3 tg(unsigned((Co + 31) / 32), unsigned((Ci + 31) / 32), kV);
   transpose_w<T><<<tg, 256, 0, s>>>(static_cast<const T*>(weight), wt, Ci, Co);
-  launch_igemm<T>(static_cast<const T*>(feats), wt, static_cast<const T*>(bias), static_cast<T*>(out), nmap,
-                  perm, reinterpret_cast<const uint32_t*>(plan + L.smask), n, Ci, Co, 0, s);
+  launch_igemm<T>(static_cast<const T*>(feats), wt, static_cast<const T*>(bias), static_cast<T*>(out),
+                  reinterpret_cast<const uint32_t*>(plan + L.snmap), perm,
+                  reinterpret_cast<const uint32_t*>(plan + L.smask), n, Ci, Co, 0,
+                  reinterpret_cast<float*>(ws + W.split), s);
   return SSC_OK;
 }
 
@@ -1001,8 +1082,10 @@ static int run_bwd(const char* plan, const uint32_t* nmap, const int32_t* perm, 
   const T* dY = static_cast<const T*>(dout);
   if (dfeats) {
     // dX = masked implicit GEMM of dY with B[k] = W[26-k] read as [Ci][Co] (K = Co, N = Ci)
-    launch_igemm<T>(dY, static_cast<const T*>(weight), nullptr, static_cast<T*>(dfeats), nmap, perm,
-                    reinterpret_cast<const uint32_t*>(plan + L.smask), n, Co, Ci, 1, s);
+    launch_igemm<T>(dY, static_cast<const T*>(weight), nullptr, static_cast<T*>(dfeats),
+                    reinterpret_cast<const uint32_t*>(plan + L.snmap), perm,
+                    reinterpret_cast<const uint32_t*>(plan + L.smask), n, Co, Ci, 1,
+                    reinterpret_cast<float*>(ws + W.split), s);
   }
   if (dweight) {
     float* part = reinterpret_cast<float*>(ws + W.partial);

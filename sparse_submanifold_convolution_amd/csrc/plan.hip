@@ -8,8 +8,8 @@
 // (sorted_idx) so that tiles of rows share their valid offsets.
 //
 // Kernels, in launch order:
-//   plan_init       header fields, status word, pair counters
-//   fill_u32/u64    empty hash slots (all ones)
+//   plan_prepare    header fields, status word, pair counters; sentinel fill
+//                   of nmap; empty (all ones) fill of the hash keys
 //   hash_insert     coordinate check, key packing, open-addressing insert with
 //                   atomicCAS on 32- or 64-bit keys; value = row index
 //   probe_half      one lookup per (voxel, offset k < 13), bounds checked per
@@ -22,6 +22,7 @@
 //   radix_scatter   equal digits; the last pass writes perm and sorted masks;
 //                   with few blocks the scatter sums the block histograms itself
 //                   instead of a device-wide scan
+//   permute_rows    the map in sorted row order (tiles read it contiguously)
 //   pair_scatter    per-offset lists of (i, nmap[i][k]) in increasing i, from the
 //                   row_scan histogram, a device-wide scan and a stable scatter
 //   scan_*          device-wide exclusive scan of uint32 (three kernels)
@@ -176,31 +177,34 @@ static void launch_scan(uint32_t* data, int64_t len, uint32_t* tmp, hipStream_t 
 // header, fills, hash insert, probe
 // ---------------------------------------------------------------------------
 
-__global__ void plan_init(PlanHeader* h, int64_t n, int B, int X, int Y, int Z, int key_bits,
-                          int zbits, uint64_t capacity) {
-  if (threadIdx.x == 0) {
-    h->magic = kPlanMagic;
-    h->status_bits = 0;
-    h->n = n;
-    h->dims[0] = B;
-    h->dims[1] = X;
-    h->dims[2] = Y;
-    h->dims[3] = Z;
-    h->key_bits = key_bits;
-    h->zbits = zbits;
-    h->capacity = capacity;
+// Header fields, status word and pair counters (block 0), the sentinel fill of
+// nmap and the empty fill of the hash keys, in one grid-stride kernel.
+template <typename KeyT>
+__global__ void __launch_bounds__(256) plan_prepare(PlanHeader* h, int64_t n, int B, int X, int Y, int Z,
+                                                   int key_bits, int zbits, uint64_t capacity,
+                                                   uint32_t* __restrict__ nmap, KeyT* __restrict__ keys) {
+  if (blockIdx.x == 0) {
+    if (threadIdx.x == 0) {
+      h->magic = kPlanMagic;
+      h->status_bits = 0;
+      h->n = n;
+      h->dims[0] = B;
+      h->dims[1] = X;
+      h->dims[2] = Y;
+      h->dims[3] = Z;
+      h->key_bits = key_bits;
+      h->zbits = zbits;
+      h->capacity = capacity;
+    }
+    if (threadIdx.x < 32) {
+      h->pair_count[threadIdx.x] = 0;
+      h->pair_off[threadIdx.x] = 0;
+    }
   }
-  if (threadIdx.x < 32) {
-    h->pair_count[threadIdx.x] = 0;
-    h->pair_off[threadIdx.x] = 0;
-  }
-}
-
-template <typename T>
-__global__ void fill_kernel(T* __restrict__ p, int64_t count, T v) {
-  int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   const int64_t stride = int64_t(gridDim.x) * blockDim.x;
-  for (; i < count; i += stride) p[i] = v;
+  const int64_t t0 = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  for (int64_t i = t0; i < n * kV; i += stride) nmap[i] = kSentinel;
+  for (int64_t i = t0; i < int64_t(capacity); i += stride) keys[i] = empty_key<KeyT>();
 }
 
 template <typename KeyT>
@@ -414,6 +418,18 @@ __global__ void __launch_bounds__(kSortThreads)
   }
 }
 
+// snmap[r] = nmap[perm[r]]: the map in sorted row order, so that a tile of
+// consecutive sorted rows reads its gather indices as one contiguous block.
+__global__ void __launch_bounds__(256) permute_rows(const uint32_t* __restrict__ nmap,
+                                                    const int32_t* __restrict__ perm, int64_t n,
+                                                    uint32_t* __restrict__ snmap) {
+  const int64_t e = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (e >= n * kV) return;
+  const int64_t r = e / kV;
+  const int k = int(e - r * kV);
+  snmap[e] = nmap[int64_t(perm[r]) * kV + k];
+}
+
 // ---------------------------------------------------------------------------
 // per-offset pair lists
 // ---------------------------------------------------------------------------
@@ -424,15 +440,56 @@ __global__ void pair_offsets(const uint32_t* __restrict__ pcnt, int64_t pblk, Pl
   if (k < kV) h->pair_count[k] = pcnt[int64_t(k + 1) * pblk] - pcnt[int64_t(k) * pblk];
 }
 
+// pcnt holds scanned offsets (direct = 0) or raw per-block counts (direct = 1:
+// few blocks, each block sums the counts itself and block 0 fills the header).
 __global__ void __launch_bounds__(256) pair_scatter(const uint32_t* __restrict__ nmap, int64_t n,
                                                     const uint32_t* __restrict__ pcnt, int64_t pblk,
                                                     uint32_t* __restrict__ pair_i,
-                                                    uint32_t* __restrict__ pair_j) {
+                                                    uint32_t* __restrict__ pair_j, int direct,
+                                                    PlanHeader* __restrict__ h) {
   __shared__ uint32_t base[32];
+  __shared__ uint32_t tot[32];
   __shared__ uint32_t wc[kV][4];
   const int tid = threadIdx.x;
   const int wave = tid / 64;
-  if (tid < kV) base[tid] = pcnt[int64_t(tid) * pblk + blockIdx.x];
+  if (direct) {
+    // offset k = tid / 8 summed over blocks b = tid % 8 (mod 8), then the 8 sums in order
+    __shared__ uint32_t part_t[kV][8], part_b[kV][8];
+    if (tid < kV * 8) {
+      const int k = tid >> 3, ph = tid & 7;
+      uint32_t t = 0, before = 0;
+      for (int64_t b = ph; b < pblk; b += 8) {
+        const uint32_t c = pcnt[int64_t(k) * pblk + b];
+        t += c;
+        if (b < int64_t(blockIdx.x)) before += c;
+      }
+      part_t[k][ph] = t;
+      part_b[k][ph] = before;
+    }
+    __syncthreads();
+    if (tid < kV) {
+      uint32_t t = 0, before = 0;
+      for (int ph = 0; ph < 8; ++ph) {
+        t += part_t[tid][ph];
+        before += part_b[tid][ph];
+      }
+      tot[tid] = t;
+      base[tid] = before;
+    }
+    __syncthreads();
+    if (tid < kV) {
+      uint32_t off = 0;
+      for (int k = 0; k < tid; ++k) off += tot[k];
+      base[tid] += off;
+      if (blockIdx.x == 0) {
+        h->pair_off[tid] = off;
+        h->pair_count[tid] = tot[tid];
+        if (tid == kV - 1) h->pair_off[kV] = off + tot[tid];
+      }
+    }
+  } else if (tid < kV) {
+    base[tid] = pcnt[int64_t(tid) * pblk + blockIdx.x];
+  }
   __syncthreads();
   __shared__ uint32_t rows[256 * kV];
   for (int q = 0; q < kPairRows / 256; ++q) {
@@ -535,8 +592,12 @@ extern "C" int ssc_build_neighbor_map(const int32_t* coords, int64_t n, int32_t 
   char* base = static_cast<char*>(plan);
   PlanHeader* h = reinterpret_cast<PlanHeader*>(base + L.header);
   (void)hipGetLastError();
-  plan_init<<<1, 64, 0, s>>>(h, n, B, X, Y, Z, kb, zbits, L.capacity);
-  if (n == 0) return hipGetLastError() == hipSuccess ? SSC_OK : SSC_ERR_HIP;
+  if (n == 0) {
+    // header only (the key fill touches the plan's own table region)
+    plan_prepare<uint32_t><<<1, 256, 0, s>>>(h, 0, B, X, Y, Z, kb, zbits, L.capacity, nullptr,
+                                             reinterpret_cast<uint32_t*>(base + L.hkeys));
+    return hipGetLastError() == hipSuccess ? SSC_OK : SSC_ERR_HIP;
+  }
 
   uint32_t* smask = reinterpret_cast<uint32_t*>(base + L.smask);
   uint32_t* pair_i = reinterpret_cast<uint32_t*>(base + L.pair_i);
@@ -551,19 +612,19 @@ extern "C" int ssc_build_neighbor_map(const int32_t* coords, int64_t n, int32_t 
   uint32_t* scan_tmp = reinterpret_cast<uint32_t*>(base + L.scan_tmp);
   const int4* c4 = reinterpret_cast<const int4*>(coords);
 
-  const unsigned fill_blocks = 1024;
   const int64_t pblk = L.pair_blocks;
-  fill_kernel<uint32_t><<<fill_blocks, 256, 0, s>>>(nmap, n * kV, kSentinel);
+  const unsigned prep_blocks = grid1d((n * kV > int64_t(L.capacity) ? n * kV : int64_t(L.capacity)) / 4, 256);
+  const unsigned prep = prep_blocks < 2048 ? prep_blocks : 2048;
   if (kb == 64) {
     uint64_t* hkeys = reinterpret_cast<uint64_t*>(base + L.hkeys);
-    fill_kernel<uint64_t><<<fill_blocks, 256, 0, s>>>(hkeys, int64_t(L.capacity), ~0ull);
+    plan_prepare<uint64_t><<<prep, 256, 0, s>>>(h, n, B, X, Y, Z, kb, zbits, L.capacity, nmap, hkeys);
     hash_insert<uint64_t><<<grid1d(n, 256), 256, 0, s>>>(c4, n, B, X, Y, Z, hkeys, hvals, L.capacity,
                                                          &h->status_bits);
     probe_half<uint64_t><<<grid1d(n * kCentre, 256), 256, 0, s>>>(c4, n, B, X, Y, Z, hkeys, hvals, L.capacity,
                                                                   nmap);
   } else {
     uint32_t* hkeys = reinterpret_cast<uint32_t*>(base + L.hkeys);
-    fill_kernel<uint32_t><<<fill_blocks, 256, 0, s>>>(hkeys, int64_t(L.capacity), ~0u);
+    plan_prepare<uint32_t><<<prep, 256, 0, s>>>(h, n, B, X, Y, Z, kb, zbits, L.capacity, nmap, hkeys);
     hash_insert<uint32_t><<<grid1d(n, 256), 256, 0, s>>>(c4, n, B, X, Y, Z, hkeys, hvals, L.capacity,
                                                          &h->status_bits);
     probe_half<uint32_t><<<grid1d(n * kCentre, 256), 256, 0, s>>>(c4, n, B, X, Y, Z, hkeys, hvals, L.capacity,
@@ -579,10 +640,10 @@ extern "C" int ssc_build_neighbor_map(const int32_t* coords, int64_t n, int32_t 
   const uint32_t* vin = val0;
   uint64_t* kout = key1;
   uint32_t* vout = val1;
+  const int direct = nblk <= kSortDirectBlocks ? 1 : 0;
   for (int p = 0; p < passes; ++p) {
     const int shift = 8 * p;
     radix_hist<<<unsigned(nblk), kSortThreads, 0, s>>>(kin, n, shift, hist, nblk);
-    const int direct = nblk <= kSortDirectBlocks ? 1 : 0;
     if (!direct) launch_scan(hist, nblk * 256 + 1, scan_tmp, s);
     radix_scatter<<<unsigned(nblk), kSortThreads, 0, s>>>(kin, vin, kout, vout, n, shift, hist, nblk,
                                                            p == 0 ? 1 : 0, p == passes - 1 ? 1 : 0, perm,
@@ -595,10 +656,15 @@ extern "C" int ssc_build_neighbor_map(const int32_t* coords, int64_t n, int32_t 
     vin = tv;
   }
 
+  permute_rows<<<grid1d(n * kV, 256), 256, 0, s>>>(nmap, perm, n, reinterpret_cast<uint32_t*>(base + L.snmap));
+
   // per-offset pair lists
-  launch_scan(pcnt, pblk * kV + 1, scan_tmp, s);
-  pair_offsets<<<1, 64, 0, s>>>(pcnt, pblk, h);
-  pair_scatter<<<unsigned(pblk), 256, 0, s>>>(nmap, n, pcnt, pblk, pair_i, pair_j);
+  const int pdirect = pblk <= kPairDirectBlocks ? 1 : 0;
+  if (!pdirect) {
+    launch_scan(pcnt, pblk * kV + 1, scan_tmp, s);
+    pair_offsets<<<1, 64, 0, s>>>(pcnt, pblk, h);
+  }
+  pair_scatter<<<unsigned(pblk), 256, 0, s>>>(nmap, n, pcnt, pblk, pair_i, pair_j, pdirect, h);
 
   return hipGetLastError() == hipSuccess ? SSC_OK : SSC_ERR_HIP;
 }

@@ -28,6 +28,8 @@ constexpr int kSortBlockKeys = kSortThreads * kSortItems;
 constexpr int kSortDirectBlocks = 64;
 // pair-list build: rows per workgroup
 constexpr int kPairRows = 256;
+// up to this many pair-list blocks, pair_scatter sums the block counts itself
+constexpr int kPairDirectBlocks = 256;
 // device-wide scan: elements per workgroup
 constexpr int kScanThreads = 256;
 constexpr int kScanItems = 16;
@@ -59,6 +61,7 @@ inline int ceil_log2_u64(uint64_t v) {
 struct PlanLayout {
   size_t header = 0;
   size_t smask = 0;   // [n] u32: neighbour mask of the row at each sorted position
+  size_t snmap = 0;   // [n][27] u32: nmap rows in sorted order, snmap[r] = nmap[perm[r]]
   size_t pair_i = 0;  // [27n] u32: pair lists, output row i
   size_t pair_j = 0;  // [27n] u32: pair lists, input row j = nmap[i][k]
   // build-only scratch
@@ -81,6 +84,7 @@ inline PlanLayout conv_layout(int64_t n) {
   };
   L.header = 0;
   L.smask = take(size_t(n) * 4);
+  L.snmap = take(size_t(n) * kV * 4);
   L.pair_i = take(size_t(n) * kV * 4);
   L.pair_j = take(size_t(n) * kV * 4);
   L.total = off;
