@@ -91,6 +91,23 @@ struct Elt<bf16s> {
   __device__ static float load(bf16s v) { return bf16_to_f32(v.bits); }
 };
 
+// Workgroup ids reach the 8 XCDs round-robin.  Work that shares data comes in
+// groups of `members` items (the column blocks of one row tile, the channel
+// tiles of one pair chunk); a group's items go to consecutive slots of one XCD
+// so they share its L2, and whole groups are dealt to the XCDs in turn so
+// neighbouring groups (similar cost) spread over all of them.  Launch
+// 8 * ceil(groups / 8) * members workgroups; returns false for the padding.
+__device__ __forceinline__ bool xcd_group_work(int groups, int members, int* group, int* member) {
+  const int x = int(blockIdx.x % 8u), slot = int(blockIdx.x / 8u);
+  *group = x + 8 * (slot / members);
+  *member = slot % members;
+  return *group < groups;
+}
+
+static inline unsigned xcd_group_grid(int groups, int members) {
+  return unsigned((groups + 7) / 8) * 8u * unsigned(members);
+}
+
 // Row index inside a 32x32 MFMA accumulator block held by `lane`, register i.
 __device__ __forceinline__ int acc_row(int lane, int i) { return (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3); }
 
@@ -155,16 +172,11 @@ __global__ void __launch_bounds__(64 * NW)
   constexpr int BM = C::kBM, BN = C::kBN, NV = C::kNV;
   static_assert(KMAP == 0 || sizeof(T) == 2, "the natural order needs one 16-byte load per MFMA fragment");
 
-  // XCD-aware order: hardware hands workgroup ids to the 8 XCDs round-robin;
-  // give each XCD a contiguous run of (tile, column block) work so that the
-  // column blocks of one row tile share that XCD's L2.
-  const int nwork = ntiles * nblk_n * nsplit;
-  const int per = (nwork + 7) / 8;
-  const int work = int(blockIdx.x % 8u) * per + int(blockIdx.x / 8u);
-  if (work >= nwork) return;
-  const int part = work % nsplit;
-  const int tile = (work / nsplit) / nblk_n;
-  const int n0 = ((work / nsplit) % nblk_n) * BN;
+  // the column blocks (and Split-K parts) of one row tile run on one XCD
+  int tile, member;
+  if (!xcd_group_work(ntiles, nblk_n * nsplit, &tile, &member)) return;
+  const int part = member % nsplit;
+  const int n0 = (member / nsplit) * BN;
 
   __shared__ __align__(16) char lds_b[2 * C::kLdsB];
   __shared__ uint32_t jtab[BM * kV];  // [row][k]: this tile's rows of the sorted-order map
@@ -623,23 +635,28 @@ template <typename T, int FM, int FN, int NWM, int NWN, int BKP, int DEPTH>
 __global__ void __launch_bounds__(64 * NWM * NWN)
     wgrad_tr(const T* __restrict__ X, const T* __restrict__ dY, const uint32_t* __restrict__ pair_i,
              const uint32_t* __restrict__ pair_j, const PlanHeader* __restrict__ hdr, float* __restrict__ partial,
-             int Ci, int Co, int64_t chunk_len, int max_chunks, int ntiles_n) {
+             int Ci, int Co, int64_t chunk_len, int max_chunks, int ntiles_m, int ntiles_n) {
   using C = WgradTrCfg<T, FM, FN, NWM, NWN, BKP>;
   using E = Elt<T>;
   using frag_t = typename E::frag_t;
   constexpr int NT = C::kThreads, BM = C::kBM, BN = C::kBN, SG = C::kSG, GP = C::kGP;
   static_assert(DEPTH >= 1 && DEPTH < C::kSG, "prefetch depth must stay inside one index group");
 
-  const int chunk = blockIdx.x;
-  const int k = blockIdx.y;
+  // the channel tiles of one (offset, chunk) run together on one XCD, so the
+  // pair rows they all gather are shared in its L2; groups cycle through the
+  // offsets first so every XCD gets a mix of dense and sparse offsets
+  int g, mn;
+  if (!xcd_group_work(kV * max_chunks, ntiles_m * ntiles_n, &g, &mn)) return;
+  const int k = g % kV;
+  const int chunk = g / kV;
   const int64_t pk = hdr->pair_count[k];
   const int64_t start = int64_t(chunk) * chunk_len;
   if (start >= pk) return;
   const int64_t end = (start + chunk_len < pk) ? start + chunk_len : pk;
   const int64_t off = hdr->pair_off[k];
   const int64_t pbeg = off + start, pend = off + end;
-  const int m0 = (blockIdx.z / ntiles_n) * BM;
-  const int c0 = (blockIdx.z % ntiles_n) * BN;
+  const int m0 = (mn / ntiles_n) * BM;
+  const int c0 = (mn % ntiles_n) * BN;
 
   __shared__ __align__(16) char lds_a[2 * C::kLdsA];
   __shared__ __align__(16) char lds_b[2 * C::kLdsB];
@@ -961,8 +978,7 @@ static void igemm_go(const T* A, const T* Bt, const T* bias, T* out, const uint3
   const int ntiles = int((n + BM - 1) / BM);
   const int nblk = (N + BN - 1) / BN;
   const int nsplit = split_parts(n, N);
-  const int nwork = ntiles * nblk * nsplit;
-  const unsigned grid = unsigned((nwork + 7) / 8 * 8);
+  const unsigned grid = xcd_group_grid(ntiles, nblk * nsplit);
   igemm<T, FM, FN, BK, NW, DEPTH, KMAP><<<grid, 64 * NW, 0, s>>>(A, Bt, bias, out, nmap, perm, smask, n, K, N,
                                                                 flip, ntiles, nblk, nsplit, partial);
   if (nsplit > 1)
@@ -1016,9 +1032,10 @@ static void launch_wgrad(const T* X, const T* dY, const uint32_t* pi, const uint
                          float* partial, int Ci, int Co, const BwdShape& b, hipStream_t s) {
   dim3 grid(unsigned(b.max_chunks), kV, unsigned(b.mt * b.nt));
   if constexpr (sizeof(T) == 2) {
-#define SSC_WTR(FM, FN, NWM, NWN)                                                                      \
-  wgrad_tr<T, FM, FN, NWM, NWN, 32, 2><<<grid, 64 * NWM * NWN, 0, s>>>(X, dY, pi, pj, h, partial, Ci, Co, \
-                                                                      b.chunk_len, b.max_chunks, b.nt)
+    const dim3 grid1(xcd_group_grid(kV * b.max_chunks, b.mt * b.nt));
+#define SSC_WTR(FM, FN, NWM, NWN)                                                                        \
+  wgrad_tr<T, FM, FN, NWM, NWN, 32, 2><<<grid1, 64 * NWM * NWN, 0, s>>>(X, dY, pi, pj, h, partial, Ci, Co, \
+                                                                       b.chunk_len, b.max_chunks, b.mt, b.nt)
     if (b.bm == 256) SSC_WTR(2, 4, 4, 2);
     else if (b.bm == 128) SSC_WTR(2, 2, 2, 2);
     else if (b.bm == 64) SSC_WTR(1, 1, 2, 2);
