@@ -104,6 +104,9 @@ __device__ __forceinline__ bool xcd_group_work(int groups, int members, int* gro
   return *group < groups;
 }
 
+// consecutive row tiles grouped per XCD when a tile is a single work item
+constexpr int kTileGroup = 4;
+
 static inline unsigned xcd_group_grid(int groups, int members) {
   return unsigned((groups + 7) / 8) * 8u * unsigned(members);
 }
@@ -164,7 +167,7 @@ __global__ void __launch_bounds__(64 * NW)
     igemm(const T* __restrict__ A, const T* __restrict__ Bt, const T* __restrict__ bias, T* __restrict__ out,
           const uint32_t* __restrict__ snmap, const int32_t* __restrict__ perm,
           const uint32_t* __restrict__ smask, int64_t n, int K, int N, int flip, int ntiles, int nblk_n,
-          int nsplit, float* __restrict__ partial) {
+          int nsplit, float* __restrict__ partial, int tgroup) {
   using C = IgemmCfg<T, FM, FN, BK, NW>;
   using E = Elt<T>;
   using frag_t = typename E::frag_t;
@@ -172,9 +175,13 @@ __global__ void __launch_bounds__(64 * NW)
   constexpr int BM = C::kBM, BN = C::kBN, NV = C::kNV;
   static_assert(KMAP == 0 || sizeof(T) == 2, "the natural order needs one 16-byte load per MFMA fragment");
 
-  // the column blocks (and Split-K parts) of one row tile run on one XCD
-  int tile, member;
-  if (!xcd_group_work(ntiles, nblk_n * nsplit, &tile, &member)) return;
+  // tgroup consecutive row tiles with all their column blocks (and Split-K
+  // parts) run on one XCD: they gather overlapping neighbour rows
+  int grp, member;
+  if (!xcd_group_work((ntiles + tgroup - 1) / tgroup, tgroup * nblk_n * nsplit, &grp, &member)) return;
+  const int tile = grp * tgroup + member / (nblk_n * nsplit);
+  if (tile >= ntiles) return;
+  member %= nblk_n * nsplit;
   const int part = member % nsplit;
   const int n0 = (member / nsplit) * BN;
 
@@ -257,14 +264,15 @@ __global__ void __launch_bounds__(64 * NW)
     }
   };
 
-  uint4 abuf[DEPTH][FM][NV];
+  constexpr int AR = FM * NV;  // per-lane MFMA fragments of the wave's rows
+  uint4 abuf[DEPTH][AR];
   uint4 bbuf[DEPTH][C::kBV];
 
   // KMAP 0: lane half h reads the run [h*BK/2, (h+1)*BK/2) of the stage, one
   // contiguous piece per lane.  KMAP 1 (16-bit only): the natural MFMA order,
   // load v of half h reads 16 bytes at element (2v + h) * 8, so each load
   // instruction covers 32 contiguous bytes of every row.
-  auto load_a = [&](uint4 (&dst)[FM][NV]) {
+  auto load_a = [&](uint4 (&dst)[AR]) {
     const int c0 = a_ks * BK + (KMAP == 0 ? half * (BK / 2) : half * C::kVec);
     constexpr int vstride = KMAP == 0 ? 1 : 2;
 #pragma unroll
@@ -273,10 +281,10 @@ __global__ void __launch_bounds__(64 * NW)
       if (j != kSentinel) {
         const uint4* src = reinterpret_cast<const uint4*>(A + int64_t(j) * K + c0);
 #pragma unroll
-        for (int v = 0; v < NV; ++v) dst[i][v] = src[v * vstride];
+        for (int v = 0; v < NV; ++v) dst[i * NV + v] = src[v * vstride];
       } else {
 #pragma unroll
-        for (int v = 0; v < NV; ++v) dst[i][v] = make_uint4(0, 0, 0, 0);
+        for (int v = 0; v < NV; ++v) dst[i * NV + v] = make_uint4(0, 0, 0, 0);
       }
     }
     advance(a_rem, a_k, a_ks);
@@ -309,20 +317,23 @@ __global__ void __launch_bounds__(64 * NW)
       }
     }
   };
-  auto compute = [&](const uint4 (&a)[FM][NV], int buf) {
+  auto compute = [&](const uint4 (&a)[AR], int buf) {
     const T* sb = reinterpret_cast<const T*>(lds_b + buf * C::kLdsB);
 #pragma unroll
     for (int s = 0; s < C::kSteps; ++s) {
       frag_t bfr[FN];
+      const int kofs = KMAP == 0 ? half * (BK / 2) + s * E::kFrag : (2 * s + half) * E::kFrag;
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
         const int c = j * 32 + (lane & 31);
-        const int kofs = KMAP == 0 ? half * (BK / 2) + s * E::kFrag : (2 * s + half) * E::kFrag;
         bfr[j] = *reinterpret_cast<const frag_t*>(sb + c * C::kLd + kofs);
       }
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
-        const frag_t af = a_frag<T, NV>(a[i], s);
+        uint4 ai[NV];
+#pragma unroll
+        for (int v = 0; v < NV; ++v) ai[v] = a[i * NV + v];
+        const frag_t af = a_frag<T, NV>(ai, s);
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc[i][j] = E::mfma(af, bfr[j], acc[i][j]);
       }
@@ -635,26 +646,45 @@ template <typename T, int FM, int FN, int NWM, int NWN, int BKP, int DEPTH>
 __global__ void __launch_bounds__(64 * NWM * NWN)
     wgrad_tr(const T* __restrict__ X, const T* __restrict__ dY, const uint32_t* __restrict__ pair_i,
              const uint32_t* __restrict__ pair_j, const PlanHeader* __restrict__ hdr, float* __restrict__ partial,
-             int Ci, int Co, int64_t chunk_len, int max_chunks, int ntiles_m, int ntiles_n) {
+             int Ci, int Co, int64_t chunk_len, int max_chunks, int ntiles_m, int ntiles_n,
+             const uint32_t* __restrict__ pseg, int pblk, int rows_bpc) {
   using C = WgradTrCfg<T, FM, FN, NWM, NWN, BKP>;
   using E = Elt<T>;
   using frag_t = typename E::frag_t;
   constexpr int NT = C::kThreads, BM = C::kBM, BN = C::kBN, SG = C::kSG, GP = C::kGP;
   static_assert(DEPTH >= 1 && DEPTH < C::kSG, "prefetch depth must stay inside one index group");
 
-  // the channel tiles of one (offset, chunk) run together on one XCD, so the
-  // pair rows they all gather are shared in its L2; groups cycle through the
-  // offsets first so every XCD gets a mix of dense and sparse offsets
-  int g, mn;
-  if (!xcd_group_work(kV * max_chunks, ntiles_m * ntiles_n, &g, &mn)) return;
-  const int k = g % kV;
-  const int chunk = g / kV;
-  const int64_t pk = hdr->pair_count[k];
-  const int64_t start = int64_t(chunk) * chunk_len;
-  if (start >= pk) return;
-  const int64_t end = (start + chunk_len < pk) ? start + chunk_len : pk;
-  const int64_t off = hdr->pair_off[k];
-  const int64_t pbeg = off + start, pend = off + end;
+  int k, chunk, mn;
+  int64_t pbeg, pend;
+  if (rows_bpc > 0) {
+    // Row-range chunks (narrow layers): chunk c holds the pairs of every offset
+    // whose output row lies in blocks [c*bpc, (c+1)*bpc) of kPairRows rows.  The
+    // 27 offsets of one chunk run together on one XCD and share its dY rows and
+    // their neighbours' X rows in L2.  Empty segments still write zeros.
+    const int nmn = ntiles_m * ntiles_n;
+    int m;
+    if (!xcd_group_work(max_chunks, kV * nmn, &chunk, &m)) return;
+    k = m / nmn;
+    mn = m % nmn;
+    const int b0 = chunk * rows_bpc, b1 = (b0 + rows_bpc < pblk) ? b0 + rows_bpc : pblk;
+    pbeg = pseg[int64_t(k) * (pblk + 1) + b0];
+    pend = pseg[int64_t(k) * (pblk + 1) + b1];
+  } else {
+    // Pair-index chunks: the channel tiles of one (offset, chunk) run together
+    // on one XCD, so the pair rows they all gather are shared in its L2; groups
+    // cycle through the offsets first so every XCD gets dense and sparse ones.
+    int g;
+    if (!xcd_group_work(kV * max_chunks, ntiles_m * ntiles_n, &g, &mn)) return;
+    k = g % kV;
+    chunk = g / kV;
+    const int64_t pk = hdr->pair_count[k];
+    const int64_t start = int64_t(chunk) * chunk_len;
+    if (start >= pk) return;
+    const int64_t end = (start + chunk_len < pk) ? start + chunk_len : pk;
+    const int64_t off = hdr->pair_off[k];
+    pbeg = off + start;
+    pend = off + end;
+  }
   const int m0 = (mn / ntiles_n) * BM;
   const int c0 = (mn % ntiles_n) * BN;
 
@@ -678,7 +708,7 @@ __global__ void __launch_bounds__(64 * NWM * NWN)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  const int nstages = int((end - start + BKP - 1) / BKP);
+  const int nstages = int((pend - pbeg + BKP - 1) / BKP);
 
   uint32_t ri[C::kPI], rj[C::kPI];
   auto fetch_idx = [&](int g) {
@@ -809,15 +839,18 @@ __global__ void __launch_bounds__(64 * NWM * NWN)
   }
 }
 
+// dW[k] = sum of offset k's chunk partials in chunk order.  Row-range chunking
+// (rowmode) writes every chunk of every offset; pair-index chunking writes the
+// first ceil(P_k / chunk_len).
 template <typename T>
 __global__ void __launch_bounds__(256) wgrad_reduce(const float* __restrict__ partial,
                                                     const PlanHeader* __restrict__ hdr, T* __restrict__ dW,
-                                                    int64_t cico, int64_t chunk_len, int max_chunks) {
+                                                    int64_t cico, int64_t chunk_len, int max_chunks, int rowmode) {
   const int k = blockIdx.y;
   const int64_t e = int64_t(blockIdx.x) * 256 + threadIdx.x;
   if (e >= cico) return;
   const int64_t pk = hdr->pair_count[k];
-  const int nch = int((pk + chunk_len - 1) / chunk_len);
+  const int nch = rowmode ? max_chunks : int((pk + chunk_len - 1) / chunk_len);
   const float* src = partial + int64_t(k) * max_chunks * cico + e;
   float s = 0.f;
   for (int c = 0; c < nch; ++c) s += src[int64_t(c) * cico];
@@ -912,6 +945,8 @@ struct BwdShape {
   int bm = 0, bn = 0, mt = 0, nt = 0;
   int64_t chunk_len = 0;
   int max_chunks = 0;
+  int rows_bpc = 0;  // > 0: row-range chunks of rows_bpc pair-list blocks
+  int pblk = 0;
   int64_t bias_rows = 0;
   int bias_blocks = 0;
 };
@@ -935,6 +970,14 @@ static BwdShape bwd_shape(int64_t n, int Ci, int Co, int esize) {
   if (len > (int64_t(1) << 20)) len = int64_t(1) << 20;
   s.chunk_len = len;
   s.max_chunks = int(n > 0 ? (n + len - 1) / len : 1);
+  s.pblk = int((n + kPairRows - 1) / kPairRows);
+  if (esize == 2 && s.mt * s.nt == 1 && int64_t(Ci) * Co <= 64 * 64 && s.pblk >= 1024) {
+    // one narrow channel tile and many rows: chunk by row ranges, about 512
+    // chunks (measured best on a 6.4M-voxel, 64-channel layer; small or wide
+    // layers keep pair-index chunks, which run faster there)
+    s.rows_bpc = (s.pblk + 511) / 512;
+    s.max_chunks = (s.pblk + s.rows_bpc - 1) / s.rows_bpc;
+  }
   s.bias_rows = n > 0 ? (n + 511) / 512 : 1;
   if (s.bias_rows < 256) s.bias_rows = 256;
   s.bias_blocks = int(n > 0 ? (n + s.bias_rows - 1) / s.bias_rows : 1);
@@ -978,9 +1021,10 @@ static void igemm_go(const T* A, const T* Bt, const T* bias, T* out, const uint3
   const int ntiles = int((n + BM - 1) / BM);
   const int nblk = (N + BN - 1) / BN;
   const int nsplit = split_parts(n, N);
-  const unsigned grid = xcd_group_grid(ntiles, nblk * nsplit);
+  const int tgroup = nblk * nsplit == 1 ? kTileGroup : 1;
+  const unsigned grid = xcd_group_grid((ntiles + tgroup - 1) / tgroup, tgroup * nblk * nsplit);
   igemm<T, FM, FN, BK, NW, DEPTH, KMAP><<<grid, 64 * NW, 0, s>>>(A, Bt, bias, out, nmap, perm, smask, n, K, N,
-                                                                flip, ntiles, nblk, nsplit, partial);
+                                                                flip, ntiles, nblk, nsplit, partial, tgroup);
   if (nsplit > 1)
     split_reduce<T><<<unsigned((n * N + 255) / 256), 256, 0, s>>>(partial, nsplit, n, N, bias, perm, out);
 }
@@ -1029,13 +1073,15 @@ static void launch_igemm(const T* A, const T* Bt, const T* bias, T* out, const u
 
 template <typename T>
 static void launch_wgrad(const T* X, const T* dY, const uint32_t* pi, const uint32_t* pj, const PlanHeader* h,
-                         float* partial, int Ci, int Co, const BwdShape& b, hipStream_t s) {
+                         const uint32_t* pseg, float* partial, int Ci, int Co, const BwdShape& b, hipStream_t s) {
   dim3 grid(unsigned(b.max_chunks), kV, unsigned(b.mt * b.nt));
   if constexpr (sizeof(T) == 2) {
-    const dim3 grid1(xcd_group_grid(kV * b.max_chunks, b.mt * b.nt));
+    const dim3 grid1(b.rows_bpc > 0 ? xcd_group_grid(b.max_chunks, kV * b.mt * b.nt)
+                                    : xcd_group_grid(kV * b.max_chunks, b.mt * b.nt));
 #define SSC_WTR(FM, FN, NWM, NWN)                                                                        \
   wgrad_tr<T, FM, FN, NWM, NWN, 32, 2><<<grid1, 64 * NWM * NWN, 0, s>>>(X, dY, pi, pj, h, partial, Ci, Co, \
-                                                                       b.chunk_len, b.max_chunks, b.mt, b.nt)
+                                                                       b.chunk_len, b.max_chunks, b.mt, b.nt, \
+                                                                       pseg, b.pblk, b.rows_bpc)
     if (b.bm == 256) SSC_WTR(2, 4, 4, 2);
     else if (b.bm == 128) SSC_WTR(2, 2, 2, 2);
     else if (b.bm == 64) SSC_WTR(1, 1, 2, 2);
@@ -1107,10 +1153,12 @@ static int run_bwd(const char* plan, const uint32_t* nmap, const int32_t* perm, 
   if (dweight) {
     float* part = reinterpret_cast<float*>(ws + W.partial);
     launch_wgrad<T>(static_cast<const T*>(feats), dY, reinterpret_cast<const uint32_t*>(plan + L.pair_i),
-                    reinterpret_cast<const uint32_t*>(plan + L.pair_j), h, part, Ci, Co, b, s);
+                    reinterpret_cast<const uint32_t*>(plan + L.pair_j), h,
+                    reinterpret_cast<const uint32_t*>(plan + L.pseg), part, Ci, Co, b, s);
     const int64_t cico = int64_t(Ci) * Co;
     dim3 rg(unsigned((cico + 255) / 256), kV);
-    wgrad_reduce<T><<<rg, 256, 0, s>>>(part, h, static_cast<T*>(dweight), cico, b.chunk_len, b.max_chunks);
+    wgrad_reduce<T><<<rg, 256, 0, s>>>(part, h, static_cast<T*>(dweight), cico, b.chunk_len, b.max_chunks,
+                                       b.rows_bpc > 0 ? 1 : 0);
   }
   if (dbias) {
     float* part = reinterpret_cast<float*>(ws + W.bias);

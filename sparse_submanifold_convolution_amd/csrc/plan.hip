@@ -446,7 +446,7 @@ __global__ void __launch_bounds__(256) pair_scatter(const uint32_t* __restrict__
                                                     const uint32_t* __restrict__ pcnt, int64_t pblk,
                                                     uint32_t* __restrict__ pair_i,
                                                     uint32_t* __restrict__ pair_j, int direct,
-                                                    PlanHeader* __restrict__ h) {
+                                                    PlanHeader* __restrict__ h, uint32_t* __restrict__ pseg) {
   __shared__ uint32_t base[32];
   __shared__ uint32_t tot[32];
   __shared__ uint32_t wc[kV][4];
@@ -491,6 +491,8 @@ __global__ void __launch_bounds__(256) pair_scatter(const uint32_t* __restrict__
     base[tid] = pcnt[int64_t(tid) * pblk + blockIdx.x];
   }
   __syncthreads();
+  // where this block's rows start in each list (the weight gradient chunks by rows)
+  if (tid < kV) pseg[int64_t(tid) * (pblk + 1) + blockIdx.x] = base[tid];
   __shared__ uint32_t rows[256 * kV];
   for (int q = 0; q < kPairRows / 256; ++q) {
     const int64_t rbase = int64_t(blockIdx.x) * kPairRows + q * 256;
@@ -523,6 +525,7 @@ __global__ void __launch_bounds__(256) pair_scatter(const uint32_t* __restrict__
     if (tid < kV) base[tid] += wc[tid][0] + wc[tid][1] + wc[tid][2] + wc[tid][3];
     __syncthreads();
   }
+  if (blockIdx.x == pblk - 1 && tid < kV) pseg[int64_t(tid) * (pblk + 1) + pblk] = base[tid];
 }
 
 // ---------------------------------------------------------------------------
@@ -620,15 +623,15 @@ extern "C" int ssc_build_neighbor_map(const int32_t* coords, int64_t n, int32_t 
     plan_prepare<uint64_t><<<prep, 256, 0, s>>>(h, n, B, X, Y, Z, kb, zbits, L.capacity, nmap, hkeys);
     hash_insert<uint64_t><<<grid1d(n, 256), 256, 0, s>>>(c4, n, B, X, Y, Z, hkeys, hvals, L.capacity,
                                                          &h->status_bits);
-    probe_half<uint64_t><<<grid1d(n * kCentre, 256), 256, 0, s>>>(c4, n, B, X, Y, Z, hkeys, hvals, L.capacity,
-                                                                  nmap);
+    probe_half<uint64_t><<<grid1d(n * kCentre, 256), 256, 0, s>>>(c4, n, B, X, Y, Z, hkeys, hvals,
+                                                                  L.capacity, nmap);
   } else {
     uint32_t* hkeys = reinterpret_cast<uint32_t*>(base + L.hkeys);
     plan_prepare<uint32_t><<<prep, 256, 0, s>>>(h, n, B, X, Y, Z, kb, zbits, L.capacity, nmap, hkeys);
     hash_insert<uint32_t><<<grid1d(n, 256), 256, 0, s>>>(c4, n, B, X, Y, Z, hkeys, hvals, L.capacity,
                                                          &h->status_bits);
-    probe_half<uint32_t><<<grid1d(n * kCentre, 256), 256, 0, s>>>(c4, n, B, X, Y, Z, hkeys, hvals, L.capacity,
-                                                                  nmap);
+    probe_half<uint32_t><<<grid1d(n * kCentre, 256), 256, 0, s>>>(c4, n, B, X, Y, Z, hkeys, hvals,
+                                                                  L.capacity, nmap);
   }
   row_scan<<<unsigned(pblk), 256, 0, s>>>(c4, nmap, n, B, X, Y, Z, axis_bits, zbits, key0, pcnt, pblk);
 
@@ -664,7 +667,8 @@ extern "C" int ssc_build_neighbor_map(const int32_t* coords, int64_t n, int32_t 
     launch_scan(pcnt, pblk * kV + 1, scan_tmp, s);
     pair_offsets<<<1, 64, 0, s>>>(pcnt, pblk, h);
   }
-  pair_scatter<<<unsigned(pblk), 256, 0, s>>>(nmap, n, pcnt, pblk, pair_i, pair_j, pdirect, h);
+  pair_scatter<<<unsigned(pblk), 256, 0, s>>>(nmap, n, pcnt, pblk, pair_i, pair_j, pdirect, h,
+                                              reinterpret_cast<uint32_t*>(base + L.pseg));
 
   return hipGetLastError() == hipSuccess ? SSC_OK : SSC_ERR_HIP;
 }

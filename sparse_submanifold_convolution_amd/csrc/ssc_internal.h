@@ -64,6 +64,7 @@ struct PlanLayout {
   size_t snmap = 0;   // [n][27] u32: nmap rows in sorted order, snmap[r] = nmap[perm[r]]
   size_t pair_i = 0;  // [27n] u32: pair lists, output row i
   size_t pair_j = 0;  // [27n] u32: pair lists, input row j = nmap[i][k]
+  size_t pseg = 0;    // [27][pblk + 1] u32: where each kPairRows block of rows starts in each list
   // build-only scratch
   size_t hkeys = 0, hvals = 0, key0 = 0, key1 = 0, val0 = 0, val1 = 0, hist = 0, pcnt = 0,
          scan_tmp = 0;
@@ -87,6 +88,7 @@ inline PlanLayout conv_layout(int64_t n) {
   L.snmap = take(size_t(n) * kV * 4);
   L.pair_i = take(size_t(n) * kV * 4);
   L.pair_j = take(size_t(n) * kV * 4);
+  L.pseg = take(size_t(kV) * size_t((n + kPairRows - 1) / kPairRows + 1) * 4);
   L.total = off;
   return L;
 }
