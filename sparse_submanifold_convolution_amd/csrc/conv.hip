@@ -38,6 +38,7 @@ namespace ssc {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 struct bf16s {
   uint16_t bits;
@@ -118,14 +119,17 @@ __device__ __forceinline__ int acc_row(int lane, int i) { return (i >> 2) * 8 + 
 // masked implicit GEMM (forward and input gradient)
 // ---------------------------------------------------------------------------
 //
-// A workgroup of NW waves owns a tile of BM = NW * FM * 32 consecutive rows in
-// sorted order and BN = FN * 32 output channels.  Wave w owns rows
-// [w*FM*32, (w+1)*FM*32) of the tile and every channel of it, so the rows it
-// gathers are its own: each lane loads its row's K-slice straight from global
-// memory into registers in MFMA operand order, DEPTH stages ahead, and no A
-// data passes through LDS.  The weight slice of the stage (dense, shared by
-// all waves) is fetched DEPTH stages ahead too and staged through a
-// double-buffered LDS tile.
+// A workgroup of NWM x NWN waves owns a tile of BM = NWM * FM * 32 consecutive
+// rows in sorted order and BN = NWN * FN * 32 output channels.  Wave (wm, wn)
+// owns rows [wm*FM*32, (wm+1)*FM*32) and channels [wn*FN*32, (wn+1)*FN*32) of
+// the tile; each lane loads its rows' K-slices straight from global memory
+// into registers in MFMA operand order, DEPTH stages ahead, and no A data
+// passes through LDS (waves of one wm gather the same rows, mostly from L1).
+// The weight slice of the stage (dense, shared by all waves) is fetched DEPTH
+// stages ahead too and staged through a double-buffered LDS tile.  Every
+// weight fragment read from LDS feeds FM MFMAs and every gathered fragment FN,
+// so NWN > 1 trades gather traffic for LDS read bandwidth, which alone would
+// match the MFMA rate when FM = 1 and 8 waves share a CU.
 //
 // Inside a stage of BK reduction elements, lane half h (lanes 32h..32h+31)
 // covers the contiguous run [h*BK/2, (h+1)*BK/2): MFMA step s takes its
@@ -134,11 +138,11 @@ __device__ __forceinline__ int acc_row(int lane, int i) { return (i >> 2) * 8 + 
 // gives the same sum, and this one makes every lane's gather one contiguous
 // run of its row.
 
-template <typename T, int FM, int FN, int BK, int NW>
+template <typename T, int FM, int FN, int BK, int NWM, int NWN>
 struct IgemmCfg {
-  static constexpr int kThreads = 64 * NW;
-  static constexpr int kBM = NW * FM * 32;
-  static constexpr int kBN = FN * 32;
+  static constexpr int kThreads = 64 * NWM * NWN;
+  static constexpr int kBM = NWM * FM * 32;
+  static constexpr int kBN = NWN * FN * 32;
   static constexpr int kVec = 16 / int(sizeof(T));                 // elements per 16-byte load
   static constexpr int kLd = BK + kVec;                            // LDS row stride of B (elements)
   static constexpr int kNV = (BK / 2) * int(sizeof(T)) / 16;       // 16-byte loads per lane per row block
@@ -150,10 +154,9 @@ struct IgemmCfg {
 };
 
 template <typename T, int NV>
-__device__ __forceinline__ typename Elt<T>::frag_t a_frag(const uint4 (&v)[NV], int s) {
+__device__ __forceinline__ typename Elt<T>::frag_t a_frag(const u32x4 (&v)[NV], int s) {
   if constexpr (sizeof(T) == 4) {
-    const float* f = reinterpret_cast<const float*>(&v[0]);
-    return f[s];
+    return __uint_as_float(v[s / 4][s % 4]);
   } else {
     return __builtin_bit_cast(typename Elt<T>::frag_t, v[s]);
   }
@@ -162,18 +165,21 @@ __device__ __forceinline__ typename Elt<T>::frag_t a_frag(const uint4 (&v)[NV], 
 // Split-K (nsplit > 1): work item (tile, column block, part) takes the part-th
 // contiguous share of the tile's offset set and writes fp32 partial sums, in
 // sorted row order, to partial[part][row][N]; split_reduce finishes them.
-template <typename T, int FM, int FN, int BK, int NW, int DEPTH, int KMAP>
-__global__ void __launch_bounds__(64 * NW)
+template <typename T, int FM, int FN, int BK, int NWM, int NWN, int DEPTH, int KMAP>
+__global__ void __launch_bounds__(64 * NWM * NWN)
     igemm(const T* __restrict__ A, const T* __restrict__ Bt, const T* __restrict__ bias, T* __restrict__ out,
           const uint32_t* __restrict__ snmap, const int32_t* __restrict__ perm,
-          const uint32_t* __restrict__ smask, int64_t n, int K, int N, int flip, int ntiles, int nblk_n,
-          int nsplit, float* __restrict__ partial, int tgroup) {
-  using C = IgemmCfg<T, FM, FN, BK, NW>;
+          const uint32_t* __restrict__ smask, const T* __restrict__ zrow, int64_t n, int K, int N, int flip,
+          int ntiles, int nblk_n, int nsplit, float* __restrict__ partial, int tgroup) {
+  using C = IgemmCfg<T, FM, FN, BK, NWM, NWN>;
   using E = Elt<T>;
   using frag_t = typename E::frag_t;
   constexpr int NT = C::kThreads;
   constexpr int BM = C::kBM, BN = C::kBN, NV = C::kNV;
   static_assert(KMAP == 0 || sizeof(T) == 2, "the natural order needs one 16-byte load per MFMA fragment");
+  static_assert(KMAP != 2 || NWN == 1, "row-coalesced gathers keep each wave's rows private");
+  // KMAP 2: lanes per gathered row segment and rows per load instruction
+  constexpr int LPR = BK / C::kVec, RPI = 64 / LPR;
 
   // tgroup consecutive row tiles with all their column blocks (and Split-K
   // parts) run on one XCD: they gather overlapping neighbour rows
@@ -186,14 +192,20 @@ __global__ void __launch_bounds__(64 * NW)
   const int n0 = (member / nsplit) * BN;
 
   __shared__ __align__(16) char lds_b[2 * C::kLdsB];
+  // KMAP 2: each wave's gathered rows of the current stage, 16-byte slots
+  // XOR-swizzled so that both the row-major writes and the MFMA-order reads
+  // of 8 lanes hit 8 distinct bank groups
+  __shared__ __align__(16) T lds_a[KMAP == 2 ? NWM * FM * 32 * BK : 8];
   __shared__ uint32_t jtab[BM * kV];  // [row][k]: this tile's rows of the sorted-order map
   __shared__ int32_t prow[BM];
   __shared__ uint32_t tile_union;
+  __shared__ uint32_t wave_union[NWM];  // offsets present among each wave row's rows
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int half = lane >> 5;
+  const int wm = wave / NWN, wn = wave % NWN;
   const int64_t row0 = int64_t(tile) * BM;
 
   // ---- prologue: rows, the tile's offset set, gather indices ----
@@ -209,6 +221,7 @@ __global__ void __launch_bounds__(64 * NW)
     jv[q] = (q * NT + tid < BM * kV && e < jend) ? snmap[e] : kSentinel;
   }
   if (tid == 0) tile_union = 0;
+  if (tid < NWM) wave_union[tid] = 0;
   int32_t pr = -1;
   uint32_t msk = 0;
   if (tid < BM) {
@@ -224,7 +237,10 @@ __global__ void __launch_bounds__(64 * NW)
   __syncthreads();
   if (tid < BM) {
     prow[tid] = pr;
-    if (msk) atomicOr(&tile_union, msk);
+    if (msk) {
+      atomicOr(&tile_union, msk);
+      atomicOr(&wave_union[tid / (FM * 32)], msk);
+    }
   }
   __syncthreads();
   uint32_t uni = tile_union;
@@ -251,11 +267,15 @@ __global__ void __launch_bounds__(64 * NW)
 
   const int kslices = K / BK;
   const int nstages = __popc(uni) * kslices;
+  // A wave skips the MFMAs of a stage whose offset none of its rows has (its
+  // loads still run and read the zero row), so only the tile's weight slices
+  // are shared and the work follows each wave's own rows.
+  const uint32_t wuni = wave_union[wm] & uni;
 
-  // stage cursors: A and B both run DEPTH stages ahead
-  uint32_t a_rem = uni, b_rem = uni;
+  // stage cursors: A and B both run DEPTH stages ahead of the compute cursor c
+  uint32_t a_rem = uni, b_rem = uni, c_rem = uni;
   int a_k = a_rem ? __ffs(a_rem) - 1 : 0, a_ks = 0;
-  int b_k = a_k, b_ks = 0;
+  int b_k = a_k, b_ks = 0, c_k = a_k, c_ks = 0;
   auto advance = [&](uint32_t& rem, int& k, int& ks) {
     if (++ks == kslices) {
       ks = 0;
@@ -265,47 +285,73 @@ __global__ void __launch_bounds__(64 * NW)
   };
 
   constexpr int AR = FM * NV;  // per-lane MFMA fragments of the wave's rows
-  uint4 abuf[DEPTH][AR];
-  uint4 bbuf[DEPTH][C::kBV];
+  // native vectors, so every ring copy is a plain register load or store
+  u32x4 abuf[DEPTH][AR];
+  u32x4 bbuf[DEPTH][C::kBV];
 
+  // Every load is unconditional (a branch around a load, even a uniform one,
+  // makes the compiler drain the whole prefetch ring at the next wait): a
+  // missing neighbour, an out-of-range weight column and any stage past the
+  // last one (the ring runs DEPTH stages ahead) read the plan's zero row.
+  //
   // KMAP 0: lane half h reads the run [h*BK/2, (h+1)*BK/2) of the stage, one
   // contiguous piece per lane.  KMAP 1 (16-bit only): the natural MFMA order,
   // load v of half h reads 16 bytes at element (2v + h) * 8, so each load
-  // instruction covers 32 contiguous bytes of every row.
-  auto load_a = [&](uint4 (&dst)[AR]) {
-    const int c0 = a_ks * BK + (KMAP == 0 ? half * (BK / 2) : half * C::kVec);
-    constexpr int vstride = KMAP == 0 ? 1 : 2;
+  // instruction covers 32 contiguous bytes of 32 rows.  KMAP 2 (16-bit only):
+  // LPR lanes read one row's whole stage segment, so each load instruction
+  // covers RPI rows completely (fewer, fuller cache lines per instruction);
+  // compute() moves the rows into MFMA order through the wave's LDS slots.
+  auto load_a = [&](u32x4 (&dst)[AR]) {
+    // a byte offset from A selects the zero row: selects, never branches
+    const int64_t zoff = reinterpret_cast<const char*>(zrow) - reinterpret_cast<const char*>(A);
+    const uint32_t live = a_rem != 0 ? ~0u : 0u;
+    if constexpr (KMAP == 2) {
+      const int c0 = a_ks * BK + (lane % LPR) * C::kVec;
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      const uint32_t j = jtab[(wave * FM * 32 + i * 32 + (lane & 31)) * kV + a_k];
-      if (j != kSentinel) {
-        const uint4* src = reinterpret_cast<const uint4*>(A + int64_t(j) * K + c0);
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+          const int rr = i * 32 + v * RPI + lane / LPR;
+          const uint32_t j = jtab[(wm * FM * 32 + rr) * kV + a_k] | ~live;
+          const int64_t off = j != kSentinel ? (int64_t(j) * K + c0) * int64_t(sizeof(T)) : zoff;
+          dst[i * NV + v] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(A) + off);
+        }
+    } else {
+      const int c0 = a_ks * BK + (KMAP == 0 ? half * (BK / 2) : half * C::kVec);
+      constexpr int vstride = KMAP == 0 ? 1 : 2;
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const uint32_t j = jtab[(wm * FM * 32 + i * 32 + (lane & 31)) * kV + a_k] | ~live;
+        const int64_t off = j != kSentinel ? (int64_t(j) * K + c0) * int64_t(sizeof(T)) : zoff;
+        const u32x4* src = reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(A) + off);
 #pragma unroll
         for (int v = 0; v < NV; ++v) dst[i * NV + v] = src[v * vstride];
-      } else {
-#pragma unroll
-        for (int v = 0; v < NV; ++v) dst[i * NV + v] = make_uint4(0, 0, 0, 0);
       }
     }
     advance(a_rem, a_k, a_ks);
   };
-  auto load_b = [&](uint4 (&rb)[C::kBV]) {
+  // KMAP 2 slot of (wave row rr, 16-byte chunk c) in the wave's LDS rows
+  auto a_slot = [&](int rr, int c) {
+    const int q = rr * LPR + c;
+    return q ^ ((q >> 3) & 7);
+  };
+  auto load_b = [&](u32x4 (&rb)[C::kBV]) {
     const int kb = flip ? (kV - 1 - b_k) : b_k;
-    const T* base = Bt + int64_t(kb) * N * K + b_ks * BK;
+    const int64_t base = (int64_t(kb) * N * K + b_ks * BK) * int64_t(sizeof(T));
+    const int64_t zoff = reinterpret_cast<const char*>(zrow) - reinterpret_cast<const char*>(Bt);
+    const int rlim = b_rem != 0 ? N - n0 : 0;  // rows at or past rlim read the zero row
     constexpr int VPR = BK / C::kVec;
 #pragma unroll
     for (int v = 0; v < C::kBV; ++v) {
       const int idx = tid + v * NT;
-      uint4 val = make_uint4(0, 0, 0, 0);
-      if (idx < BN * VPR) {
-        const int r = idx / VPR, cv = idx % VPR;
-        if (n0 + r < N) val = *reinterpret_cast<const uint4*>(base + int64_t(n0 + r) * K + cv * C::kVec);
-      }
-      rb[v] = val;
+      const int id = idx < BN * VPR ? idx : 0;  // surplus threads reload element 0 and store nothing
+      const int r = id / VPR, cv = id % VPR;
+      const int64_t off = (r < rlim ? base + int64_t(n0 + r) * K * int64_t(sizeof(T)) : zoff) + cv * 16;
+      rb[v] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(Bt) + off);
     }
     advance(b_rem, b_k, b_ks);
   };
-  auto store_b = [&](int buf, const uint4 (&rb)[C::kBV]) {
+  auto store_b = [&](int buf, const u32x4 (&rb)[C::kBV]) {
     T* sb = reinterpret_cast<T*>(lds_b + buf * C::kLdsB);
     constexpr int VPR = BK / C::kVec;
 #pragma unroll
@@ -313,53 +359,75 @@ __global__ void __launch_bounds__(64 * NW)
       const int idx = tid + v * NT;
       if (idx < BN * VPR) {
         const int r = idx / VPR, cv = idx % VPR;
-        *reinterpret_cast<uint4*>(sb + r * C::kLd + cv * C::kVec) = rb[v];
+        *reinterpret_cast<u32x4*>(sb + r * C::kLd + cv * C::kVec) = rb[v];
       }
     }
   };
-  auto compute = [&](const uint4 (&a)[AR], int buf) {
+  auto compute = [&](const u32x4 (&a)[AR], int buf) {
     const T* sb = reinterpret_cast<const T*>(lds_b + buf * C::kLdsB);
+    T* sa = lds_a + (KMAP == 2 ? wave * FM * 32 * BK : 0);
+    if constexpr (KMAP == 2) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int v = 0; v < NV; ++v)
+          *reinterpret_cast<u32x4*>(sa + a_slot(i * 32 + v * RPI + lane / LPR, lane % LPR) * C::kVec) =
+              a[i * NV + v];
+      // the wave's own rows: in-order LDS needs no barrier, only no reordering
+      __builtin_amdgcn_wave_barrier();
+    }
 #pragma unroll
     for (int s = 0; s < C::kSteps; ++s) {
       frag_t bfr[FN];
       const int kofs = KMAP == 0 ? half * (BK / 2) + s * E::kFrag : (2 * s + half) * E::kFrag;
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
-        const int c = j * 32 + (lane & 31);
+        const int c = (wn * FN + j) * 32 + (lane & 31);
         bfr[j] = *reinterpret_cast<const frag_t*>(sb + c * C::kLd + kofs);
       }
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
-        uint4 ai[NV];
+        frag_t af;
+        if constexpr (KMAP == 2) {
+          af = *reinterpret_cast<const frag_t*>(sa + a_slot(i * 32 + (lane & 31), 2 * s + half) * C::kVec);
+        } else {
+          u32x4 ai[NV];
 #pragma unroll
-        for (int v = 0; v < NV; ++v) ai[v] = a[i * NV + v];
-        const frag_t af = a_frag<T, NV>(ai, s);
+          for (int v = 0; v < NV; ++v) ai[v] = a[i * NV + v];
+          af = a_frag<T, NV>(ai, s);
+        }
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc[i][j] = E::mfma(af, bfr[j], acc[i][j]);
       }
     }
+    // the next stage's slot writes stay behind this stage's reads
+    if constexpr (KMAP == 2) __builtin_amdgcn_wave_barrier();
   };
 
   // prologue loads: both operands DEPTH stages deep
 #pragma unroll
-  for (int d = 0; d < DEPTH; ++d)
-    if (d < nstages) {
-      load_a(abuf[d]);
-      load_b(bbuf[d]);
-    }
+  for (int d = 0; d < DEPTH; ++d) {
+    load_a(abuf[d]);
+    load_b(bbuf[d]);
+  }
 
+  // Each stage refills its ring slot DEPTH stages ahead.  Only the LDS store,
+  // the barrier and the MFMAs depend on the (uniform) stage bound; the loads
+  // are issued on every path.
   for (int s0 = 0; s0 < nstages; s0 += DEPTH) {
 #pragma unroll
     for (int d = 0; d < DEPTH; ++d) {
       const int s = s0 + d;
-      if (s < nstages) {
-        const int buf = s & 1;
+      const int buf = s & 1;
+      const bool run = s < nstages;
+      if (run) {
         store_b(buf, bbuf[d]);
         __syncthreads();
-        if (s + DEPTH < nstages) load_b(bbuf[d]);
-        compute(abuf[d], buf);
-        if (s + DEPTH < nstages) load_a(abuf[d]);
       }
+      load_b(bbuf[d]);
+      if (run && ((wuni >> c_k) & 1u)) compute(abuf[d], buf);
+      advance(c_rem, c_k, c_ks);
+      load_a(abuf[d]);
     }
   }
 
@@ -368,13 +436,13 @@ __global__ void __launch_bounds__(64 * NW)
     float* dst = partial + int64_t(part) * n * N;
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
-      const int c = n0 + j * 32 + (lane & 31);
+      const int c = n0 + (wn * FN + j) * 32 + (lane & 31);
       if (c >= N) continue;
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const int64_t g = row0 + wave * FM * 32 + i * 32 + acc_row(lane, e);
+          const int64_t g = row0 + wm * FM * 32 + i * 32 + acc_row(lane, e);
           if (g < n) dst[g * N + c] = acc[i][j][e];
         }
     }
@@ -384,14 +452,14 @@ __global__ void __launch_bounds__(64 * NW)
   // ---- epilogue: bias, round once, scatter rows to perm ----
 #pragma unroll
   for (int j = 0; j < FN; ++j) {
-    const int c = n0 + j * 32 + (lane & 31);
+    const int c = n0 + (wn * FN + j) * 32 + (lane & 31);
     if (c >= N) continue;
     const float bv = bias ? E::load(bias[c]) : 0.f;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int r = wave * FM * 32 + i * 32 + acc_row(lane, e);
+        const int r = wm * FM * 32 + i * 32 + acc_row(lane, e);
         const int32_t p = prow[r];
         if (p >= 0) out[int64_t(p) * N + c] = E::store(acc[i][j][e] + bv);
       }
@@ -1014,34 +1082,37 @@ static bool channels_ok(int Ci, int Co) {
   return Ci > 0 && Co > 0 && Ci % 16 == 0 && Co % 16 == 0 && Ci <= 4096 && Co <= 4096;
 }
 
-template <typename T, int FM, int FN, int BK, int NW, int DEPTH, int KMAP>
+template <typename T, int FM, int FN, int BK, int NWM, int NWN, int DEPTH, int KMAP>
 static void igemm_go(const T* A, const T* Bt, const T* bias, T* out, const uint32_t* nmap, const int32_t* perm,
-                     const uint32_t* smask, int64_t n, int K, int N, int flip, float* partial, hipStream_t s) {
-  constexpr int BM = NW * FM * 32, BN = FN * 32;
+                     const uint32_t* smask, const T* zrow, int64_t n, int K, int N, int flip, float* partial,
+                     hipStream_t s) {
+  constexpr int BM = NWM * FM * 32, BN = NWN * FN * 32;
   const int ntiles = int((n + BM - 1) / BM);
   const int nblk = (N + BN - 1) / BN;
   const int nsplit = split_parts(n, N);
   const int tgroup = nblk * nsplit == 1 ? kTileGroup : 1;
   const unsigned grid = xcd_group_grid((ntiles + tgroup - 1) / tgroup, tgroup * nblk * nsplit);
-  igemm<T, FM, FN, BK, NW, DEPTH, KMAP><<<grid, 64 * NW, 0, s>>>(A, Bt, bias, out, nmap, perm, smask, n, K, N,
-                                                                flip, ntiles, nblk, nsplit, partial, tgroup);
+  igemm<T, FM, FN, BK, NWM, NWN, DEPTH, KMAP><<<grid, 64 * NWM * NWN, 0, s>>>(
+      A, Bt, bias, out, nmap, perm, smask, zrow, n, K, N, flip, ntiles, nblk, nsplit, partial, tgroup);
   if (nsplit > 1)
     split_reduce<T><<<unsigned((n * N + 255) / 256), 256, 0, s>>>(partial, nsplit, n, N, bias, perm, out);
 }
 
-// Tile choice (measured on MI355X, see the tuning notes): every wave owns 32
-// rows; the workgroup spans as many output channels as the layer has, up to
-// 256, so the gathered rows are fetched once per channel block; 8 waves share
-// one weight tile when there are enough rows to fill the chip, fewer waves
-// (more, smaller workgroups) otherwise.
+// Tile choice (measured on MI355X): every wave owns 32 rows; the workgroup
+// spans as many output channels as the layer has, up to 256, so the gathered
+// rows are fetched once per channel block; 8 waves share one weight tile when
+// there are enough rows to fill the chip, fewer waves (more, smaller
+// workgroups) otherwise.  With 8 waves and a reduction of at most 128 (at most
+// two stages per offset, so the gathers dominate) the rows are gathered whole
+// (KMAP 2); wider reductions keep the register-only natural order.
 template <typename T, int FN>
 static void igemm_pick_rows(const T* A, const T* Bt, const T* bias, T* out, const uint32_t* nmap,
-                            const int32_t* perm, const uint32_t* smask, int64_t n, int K, int N, int flip,
-                            float* partial, hipStream_t s) {
+                            const int32_t* perm, const uint32_t* smask, const T* zrow, int64_t n, int K, int N,
+                            int flip, float* partial, hipStream_t s) {
   const int64_t nblk = (N + FN * 32 - 1) / (FN * 32);
   const int64_t wg256 = (n + 255) / 256 * nblk, wg128 = (n + 127) / 128 * nblk;
 #define SSC_GO(NW, BK, DEPTH, KMAP) \
-  igemm_go<T, 1, FN, BK, NW, DEPTH, KMAP>(A, Bt, bias, out, nmap, perm, smask, n, K, N, flip, partial, s)
+  igemm_go<T, 1, FN, BK, NW, 1, DEPTH, KMAP>(A, Bt, bias, out, nmap, perm, smask, zrow, n, K, N, flip, partial, s)
 #define SSC_BK(NW, DEPTH)                                                 \
   do {                                                                    \
     if constexpr (sizeof(T) == 4) {                                       \
@@ -1054,21 +1125,31 @@ static void igemm_pick_rows(const T* A, const T* Bt, const T* bias, T* out, cons
   } while (0)
   // prefetch depth: as deep as the registers allow without spilling
   constexpr int D8 = FN >= 8 ? 2 : 3, D4 = FN >= 8 ? 3 : 4;
-  if (FN >= 4 && wg256 >= 512) SSC_BK(8, D8);
-  else if (wg128 >= 256) SSC_BK(4, D4);
-  else SSC_BK(2, D4);
+  if (FN >= 2 && wg256 >= 512) {
+    if constexpr (sizeof(T) == 2) {
+      if (K % 64 == 0 && K <= 128) {
+        SSC_GO(8, 64, 2, 2);
+        return;
+      }
+    }
+    SSC_BK(8, D8);
+  } else if (wg128 >= 128) {
+    SSC_BK(4, D4);
+  } else {
+    SSC_BK(2, D4);
+  }
 #undef SSC_BK
 #undef SSC_GO
 }
 
 template <typename T>
 static void launch_igemm(const T* A, const T* Bt, const T* bias, T* out, const uint32_t* nmap,
-                         const int32_t* perm, const uint32_t* smask, int64_t n, int K, int N, int flip,
-                         float* partial, hipStream_t s) {
-  if (N > 128) igemm_pick_rows<T, 8>(A, Bt, bias, out, nmap, perm, smask, n, K, N, flip, partial, s);
-  else if (N > 64) igemm_pick_rows<T, 4>(A, Bt, bias, out, nmap, perm, smask, n, K, N, flip, partial, s);
-  else if (N > 32) igemm_pick_rows<T, 2>(A, Bt, bias, out, nmap, perm, smask, n, K, N, flip, partial, s);
-  else igemm_pick_rows<T, 1>(A, Bt, bias, out, nmap, perm, smask, n, K, N, flip, partial, s);
+                         const int32_t* perm, const uint32_t* smask, const T* zrow, int64_t n, int K, int N,
+                         int flip, float* partial, hipStream_t s) {
+  if (N > 128) igemm_pick_rows<T, 8>(A, Bt, bias, out, nmap, perm, smask, zrow, n, K, N, flip, partial, s);
+  else if (N > 64) igemm_pick_rows<T, 4>(A, Bt, bias, out, nmap, perm, smask, zrow, n, K, N, flip, partial, s);
+  else if (N > 32) igemm_pick_rows<T, 2>(A, Bt, bias, out, nmap, perm, smask, zrow, n, K, N, flip, partial, s);
+  else igemm_pick_rows<T, 1>(A, Bt, bias, out, nmap, perm, smask, zrow, n, K, N, flip, partial, s);
 }
 
 template <typename T>
@@ -1129,8 +1210,8 @@ static int run_fwd(const char* plan, const uint32_t* nmap, const int32_t* perm, 
   transpose_w<T><<<tg, 256, 0, s>>>(static_cast<const T*>(weight), wt, Ci, Co);
   launch_igemm<T>(static_cast<const T*>(feats), wt, static_cast<const T*>(bias), static_cast<T*>(out),
                   reinterpret_cast<const uint32_t*>(plan + L.snmap), perm,
-                  reinterpret_cast<const uint32_t*>(plan + L.smask), n, Ci, Co, 0,
-                  reinterpret_cast<float*>(ws + W.split), s);
+                  reinterpret_cast<const uint32_t*>(plan + L.smask), reinterpret_cast<const T*>(plan + L.zrow), n,
+                  Ci, Co, 0, reinterpret_cast<float*>(ws + W.split), s);
   return SSC_OK;
 }
 
@@ -1147,8 +1228,8 @@ static int run_bwd(const char* plan, const uint32_t* nmap, const int32_t* perm, 
     // dX = masked implicit GEMM of dY with B[k] = W[26-k] read as [Ci][Co] (K = Co, N = Ci)
     launch_igemm<T>(dY, static_cast<const T*>(weight), nullptr, static_cast<T*>(dfeats),
                     reinterpret_cast<const uint32_t*>(plan + L.snmap), perm,
-                    reinterpret_cast<const uint32_t*>(plan + L.smask), n, Co, Ci, 1,
-                    reinterpret_cast<float*>(ws + W.split), s);
+                    reinterpret_cast<const uint32_t*>(plan + L.smask), reinterpret_cast<const T*>(plan + L.zrow),
+                    n, Co, Ci, 1, reinterpret_cast<float*>(ws + W.split), s);
   }
   if (dweight) {
     float* part = reinterpret_cast<float*>(ws + W.partial);

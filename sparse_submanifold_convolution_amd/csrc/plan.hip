@@ -8,8 +8,8 @@
 // (sorted_idx) so that tiles of rows share their valid offsets.
 //
 // Kernels, in launch order:
-//   plan_prepare    header fields, status word, pair counters; sentinel fill
-//                   of nmap; empty (all ones) fill of the hash keys
+//   plan_prepare    header fields, status word, pair counters; the zero row;
+//                   sentinel fill of nmap; empty (all ones) fill of the hash keys
 //   hash_insert     coordinate check, key packing, open-addressing insert with
 //                   atomicCAS on 32- or 64-bit keys; value = row index
 //   probe_half      one lookup per (voxel, offset k < 13), bounds checked per
@@ -182,7 +182,8 @@ static void launch_scan(uint32_t* data, int64_t len, uint32_t* tmp, hipStream_t 
 template <typename KeyT>
 __global__ void __launch_bounds__(256) plan_prepare(PlanHeader* h, int64_t n, int B, int X, int Y, int Z,
                                                    int key_bits, int zbits, uint64_t capacity,
-                                                   uint32_t* __restrict__ nmap, KeyT* __restrict__ keys) {
+                                                   uint32_t* __restrict__ nmap, KeyT* __restrict__ keys,
+                                                   uint4* __restrict__ zrow) {
   if (blockIdx.x == 0) {
     if (threadIdx.x == 0) {
       h->magic = kPlanMagic;
@@ -203,6 +204,7 @@ __global__ void __launch_bounds__(256) plan_prepare(PlanHeader* h, int64_t n, in
   }
   const int64_t stride = int64_t(gridDim.x) * blockDim.x;
   const int64_t t0 = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  for (int64_t i = t0; i < int64_t(kZeroRowBytes / 16); i += stride) zrow[i] = make_uint4(0, 0, 0, 0);
   for (int64_t i = t0; i < n * kV; i += stride) nmap[i] = kSentinel;
   for (int64_t i = t0; i < int64_t(capacity); i += stride) keys[i] = empty_key<KeyT>();
 }
@@ -594,11 +596,12 @@ extern "C" int ssc_build_neighbor_map(const int32_t* coords, int64_t n, int32_t 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* base = static_cast<char*>(plan);
   PlanHeader* h = reinterpret_cast<PlanHeader*>(base + L.header);
+  uint4* zrow = reinterpret_cast<uint4*>(base + L.zrow);
   (void)hipGetLastError();
   if (n == 0) {
     // header only (the key fill touches the plan's own table region)
     plan_prepare<uint32_t><<<1, 256, 0, s>>>(h, 0, B, X, Y, Z, kb, zbits, L.capacity, nullptr,
-                                             reinterpret_cast<uint32_t*>(base + L.hkeys));
+                                             reinterpret_cast<uint32_t*>(base + L.hkeys), zrow);
     return hipGetLastError() == hipSuccess ? SSC_OK : SSC_ERR_HIP;
   }
 
@@ -620,14 +623,14 @@ extern "C" int ssc_build_neighbor_map(const int32_t* coords, int64_t n, int32_t 
   const unsigned prep = prep_blocks < 2048 ? prep_blocks : 2048;
   if (kb == 64) {
     uint64_t* hkeys = reinterpret_cast<uint64_t*>(base + L.hkeys);
-    plan_prepare<uint64_t><<<prep, 256, 0, s>>>(h, n, B, X, Y, Z, kb, zbits, L.capacity, nmap, hkeys);
+    plan_prepare<uint64_t><<<prep, 256, 0, s>>>(h, n, B, X, Y, Z, kb, zbits, L.capacity, nmap, hkeys, zrow);
     hash_insert<uint64_t><<<grid1d(n, 256), 256, 0, s>>>(c4, n, B, X, Y, Z, hkeys, hvals, L.capacity,
                                                          &h->status_bits);
     probe_half<uint64_t><<<grid1d(n * kCentre, 256), 256, 0, s>>>(c4, n, B, X, Y, Z, hkeys, hvals,
                                                                   L.capacity, nmap);
   } else {
     uint32_t* hkeys = reinterpret_cast<uint32_t*>(base + L.hkeys);
-    plan_prepare<uint32_t><<<prep, 256, 0, s>>>(h, n, B, X, Y, Z, kb, zbits, L.capacity, nmap, hkeys);
+    plan_prepare<uint32_t><<<prep, 256, 0, s>>>(h, n, B, X, Y, Z, kb, zbits, L.capacity, nmap, hkeys, zrow);
     hash_insert<uint32_t><<<grid1d(n, 256), 256, 0, s>>>(c4, n, B, X, Y, Z, hkeys, hvals, L.capacity,
                                                          &h->status_bits);
     probe_half<uint32_t><<<grid1d(n * kCentre, 256), 256, 0, s>>>(c4, n, B, X, Y, Z, hkeys, hvals,

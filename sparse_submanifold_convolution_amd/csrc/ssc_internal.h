@@ -30,6 +30,9 @@ constexpr int kSortDirectBlocks = 64;
 constexpr int kPairRows = 256;
 // up to this many pair-list blocks, pair_scatter sums the block counts itself
 constexpr int kPairDirectBlocks = 256;
+// bytes of the plan's all-zero row: the GEMM loads it in place of a missing
+// neighbour or an out-of-range weight column, so that no load is conditional
+constexpr size_t kZeroRowBytes = 16384;
 // device-wide scan: elements per workgroup
 constexpr int kScanThreads = 256;
 constexpr int kScanItems = 16;
@@ -60,6 +63,7 @@ inline int ceil_log2_u64(uint64_t v) {
 // convolution calls read depend on n only and come first.
 struct PlanLayout {
   size_t header = 0;
+  size_t zrow = 0;    // kZeroRowBytes of zeros (a row of up to 4096 fp32 channels)
   size_t smask = 0;   // [n] u32: neighbour mask of the row at each sorted position
   size_t snmap = 0;   // [n][27] u32: nmap rows in sorted order, snmap[r] = nmap[perm[r]]
   size_t pair_i = 0;  // [27n] u32: pair lists, output row i
@@ -84,6 +88,7 @@ inline PlanLayout conv_layout(int64_t n) {
     return o;
   };
   L.header = 0;
+  L.zrow = take(kZeroRowBytes);
   L.smask = take(size_t(n) * 4);
   L.snmap = take(size_t(n) * kV * 4);
   L.pair_i = take(size_t(n) * kV * 4);

@@ -171,6 +171,23 @@ def test_small_parity(ssc, case):
     _full_parity(ssc, w)
 
 
+# Enough rows (over 512 tiles of 256) for the 8-wave GEMM tiles, with unequal
+# channel counts: reductions of 64 and 128 gather whole rows, 96 takes the
+# natural-order path; 96 output channels leave a ragged column block.
+MID = [
+    (10, 1, (64, 64, 64), 0.6, 128, 64, "f16", True),
+    (11, 2, (48, 48, 48), 0.7, 96, 128, "bf16", False),
+]
+
+
+@pytest.mark.parametrize("case", MID, ids=[f"m{c[0]}" for c in MID])
+def test_mid_parity(ssc, case):
+    seed, B, dims, p, ci, co, dt, shuffle = case
+    w = WL.random_workload(seed, B, dims, p, ci, co, dt, random_bias=True, shuffle=shuffle)
+    assert w.n > 512 * 256
+    _full_parity(ssc, w)
+
+
 def test_single_voxel(ssc):
     w = WL.values_for(np.array([[0, 3, 4, 5]], np.int32), (1, 8, 8, 8), 4, 32, 32, "f32")
     _full_parity(ssc, w)
