@@ -925,58 +925,80 @@ __global__ void __launch_bounds__(256) wgrad_reduce(const float* __restrict__ pa
   dW[int64_t(k) * cico + e] = Elt<T>::store(s);
 }
 
-// dbias stage 1: block (b, y) sums rows [b*rows, (b+1)*rows) of the 256
-// columns of chunk y.  Threads are 32 column vectors of 8 x 8 row phases; each
-// loads 16 bytes a row and the phases are added in a fixed order.
+// dbias stage 1: workgroup (x, y) sums rows [x*rows, (x+1)*rows) of the
+// column vectors [y*cvb, (y+1)*cvb) (16 bytes each).  Thread t takes vector
+// t % cvb and every (256/cvb)-th row from phase t / cvb, four loads in
+// flight, adding in increasing row order; the phases are then added in order.
 template <typename T>
 __global__ void __launch_bounds__(256) colsum_partial(const T* __restrict__ dY, int64_t n, int Co,
-                                                      int64_t rows, float* __restrict__ part) {
-  __shared__ float red[8][256];
-  const int cv = threadIdx.x & 31, ph = threadIdx.x >> 5;
-  const int col = blockIdx.y * 256 + cv * 8;
+                                                      int64_t rows, int cvb, float* __restrict__ part) {
+  constexpr int VEC = 16 / int(sizeof(T));
+  __shared__ float red[256 * VEC];
+  const int cv = threadIdx.x % cvb, ph = threadIdx.x / cvb, nph = 256 / cvb;
+  const int col = (blockIdx.y * cvb + cv) * VEC;
   const int64_t r0 = int64_t(blockIdx.x) * rows;
   const int64_t r1 = (r0 + rows < n) ? r0 + rows : n;
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  if (col < Co) {
-    for (int64_t r = r0 + ph; r < r1; r += 8) {
-      const uint4 v = *reinterpret_cast<const uint4*>(dY + r * Co + col);
-      const T* e = reinterpret_cast<const T*>(&v);
+  float acc[VEC];
 #pragma unroll
-      for (int q = 0; q < 16 / int(sizeof(T)); ++q) acc[q] += Elt<T>::load(e[q]);
-      if constexpr (sizeof(T) == 4) {
-        const uint4 w = *reinterpret_cast<const uint4*>(dY + r * Co + col + 4);
-        const T* f = reinterpret_cast<const T*>(&w);
+  for (int q = 0; q < VEC; ++q) acc[q] = 0.f;
+  auto add = [&](const u32x4& v) {
+    const T* e = reinterpret_cast<const T*>(&v);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) acc[4 + q] += Elt<T>::load(f[q]);
-      }
+    for (int q = 0; q < VEC; ++q) acc[q] += Elt<T>::load(e[q]);
+  };
+  if (col < Co && ph < nph) {
+    const T* base = dY + col;
+    int64_t r = r0 + ph;
+    for (; r + 3 * nph < r1; r += 4 * nph) {
+      u32x4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const u32x4*>(base + (r + u * nph) * Co);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) add(v[u]);
     }
+    for (; r < r1; r += nph) add(*reinterpret_cast<const u32x4*>(base + r * Co));
   }
+  if (ph < nph) {
 #pragma unroll
-  for (int q = 0; q < 8; ++q) red[ph][cv * 8 + q] = acc[q];
+    for (int q = 0; q < VEC; ++q) red[(ph * cvb + cv) * VEC + q] = acc[q];
+  }
   __syncthreads();
-  const int c = blockIdx.y * 256 + threadIdx.x;
-  if (c < Co) {
+  const int c = blockIdx.y * cvb * VEC + threadIdx.x;
+  if (threadIdx.x < cvb * VEC && c < Co) {
     float sum = 0.f;
-#pragma unroll
-    for (int q = 0; q < 8; ++q) sum += red[q][threadIdx.x];
+    for (int q = 0; q < nph; ++q) sum += red[q * cvb * VEC + threadIdx.x];
     part[int64_t(blockIdx.x) * Co + c] = sum;
   }
 }
 
-// dbias stage 2: 64 columns per workgroup, 4 phases each adding every 4th
-// partial, then the phases in a fixed order.
+// dbias stage 2: 16 columns per workgroup, 16 phases each adding every 16th
+// partial (four loads in flight), then the phases in a fixed order.
 template <typename T>
 __global__ void __launch_bounds__(256) colsum_final(const float* __restrict__ part, int nb, int Co,
                                                     T* __restrict__ dbias) {
-  __shared__ float red[4][64];
-  const int cl = threadIdx.x & 63, ph = threadIdx.x >> 6;
-  const int c = blockIdx.x * 64 + cl;
+  __shared__ float red[16][16];
+  const int cl = threadIdx.x & 15, ph = threadIdx.x >> 4;
+  const int c = blockIdx.x * 16 + cl;
   float s = 0.f;
-  if (c < Co)
-    for (int b = ph; b < nb; b += 4) s += part[int64_t(b) * Co + c];
+  if (c < Co) {
+    int b = ph;
+    for (; b + 48 < nb; b += 64) {
+      float v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = part[int64_t(b + 16 * u) * Co + c];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) s += v[u];
+    }
+    for (; b < nb; b += 16) s += part[int64_t(b) * Co + c];
+  }
   red[ph][cl] = s;
   __syncthreads();
-  if (ph == 0 && c < Co) dbias[c] = Elt<T>::store(((red[0][cl] + red[1][cl]) + red[2][cl]) + red[3][cl]);
+  if (ph == 0 && c < Co) {
+    float t = 0.f;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) t += red[q][cl];
+    dbias[c] = Elt<T>::store(t);
+  }
 }
 
 template <typename T>
@@ -1243,8 +1265,13 @@ static int run_bwd(const char* plan, const uint32_t* nmap, const int32_t* perm, 
   }
   if (dbias) {
     float* part = reinterpret_cast<float*>(ws + W.bias);
-    colsum_partial<T><<<dim3(unsigned(b.bias_blocks), unsigned((Co + 255) / 256)), 256, 0, s>>>(dY, n, Co, b.bias_rows, part);
-    colsum_final<T><<<unsigned((Co + 63) / 64), 256, 0, s>>>(part, b.bias_blocks, Co, static_cast<T*>(dbias));
+    // column vectors per workgroup: all of them up to 32, as a power of two
+    const int vec = 16 / int(sizeof(T)), nvec = Co / vec;
+    int cvb = 1;
+    while (cvb < nvec && cvb < 32) cvb *= 2;
+    colsum_partial<T><<<dim3(unsigned(b.bias_blocks), unsigned((nvec + cvb - 1) / cvb)), 256, 0, s>>>(
+        dY, n, Co, b.bias_rows, cvb, part);
+    colsum_final<T><<<unsigned((Co + 15) / 16), 256, 0, s>>>(part, b.bias_blocks, Co, static_cast<T*>(dbias));
   }
   return SSC_OK;
 }
