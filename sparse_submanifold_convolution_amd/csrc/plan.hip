@@ -285,6 +285,23 @@ __global__ void __launch_bounds__(256) probe_half(const int4* __restrict__ coord
 // loads coalesce.  Per row: the neighbour mask and the 64-bit sort key
 // (mask << zbits) | (b << 3*axis_bits) | zorder(x, y, z).  Per block: the
 // number of valid entries of each offset (the pair-list histogram).
+// The block's rows of nmap (up to 256 x kV entries) into LDS.  The loads of
+// all kV rounds are issued before the first store, so the copy costs one
+// memory round trip instead of kV.
+__device__ __forceinline__ void fetch_rows(const uint32_t* __restrict__ nmap, int64_t row0, int64_t here,
+                                           uint32_t (&v)[kV]) {
+  const int64_t lim = here * kV;
+#pragma unroll
+  for (int t = 0; t < kV; ++t) {
+    const int64_t e = int64_t(t) * 256 + threadIdx.x;
+    v[t] = e < lim ? nmap[row0 * kV + e] : kSentinel;
+  }
+}
+__device__ __forceinline__ void store_rows(uint32_t* rows, const uint32_t (&v)[kV]) {
+#pragma unroll
+  for (int t = 0; t < kV; ++t) rows[t * 256 + threadIdx.x] = v[t];
+}
+
 __global__ void __launch_bounds__(256) row_scan(const int4* __restrict__ coords, const uint32_t* __restrict__ nmap,
                                                 int64_t n, int B, int X, int Y, int Z, int axis_bits, int zbits,
                                                 uint64_t* __restrict__ sort_key, uint32_t* __restrict__ pcnt,
@@ -295,12 +312,14 @@ __global__ void __launch_bounds__(256) row_scan(const int4* __restrict__ coords,
   uint32_t local[kV];
 #pragma unroll
   for (int k = 0; k < kV; ++k) local[k] = 0;
-  for (int q = 0; q < kPairRows / 256; ++q) {
-    const int64_t row0 = int64_t(blockIdx.x) * kPairRows + q * 256;
-    if (row0 >= n) break;
+  static_assert(kPairRows == 256, "one row per thread");
+  {
+    const int64_t row0 = int64_t(blockIdx.x) * kPairRows;
     const int64_t here = (n - row0) < 256 ? (n - row0) : 256;
-    __syncthreads();
-    for (int64_t e = threadIdx.x; e < here * kV; e += 256) rows[e] = nmap[row0 * kV + e];
+    const int4 c = threadIdx.x < here ? coords[row0 + threadIdx.x] : make_int4(0, 0, 0, 0);
+    uint32_t v[kV];
+    fetch_rows(nmap, row0, here, v);
+    store_rows(rows, v);
     __syncthreads();
     if (threadIdx.x < here) {
       const int64_t i = row0 + threadIdx.x;
@@ -311,7 +330,6 @@ __global__ void __launch_bounds__(256) row_scan(const int4* __restrict__ coords,
         mask |= uint32_t(v) << k;
         local[k] += v ? 1u : 0u;
       }
-      const int4 c = coords[i];
       uint64_t key = 0;
       if (coord_ok(c.x, c.y, c.z, c.w, B, X, Y, Z)) {
         const uint64_t z = (uint64_t(uint32_t(c.x)) << (3 * axis_bits)) |
@@ -364,12 +382,34 @@ __global__ void __launch_bounds__(kSortThreads)
   __shared__ uint32_t wcnt[kSortThreads / 64][256];
   const int tid = threadIdx.x;
   const int wave = tid / 64;
+  // every round's keys and values are loaded before anything else
+  const int64_t blk0 = int64_t(blockIdx.x) * kSortBlockKeys;
+  uint64_t kk[kSortItems];
+  uint32_t vv[kSortItems];
+#pragma unroll
+  for (int q = 0; q < kSortItems; ++q) {
+    const int64_t idx = blk0 + int64_t(q) * kSortThreads + tid;
+    const bool valid = idx < n;
+    kk[q] = valid ? keys_in[idx] : 0ull;
+    vv[q] = valid ? (first ? uint32_t(idx) : vals_in[idx]) : 0u;
+  }
   if (direct) {
     // few blocks: this block's start for digit tid = (keys of smaller digits) +
     // (keys of digit tid in earlier blocks), read straight from the histograms
     __shared__ uint32_t waves_sum[kSortThreads / 64];
     uint32_t tot = 0, before = 0;
-    for (int64_t b = 0; b < nblk; ++b) {
+    int64_t b = 0;
+    for (; b + 3 < nblk; b += 4) {
+      uint32_t c[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) c[u] = offsets[int64_t(tid) * nblk + b + u];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        tot += c[u];
+        if (b + u < int64_t(blockIdx.x)) before += c[u];
+      }
+    }
+    for (; b < nblk; ++b) {
       const uint32_t c = offsets[int64_t(tid) * nblk + b];
       tot += c;
       if (b < int64_t(blockIdx.x)) before += c;
@@ -380,12 +420,12 @@ __global__ void __launch_bounds__(kSortThreads)
   } else {
     base[tid] = offsets[int64_t(tid) * nblk + blockIdx.x];
   }
-  const int64_t blk0 = int64_t(blockIdx.x) * kSortBlockKeys;
+#pragma unroll
   for (int q = 0; q < kSortItems; ++q) {
     const int64_t idx = blk0 + int64_t(q) * kSortThreads + tid;
     const bool valid = idx < n;
-    const uint64_t key = valid ? keys_in[idx] : 0ull;
-    const uint32_t val = valid ? (first ? uint32_t(idx) : vals_in[idx]) : 0u;
+    const uint64_t key = kk[q];
+    const uint32_t val = vv[q];
     const uint32_t d = uint32_t(key >> shift) & 255u;
 #pragma unroll
     for (int w = 0; w < kSortThreads / 64; ++w) wcnt[w][tid] = 0;
@@ -452,15 +492,36 @@ __global__ void __launch_bounds__(256) pair_scatter(const uint32_t* __restrict__
   __shared__ uint32_t base[32];
   __shared__ uint32_t tot[32];
   __shared__ uint32_t wc[kV][4];
+  __shared__ uint32_t rows[256 * kV];
   const int tid = threadIdx.x;
   const int wave = tid / 64;
+  static_assert(kPairRows == 256, "one row per thread");
+  const int64_t rbase = int64_t(blockIdx.x) * kPairRows;
+  const int64_t here = (n - rbase) < 256 ? (n - rbase) : 256;
+  {
+    // the rows' loads go out first; the offsets below overlap them
+    uint32_t v[kV];
+    fetch_rows(nmap, rbase, here, v);
+    store_rows(rows, v);
+  }
   if (direct) {
     // offset k = tid / 8 summed over blocks b = tid % 8 (mod 8), then the 8 sums in order
     __shared__ uint32_t part_t[kV][8], part_b[kV][8];
     if (tid < kV * 8) {
       const int k = tid >> 3, ph = tid & 7;
       uint32_t t = 0, before = 0;
-      for (int64_t b = ph; b < pblk; b += 8) {
+      int64_t b = ph;
+      for (; b + 24 < pblk; b += 32) {
+        uint32_t c[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) c[u] = pcnt[int64_t(k) * pblk + b + 8 * u];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          t += c[u];
+          if (b + 8 * u < int64_t(blockIdx.x)) before += c[u];
+        }
+      }
+      for (; b < pblk; b += 8) {
         const uint32_t c = pcnt[int64_t(k) * pblk + b];
         t += c;
         if (b < int64_t(blockIdx.x)) before += c;
@@ -495,13 +556,7 @@ __global__ void __launch_bounds__(256) pair_scatter(const uint32_t* __restrict__
   __syncthreads();
   // where this block's rows start in each list (the weight gradient chunks by rows)
   if (tid < kV) pseg[int64_t(tid) * (pblk + 1) + blockIdx.x] = base[tid];
-  __shared__ uint32_t rows[256 * kV];
-  for (int q = 0; q < kPairRows / 256; ++q) {
-    const int64_t rbase = int64_t(blockIdx.x) * kPairRows + q * 256;
-    if (rbase >= n) break;
-    const int64_t here = (n - rbase) < 256 ? (n - rbase) : 256;
-    for (int64_t e = tid; e < here * kV; e += 256) rows[e] = nmap[rbase * kV + e];
-    __syncthreads();
+  {
     const int64_t row = rbase + tid;
     const bool in = row < n;
     uint32_t j[kV];
