@@ -11,7 +11,8 @@
 //   plan_prepare    header fields, status word, pair counters; the zero row;
 //                   sentinel fill of nmap; empty (all ones) fill of the hash keys
 //   hash_insert     coordinate check, key packing, open-addressing insert with
-//                   atomicCAS on 32- or 64-bit keys; value = row index
+//                   atomicCAS on 32- or 64-bit keys; the row index is stored
+//                   in the same slot, so a lookup is one load
 //   probe_half      one lookup per (voxel, offset k < 13), bounds checked per
 //                   axis before a key is packed (no off-grid neighbour can alias
 //                   a real one); a hit j fills nmap[i][k] and its mirror
@@ -55,6 +56,20 @@ __device__ __forceinline__ uint32_t mix_hash(uint64_t k) {
   k ^= k >> 33;
   return uint32_t(k);
 }
+
+// One hash-table slot: the key and its row index side by side, so a lookup
+// that hits reads one aligned 8- or 16-byte entry.
+template <typename KeyT>
+struct Slot;
+template <>
+struct __align__(8) Slot<uint32_t> {
+  uint32_t key, val;
+};
+template <>
+struct __align__(16) Slot<uint64_t> {
+  uint64_t key;
+  uint32_t val, pad;
+};
 
 template <typename KeyT>
 __device__ __forceinline__ KeyT empty_key() {
@@ -182,7 +197,7 @@ static void launch_scan(uint32_t* data, int64_t len, uint32_t* tmp, hipStream_t 
 template <typename KeyT>
 __global__ void __launch_bounds__(256) plan_prepare(PlanHeader* h, int64_t n, int B, int X, int Y, int Z,
                                                    int key_bits, int zbits, uint64_t capacity,
-                                                   uint32_t* __restrict__ nmap, KeyT* __restrict__ keys,
+                                                   uint32_t* __restrict__ nmap, Slot<KeyT>* __restrict__ table,
                                                    uint4* __restrict__ zrow) {
   if (blockIdx.x == 0) {
     if (threadIdx.x == 0) {
@@ -206,14 +221,14 @@ __global__ void __launch_bounds__(256) plan_prepare(PlanHeader* h, int64_t n, in
   const int64_t t0 = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   for (int64_t i = t0; i < int64_t(kZeroRowBytes / 16); i += stride) zrow[i] = make_uint4(0, 0, 0, 0);
   for (int64_t i = t0; i < n * kV; i += stride) nmap[i] = kSentinel;
-  for (int64_t i = t0; i < int64_t(capacity); i += stride) keys[i] = empty_key<KeyT>();
+  for (int64_t i = t0; i < int64_t(capacity); i += stride) table[i].key = empty_key<KeyT>();
 }
 
 template <typename KeyT>
 __global__ void __launch_bounds__(256) hash_insert(const int4* __restrict__ coords, int64_t n,
                                                    int B, int X, int Y, int Z,
-                                                   KeyT* __restrict__ keys, uint32_t* __restrict__ vals,
-                                                   uint64_t capacity, uint32_t* __restrict__ status) {
+                                                   Slot<KeyT>* __restrict__ table, uint64_t capacity,
+                                                   uint32_t* __restrict__ status) {
   const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   if (i >= n) return;
   const int4 c = coords[i];
@@ -225,9 +240,9 @@ __global__ void __launch_bounds__(256) hash_insert(const int4* __restrict__ coor
   const uint64_t mask = capacity - 1;
   uint64_t slot = mix_hash(key) & mask;
   for (uint64_t probe = 0; probe < capacity; ++probe) {
-    KeyT prev = atomicCAS(&keys[slot], empty_key<KeyT>(), key);
+    KeyT prev = atomicCAS(&table[slot].key, empty_key<KeyT>(), key);
     if (prev == empty_key<KeyT>()) {
-      vals[slot] = uint32_t(i);
+      table[slot].val = uint32_t(i);
       return;
     }
     if (prev == key) {
@@ -240,15 +255,14 @@ __global__ void __launch_bounds__(256) hash_insert(const int4* __restrict__ coor
 }
 
 template <typename KeyT>
-__device__ __forceinline__ uint32_t hash_lookup(const KeyT* __restrict__ keys,
-                                                const uint32_t* __restrict__ vals, uint64_t capacity,
+__device__ __forceinline__ uint32_t hash_lookup(const Slot<KeyT>* __restrict__ table, uint64_t capacity,
                                                 KeyT key) {
   const uint64_t mask = capacity - 1;
   uint64_t slot = mix_hash(key) & mask;
   for (uint64_t probe = 0; probe < capacity; ++probe) {
-    const KeyT k = keys[slot];
-    if (k == key) return vals[slot];
-    if (k == empty_key<KeyT>()) return kSentinel;
+    const Slot<KeyT> e = table[slot];
+    if (e.key == key) return e.val;
+    if (e.key == empty_key<KeyT>()) return kSentinel;
     slot = (slot + 1) & mask;
   }
   return kSentinel;
@@ -261,9 +275,8 @@ __device__ __forceinline__ uint32_t hash_lookup(const KeyT* __restrict__ keys,
 // with.  The centre entry is the row itself.
 template <typename KeyT>
 __global__ void __launch_bounds__(256) probe_half(const int4* __restrict__ coords, int64_t n, int B, int X,
-                                                  int Y, int Z, const KeyT* __restrict__ keys,
-                                                  const uint32_t* __restrict__ vals, uint64_t capacity,
-                                                  uint32_t* __restrict__ nmap) {
+                                                  int Y, int Z, const Slot<KeyT>* __restrict__ table,
+                                                  uint64_t capacity, uint32_t* __restrict__ nmap) {
   const int64_t g = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   if (g >= n * kCentre) return;
   const int64_t i = g / kCentre;
@@ -275,7 +288,7 @@ __global__ void __launch_bounds__(256) probe_half(const int4* __restrict__ coord
   const int py = c.z + (k / 3) % 3 - 1;
   const int pz = c.w + k % 3 - 1;
   if (px < 0 || px >= X || py < 0 || py >= Y || pz < 0 || pz >= Z) return;
-  const uint32_t j = hash_lookup<KeyT>(keys, vals, capacity, KeyT(pack_key(c.x, px, py, pz, X, Y, Z)));
+  const uint32_t j = hash_lookup<KeyT>(table, capacity, KeyT(pack_key(c.x, px, py, pz, X, Y, Z)));
   if (j == kSentinel) return;
   nmap[i * kV + k] = j;
   nmap[int64_t(j) * kV + (kV - 1 - k)] = uint32_t(i);
@@ -656,14 +669,13 @@ extern "C" int ssc_build_neighbor_map(const int32_t* coords, int64_t n, int32_t 
   if (n == 0) {
     // header only (the key fill touches the plan's own table region)
     plan_prepare<uint32_t><<<1, 256, 0, s>>>(h, 0, B, X, Y, Z, kb, zbits, L.capacity, nullptr,
-                                             reinterpret_cast<uint32_t*>(base + L.hkeys), zrow);
+                                             reinterpret_cast<Slot<uint32_t>*>(base + L.table), zrow);
     return hipGetLastError() == hipSuccess ? SSC_OK : SSC_ERR_HIP;
   }
 
   uint32_t* smask = reinterpret_cast<uint32_t*>(base + L.smask);
   uint32_t* pair_i = reinterpret_cast<uint32_t*>(base + L.pair_i);
   uint32_t* pair_j = reinterpret_cast<uint32_t*>(base + L.pair_j);
-  uint32_t* hvals = reinterpret_cast<uint32_t*>(base + L.hvals);
   uint64_t* key0 = reinterpret_cast<uint64_t*>(base + L.key0);
   uint64_t* key1 = reinterpret_cast<uint64_t*>(base + L.key1);
   uint32_t* val0 = reinterpret_cast<uint32_t*>(base + L.val0);
@@ -677,19 +689,19 @@ extern "C" int ssc_build_neighbor_map(const int32_t* coords, int64_t n, int32_t 
   const unsigned prep_blocks = grid1d((n * kV > int64_t(L.capacity) ? n * kV : int64_t(L.capacity)) / 4, 256);
   const unsigned prep = prep_blocks < 2048 ? prep_blocks : 2048;
   if (kb == 64) {
-    uint64_t* hkeys = reinterpret_cast<uint64_t*>(base + L.hkeys);
-    plan_prepare<uint64_t><<<prep, 256, 0, s>>>(h, n, B, X, Y, Z, kb, zbits, L.capacity, nmap, hkeys, zrow);
-    hash_insert<uint64_t><<<grid1d(n, 256), 256, 0, s>>>(c4, n, B, X, Y, Z, hkeys, hvals, L.capacity,
+    Slot<uint64_t>* table = reinterpret_cast<Slot<uint64_t>*>(base + L.table);
+    plan_prepare<uint64_t><<<prep, 256, 0, s>>>(h, n, B, X, Y, Z, kb, zbits, L.capacity, nmap, table, zrow);
+    hash_insert<uint64_t><<<grid1d(n, 256), 256, 0, s>>>(c4, n, B, X, Y, Z, table, L.capacity,
                                                          &h->status_bits);
-    probe_half<uint64_t><<<grid1d(n * kCentre, 256), 256, 0, s>>>(c4, n, B, X, Y, Z, hkeys, hvals,
-                                                                  L.capacity, nmap);
+    probe_half<uint64_t><<<grid1d(n * kCentre, 256), 256, 0, s>>>(c4, n, B, X, Y, Z, table, L.capacity,
+                                                                  nmap);
   } else {
-    uint32_t* hkeys = reinterpret_cast<uint32_t*>(base + L.hkeys);
-    plan_prepare<uint32_t><<<prep, 256, 0, s>>>(h, n, B, X, Y, Z, kb, zbits, L.capacity, nmap, hkeys, zrow);
-    hash_insert<uint32_t><<<grid1d(n, 256), 256, 0, s>>>(c4, n, B, X, Y, Z, hkeys, hvals, L.capacity,
+    Slot<uint32_t>* table = reinterpret_cast<Slot<uint32_t>*>(base + L.table);
+    plan_prepare<uint32_t><<<prep, 256, 0, s>>>(h, n, B, X, Y, Z, kb, zbits, L.capacity, nmap, table, zrow);
+    hash_insert<uint32_t><<<grid1d(n, 256), 256, 0, s>>>(c4, n, B, X, Y, Z, table, L.capacity,
                                                          &h->status_bits);
-    probe_half<uint32_t><<<grid1d(n * kCentre, 256), 256, 0, s>>>(c4, n, B, X, Y, Z, hkeys, hvals,
-                                                                  L.capacity, nmap);
+    probe_half<uint32_t><<<grid1d(n * kCentre, 256), 256, 0, s>>>(c4, n, B, X, Y, Z, table, L.capacity,
+                                                                  nmap);
   }
   row_scan<<<unsigned(pblk), 256, 0, s>>>(c4, nmap, n, B, X, Y, Z, axis_bits, zbits, key0, pcnt, pblk);
 

@@ -70,8 +70,8 @@ struct PlanLayout {
   size_t pair_j = 0;  // [27n] u32: pair lists, input row j = nmap[i][k]
   size_t pseg = 0;    // [27][pblk + 1] u32: where each kPairRows block of rows starts in each list
   // build-only scratch
-  size_t hkeys = 0, hvals = 0, key0 = 0, key1 = 0, val0 = 0, val1 = 0, hist = 0, pcnt = 0,
-         scan_tmp = 0;
+  size_t table = 0;  // hash slots: {key, row} pairs, 8 bytes (32-bit keys) or 16 (64-bit)
+  size_t key0 = 0, key1 = 0, val0 = 0, val1 = 0, hist = 0, pcnt = 0, scan_tmp = 0;
   size_t total = 0;
   uint64_t capacity = 0;
   int key_bytes = 4;
@@ -111,8 +111,7 @@ inline PlanLayout plan_layout(int64_t n, int key_bits) {
   L.key_bytes = key_bits == 64 ? 8 : 4;
   L.sort_blocks = (n + kSortBlockKeys - 1) / kSortBlockKeys;
   L.pair_blocks = (n + kPairRows - 1) / kPairRows;
-  L.hkeys = take(L.capacity * L.key_bytes);
-  L.hvals = take(L.capacity * 4);
+  L.table = take(L.capacity * (L.key_bytes == 8 ? 16 : 8));
   L.key0 = take(size_t(n) * 8);
   L.key1 = take(size_t(n) * 8);
   L.val0 = take(size_t(n) * 4);
