@@ -131,11 +131,14 @@ size_t ssc_conv_workspace_bytes(int64_t n, int32_t Ci, int32_t Co, int32_t dtype
 /*
  * Forward pass: out[n][Co] = the definition of out above.
  *   plan, nmap, perm  as filled by ssc_build_neighbor_map for these n rows.
+ *                     The kernels read the plan (its sorted-order copy of
+ *                     nmap, the sorted masks, the pair lists) and perm;
+ *                     nmap itself is only checked (non-NULL, aligned).
  *   feats  [n][Ci], weight [27][Ci][Co], bias [Co] or NULL (zero), all `dtype`.
  *   out    [n][Co] `dtype`, out.
  * Ci and Co must be multiples of 16 and at most 4096.  The kernel walks
  * tiles of rows in perm order and, per tile, only the offsets some row of
- * the tile has; rows are gathered through nmap, products run on MFMA with
+ * the tile has; rows are gathered through the map, products run on MFMA with
  * fp32 accumulation, and out is rounded to `dtype` once.
  */
 int ssc_subm_conv3d_fwd(const void* plan, const uint32_t* nmap, const int32_t* perm, int64_t n,
