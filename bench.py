@@ -45,6 +45,9 @@ def parse():
     p.add_argument("--cpu-budget-s", type=float, default=20.0)
     p.add_argument("--copy-calib", type=int, default=0,
                    help="only run a device copy of this many MiB (HBM counter calibration)")
+    p.add_argument("--serialize", action="store_true",
+                   help="only time encode_seq + decode_seq (z-order and Hilbert) on the workload's "
+                        "coordinates; prints its own JSON line")
     return p.parse_args()
 
 
@@ -122,6 +125,76 @@ def cpu_baseline(w, budget_s: float) -> dict:
             "stage_seconds": {k: v / reps for k, v in t_stage.items()}}
 
 
+def serialize_bench(args) -> None:
+    """encode_seq + decode_seq in both modes on the workload's coordinates, inputs resident in HBM.
+
+    Each measured sequence is captured once in a HIP graph and replayed, so host-side
+    marshalling stays out of the timed region.
+    """
+    import torch
+    import sparse_submanifold_convolution_amd as ssc
+    from sparse_submanifold_convolution_amd import workloads as WL
+
+    dev = torch.device("cuda:0")
+    w = WL.make_workload(args.config)
+    coords = torch.from_numpy(w.coords).to(dev)
+    width = ssc.seq_code_width(w.shape)
+    reps = 20
+    side = torch.cuda.Stream(dev)
+
+    def timed(fn):
+        side.wait_stream(torch.cuda.current_stream(dev))
+        with torch.cuda.stream(side):
+            fn()  # warm the allocator outside capture
+        torch.cuda.current_stream(dev).wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(reps):
+                fn()
+        for _ in range(max(1, args.warmup)):
+            g.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        best = 1e30
+        for _ in range(args.steps):
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            best = min(best, e0.elapsed_time(e1) / reps)
+        return best
+
+    per, results = {}, {}
+    for mode in ("z_order", "hilbert"):
+        codes = ssc.encode_seq(coords, w.shape, mode)
+        results[mode] = ssc.decode_seq(codes, w.shape, mode)
+        per[f"{mode}_encode"] = timed(lambda m=mode: ssc.encode_seq(coords, w.shape, m))
+        per[f"{mode}_decode"] = timed(lambda m=mode, c=codes: ssc.decode_seq(c, w.shape, m))
+    torch.cuda.synchronize()
+    ok = all(torch.equal(v, coords) for v in results.values())
+    ms = sum(per.values())
+    # algorithmic bytes per launch: 16-byte rows in and a 4- or 8-byte code out (or the reverse)
+    bytes_per_launch = w.n * (16 + width // 8)
+    dom = max(per, key=per.get)
+    ach = bytes_per_launch / (per[dom] * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "voxels/s, encode_seq + decode_seq (z-order and Hilbert), 1 MI355X",
+        "value": 4 * w.n / (ms * 1e-3), "unit": "voxels/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": f"int{width}", "data": "synthetic",
+        "config": {"workload": f"config {args.config}: {w.desc}", "voxels": w.n, "code_width": width,
+                   "step": "encode + decode, z-order and Hilbert (four launches)",
+                   "launch": f"graph of {reps} calls per launch kind, best replay",
+                   "parallelism": "single GPU"},
+        "per_call_ms": per, "round_trip_exact": ok,
+        "roofline": {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": ach / PEAK_HBM_GBS, "traffic": None, "kernel": f"seq_{dom}",
+                     "avg_launch_ms": per[dom], "alg_bytes_per_launch": bytes_per_launch},
+    }), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -130,6 +203,9 @@ def main():
         sys.exit(2)
     if args.copy_calib:
         copy_calibration(args.copy_calib)
+        return
+    if args.serialize:
+        serialize_bench(args)
         return
 
     import numpy as np

@@ -161,6 +161,53 @@ int ssc_subm_conv3d_bwd(const void* plan, const uint32_t* nmap, const int32_t* p
                         const void* weight, const void* dout, void* dfeats, void* dweight,
                         void* dbias, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Voxel serialisation: encode_seq / decode_seq of the report's serialize
+ * module (section two: the ops.serialize and kernels.cuda.serialize rows and
+ * the z_order / hilbert encode and decode functions; section three: the
+ * serialize snippet, which round-trips coordinates).  Layout of a code, for
+ * a grid (B, X, Y, Z) with n = ceil(log2(max(X, Y, Z))) bits per axis:
+ *   code = (b << 3n) | index(x, y, z),
+ * where index is the z-order index (bits interleaved from the top, x most
+ * significant in each triplet -- the key the plan's row sort uses) or the
+ * Hilbert index of J. Skilling's transform (AIP Conf. Proc. 707, 2004) with
+ * axes (x, y, z), its transposed bits interleaved the same way.  A code is
+ * int32 when it needs at most 31 bits, else int64.
+ */
+enum ssc_seq_mode {
+  SSC_SEQ_ZORDER = 0,
+  SSC_SEQ_HILBERT = 1
+};
+
+/* Bits of a code for this grid, or -1 for invalid dimensions (each in
+ * [1, 2^20]).  Needs no GPU. */
+int32_t ssc_seq_code_bits(int32_t B, int32_t X, int32_t Y, int32_t Z);
+
+/* 32 or 64: the code width for this grid (32 when the code fits 31 bits);
+ * -1 for invalid dimensions or codes wider than 63 bits.  Needs no GPU. */
+int32_t ssc_seq_code_width(int32_t B, int32_t X, int32_t Y, int32_t Z);
+
+/*
+ * codes[i] = the code of coords[i], or -1 for a row outside the grid.
+ *   coords  [n][4] int32 rows (b, x, y, z), 16-byte aligned.
+ *   mode    an ssc_seq_mode.
+ *   codes   [n] int32 (code_width 32) or int64 (code_width 64), out.
+ * code_width may exceed ssc_seq_code_width (64 is always allowed when the
+ * grid fits); a narrower width, a bad mode or bad dimensions return
+ * SSC_ERR_UNSUPPORTED / SSC_ERR_INVALID_ARG with nothing enqueued.
+ */
+int ssc_encode_seq(const int32_t* coords, int64_t n, int32_t B, int32_t X, int32_t Y, int32_t Z,
+                   int32_t mode, void* codes, int32_t code_width, void* stream);
+
+/*
+ * coords[i] = the row (b, x, y, z) whose code is codes[i]; (-1, -1, -1, -1)
+ * for a negative code or one that names no cell of the grid (the curve
+ * covers the cube of side 2^n, which may exceed X, Y or Z).  Same argument
+ * rules as ssc_encode_seq; coords [n][4] int32, 16-byte aligned, out.
+ */
+int ssc_decode_seq(const void* codes, int64_t n, int32_t B, int32_t X, int32_t Y, int32_t Z,
+                   int32_t mode, int32_t code_width, int32_t* coords, void* stream);
+
 /* Static, human-readable name of a status code (host only). */
 const char* ssc_status_string(int status);
 

@@ -31,7 +31,13 @@ SIGNATURES = {
     "ssc_subm_conv3d_bwd": (ctypes.c_int, [_VP, _VP, _VP, _I64, _I32, _I32, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                                            _SZ, _VP]),
     "ssc_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "ssc_seq_code_bits": (_I32, [_I32, _I32, _I32, _I32]),
+    "ssc_seq_code_width": (_I32, [_I32, _I32, _I32, _I32]),
+    "ssc_encode_seq": (ctypes.c_int, [_VP, _I64, _I32, _I32, _I32, _I32, _I32, _VP, _I32, _VP]),
+    "ssc_decode_seq": (ctypes.c_int, [_VP, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _VP, _VP]),
 }
+
+SEQ_MODES = {"z_order": 0, "hilbert": 1}
 
 
 class SSCError(RuntimeError):
@@ -225,3 +231,59 @@ class SubmConv3dFunction(torch.autograd.Function):
 def subm_conv3d(feats: torch.Tensor, plan: Plan, weight: torch.Tensor, bias: torch.Tensor | None = None):
     """Differentiable submanifold convolution over a built plan."""
     return SubmConv3dFunction.apply(feats, weight, bias, plan)
+
+
+# ---------------------------------------------------------------------------
+# serialisation
+# ---------------------------------------------------------------------------
+
+def _grid(shape) -> tuple:
+    """(B, X, Y, Z) from a (B, X, Y, Z) or (B, C, X, Y, Z) shape; C is ignored."""
+    s = tuple(int(v) for v in shape)
+    if len(s) == 5:
+        s = (s[0],) + s[2:]
+    if len(s) != 4:
+        raise ValueError(f"shape must be (B, X, Y, Z) or (B, C, X, Y, Z), got {shape}")
+    return s
+
+
+def _mode(mode: str) -> int:
+    if mode not in SEQ_MODES:
+        raise ValueError(f"mode must be one of {tuple(SEQ_MODES)}, got {mode!r}")
+    return SEQ_MODES[mode]
+
+
+def seq_code_width(shape) -> int:
+    """32 or 64: the code width ssc_encode_seq picks for this grid."""
+    w = int(lib().ssc_seq_code_width(*_grid(shape)))
+    if w < 0:
+        raise SSCError("ssc_seq_code_width", 2)
+    return w
+
+
+def encode_seq(coords: torch.Tensor, shape, mode: str = "z_order") -> torch.Tensor:
+    """ssc_encode_seq: int32 [n, 4] rows (b, x, y, z) -> [n] codes (int32 or int64 by grid size)."""
+    dev = coords.device
+    n = int(coords.shape[0])
+    _need(coords, "coords", torch.int32, (n, 4), dev)
+    grid = _grid(shape)
+    width = seq_code_width(grid)
+    codes = torch.empty((n,), dtype=torch.int32 if width == 32 else torch.int64, device=dev)
+    _check("ssc_encode_seq", lib().ssc_encode_seq(_ptr(coords), n, *grid, _mode(mode), _ptr(codes), width,
+                                                  _stream(dev)))
+    return codes
+
+
+def decode_seq(codes: torch.Tensor, shape, mode: str = "z_order") -> torch.Tensor:
+    """ssc_decode_seq: [n] int32 or int64 codes -> int32 [n, 4] rows; (-1, -1, -1, -1) where none."""
+    dev = codes.device
+    n = int(codes.shape[0])
+    if codes.dtype not in (torch.int32, torch.int64) or codes.dim() != 1 or not codes.is_contiguous():
+        raise ValueError(f"codes: expected a contiguous 1-d int32 or int64 tensor, got {codes.dtype} "
+                         f"{tuple(codes.shape)}")
+    grid = _grid(shape)
+    width = 32 if codes.dtype == torch.int32 else 64
+    coords = torch.empty((n, 4), dtype=torch.int32, device=dev)
+    _check("ssc_decode_seq", lib().ssc_decode_seq(_ptr(codes), n, *grid, _mode(mode), width, _ptr(coords),
+                                                  _stream(dev)))
+    return coords

@@ -91,15 +91,6 @@ __device__ __forceinline__ uint64_t pack_key(int b, int x, int y, int z, int X, 
 }
 
 // interleave the low `bits` bits of x, y, z: triplet (x, y, z) per bit, x highest
-__device__ __forceinline__ uint64_t zorder(uint32_t x, uint32_t y, uint32_t z, int bits) {
-  uint64_t code = 0;
-  for (int b = 0; b < bits; ++b) {
-    code |= uint64_t((x >> b) & 1u) << (3 * b + 2);
-    code |= uint64_t((y >> b) & 1u) << (3 * b + 1);
-    code |= uint64_t((z >> b) & 1u) << (3 * b);
-  }
-  return code;
-}
 
 // ---------------------------------------------------------------------------
 // device-wide exclusive scan of uint32

@@ -125,6 +125,18 @@ inline PlanLayout plan_layout(int64_t n, int key_bits) {
   return L;
 }
 
+// z-order index of (x, y, z) over `bits` bits per axis: bits interleaved from
+// the top, each triplet (x, y, z) with x most significant.
+__device__ __forceinline__ uint64_t zorder(uint32_t x, uint32_t y, uint32_t z, int bits) {
+  uint64_t code = 0;
+  for (int b = 0; b < bits; ++b) {
+    code |= uint64_t((x >> b) & 1u) << (3 * b + 2);
+    code |= uint64_t((y >> b) & 1u) << (3 * b + 1);
+    code |= uint64_t((z >> b) & 1u) << (3 * b);
+  }
+  return code;
+}
+
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 }  // namespace ssc

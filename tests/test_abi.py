@@ -100,3 +100,32 @@ def test_binding_raises_without_library(monkeypatch):
     monkeypatch.setattr(binding, "_LIB_PATH", "/nonexistent/libssc.so")
     with pytest.raises(RuntimeError):
         binding.lib()
+
+
+def test_seq_width_and_bits(L):
+    assert L.ssc_seq_code_bits(1, 64, 64, 64) == 18 and L.ssc_seq_code_width(1, 64, 64, 64) == 32
+    assert L.ssc_seq_code_bits(2, 1024, 1024, 1024) == 31 and L.ssc_seq_code_width(2, 1024, 1024, 1024) == 32
+    assert L.ssc_seq_code_width(3, 1024, 1024, 1024) == 64
+    assert L.ssc_seq_code_bits(1, 1, 1, 1) == 0
+    assert L.ssc_seq_code_bits(0, 4, 4, 4) == -1 and L.ssc_seq_code_width(1, 0, 4, 4) == -1
+    assert L.ssc_seq_code_width(1 << 20, 1 << 20, 1, 1) == -1  # 80-bit codes
+
+
+def test_seq_rejections(L):
+    ok, bad_arg, unsup = 0, 1, 2
+    c = ctypes.c_void_p(FAKE.value)
+    k = ctypes.c_void_p(FAKE.value + 256)
+    enc, dec = L.ssc_encode_seq, L.ssc_decode_seq
+    assert enc(c, -1, 1, 8, 8, 8, 0, k, 32, None) == bad_arg
+    assert enc(c, 10, 0, 8, 8, 8, 0, k, 32, None) == bad_arg
+    assert enc(c, 10, 1, 8, 8, 8, 2, k, 32, None) == unsup           # no such mode
+    assert enc(c, 10, 1, 8, 8, 8, 0, k, 16, None) == unsup           # no such width
+    assert enc(c, 10, 3, 1024, 1024, 1024, 0, k, 32, None) == unsup  # needs 64-bit codes
+    assert enc(None, 10, 1, 8, 8, 8, 0, k, 32, None) == bad_arg
+    assert enc(ctypes.c_void_p(FAKE.value + 4), 10, 1, 8, 8, 8, 0, k, 32, None) == bad_arg
+    assert enc(c, 10, 1, 8, 8, 8, 0, ctypes.c_void_p(FAKE.value + 260), 64, None) == bad_arg
+    assert enc(c, 0, 1, 8, 8, 8, 1, k, 64, None) == ok                # nothing to do
+    assert dec(k, 10, 1, 8, 8, 8, 5, 32, c, None) == unsup
+    assert dec(k, 10, 1, 8, 8, 8, 0, 32, None, None) == bad_arg
+    assert dec(k, 10, 1, 8, 8, 8, 0, 32, ctypes.c_void_p(FAKE.value + 8), None) == bad_arg
+    assert dec(k, 0, 1, 8, 8, 8, 0, 64, c, None) == ok
