@@ -28,28 +28,33 @@ namespace ssc {
 
 namespace {
 
+// Grids have at most 2^20 cells per axis, so a curve has at most 20 levels;
+// the level loops below run a fixed count (fully unrolled) with a uniform
+// guard, and each per-axis step is a select, not a branch.
+constexpr int kMaxLevel = 20;
+
 // Axes -> transposed Hilbert index, in place.
 __device__ __forceinline__ void hilbert_from_axes(uint32_t (&t)[3], int bits) {
-  if (bits == 0) return;
-  const uint32_t top = 1u << (bits - 1);
-  for (uint32_t q = top; q > 1; q >>= 1) {
-    const uint32_t low = q - 1;
 #pragma unroll
-    for (int i = 0; i < 3; ++i) {
-      if (t[i] & q) {
-        t[0] ^= low;
-      } else {
+  for (int lvl = kMaxLevel - 1; lvl >= 1; --lvl) {  // q = 2^lvl from the top bit down to 2
+    if (lvl < bits) {
+      const uint32_t q = 1u << lvl, low = q - 1;
+      t[0] ^= (t[0] & q) ? low : 0u;  // axis 0: invert, or a swap with itself
+#pragma unroll
+      for (int i = 1; i < 3; ++i) {
         const uint32_t sw = (t[0] ^ t[i]) & low;
-        t[0] ^= sw;
-        t[i] ^= sw;
+        const bool set = (t[i] & q) != 0;
+        t[0] ^= set ? low : sw;
+        t[i] ^= set ? 0u : sw;
       }
     }
   }
   t[1] ^= t[0];
   t[2] ^= t[1];
   uint32_t flip = 0;
-  for (uint32_t q = top; q > 1; q >>= 1)
-    if (t[2] & q) flip ^= q - 1;
+#pragma unroll
+  for (int lvl = kMaxLevel - 1; lvl >= 1; --lvl)
+    if (lvl < bits && (t[2] & (1u << lvl))) flip ^= (1u << lvl) - 1;
   t[0] ^= flip;
   t[1] ^= flip;
   t[2] ^= flip;
@@ -62,29 +67,27 @@ __device__ __forceinline__ void hilbert_to_axes(uint32_t (&a)[3], int bits) {
   a[2] ^= a[1];
   a[1] ^= a[0];
   a[0] ^= g;
-  for (uint32_t q = 2; q != (1u << bits); q <<= 1) {
-    const uint32_t low = q - 1;
 #pragma unroll
-    for (int i = 2; i >= 0; --i) {
-      if (a[i] & q) {
-        a[0] ^= low;
-      } else {
+  for (int lvl = 1; lvl < kMaxLevel; ++lvl) {  // q = 2^lvl from 2 up to the top bit
+    if (lvl < bits) {
+      const uint32_t q = 1u << lvl, low = q - 1;
+#pragma unroll
+      for (int i = 2; i >= 1; --i) {
         const uint32_t sw = (a[0] ^ a[i]) & low;
-        a[0] ^= sw;
-        a[i] ^= sw;
+        const bool set = (a[i] & q) != 0;
+        a[0] ^= set ? low : sw;
+        a[i] ^= set ? 0u : sw;
       }
+      a[0] ^= (a[0] & q) ? low : 0u;
     }
   }
 }
 
 // inverse of zorder(): the three axes of a z-order index
-__device__ __forceinline__ void zorder_split(uint64_t code, int bits, uint32_t (&a)[3]) {
-  a[0] = a[1] = a[2] = 0;
-  for (int b = 0; b < bits; ++b) {
-    a[0] |= uint32_t((code >> (3 * b + 2)) & 1u) << b;
-    a[1] |= uint32_t((code >> (3 * b + 1)) & 1u) << b;
-    a[2] |= uint32_t((code >> (3 * b)) & 1u) << b;
-  }
+__device__ __forceinline__ void zorder_split(uint64_t code, int /*bits*/, uint32_t (&a)[3]) {
+  a[0] = gather3(code >> 2);
+  a[1] = gather3(code >> 1);
+  a[2] = gather3(code);
 }
 
 template <typename CodeT>
