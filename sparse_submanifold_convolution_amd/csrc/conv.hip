@@ -709,18 +709,23 @@ __device__ __forceinline__ s16x4 lds_tr16(const void* p) {
 // Pipeline: pair indices for group g+1 are written to LDS at the first stage
 // of group g (fetched one group earlier into registers); row gathers for stage
 // s+DEPTH are issued during stage s from indices already in LDS; the stage's
-// rows go through double-buffered LDS into transpose reads and MFMAs.
+// rows go through double-buffered LDS into transpose reads and MFMAs.  As in
+// the GEMM, no load sits under a branch (the compiler would drain the ring at
+// the next wait): a pair past the chunk or a channel past the layer reads the
+// plan's zero row, and the stage loop runs whole index groups, unrolled, with
+// only the LDS store, the barrier and the MFMAs guarded by the stage bound.
 template <typename T, int FM, int FN, int NWM, int NWN, int BKP, int DEPTH>
 __global__ void __launch_bounds__(64 * NWM * NWN)
     wgrad_tr(const T* __restrict__ X, const T* __restrict__ dY, const uint32_t* __restrict__ pair_i,
              const uint32_t* __restrict__ pair_j, const PlanHeader* __restrict__ hdr, float* __restrict__ partial,
              int Ci, int Co, int64_t chunk_len, int max_chunks, int ntiles_m, int ntiles_n,
-             const uint32_t* __restrict__ pseg, int pblk, int rows_bpc) {
+             const uint32_t* __restrict__ pseg, int pblk, int rows_bpc, const T* __restrict__ zrow) {
   using C = WgradTrCfg<T, FM, FN, NWM, NWN, BKP>;
   using E = Elt<T>;
   using frag_t = typename E::frag_t;
   constexpr int NT = C::kThreads, BM = C::kBM, BN = C::kBN, SG = C::kSG, GP = C::kGP;
-  static_assert(DEPTH >= 1 && DEPTH < C::kSG, "prefetch depth must stay inside one index group");
+  static_assert(DEPTH >= 1 && DEPTH < C::kSG && C::kSG % DEPTH == 0,
+                "prefetch depth must stay inside one index group and divide it");
 
   int k, chunk, mn;
   int64_t pbeg, pend;
@@ -795,34 +800,32 @@ __global__ void __launch_bounds__(64 * NWM * NWN)
     }
   };
 
-  uint4 ra[DEPTH][C::kIA], rb[DEPTH][C::kIB];
-  auto load_stage = [&](int s, uint4 (&da)[C::kIA], uint4 (&db)[C::kIB]) {
+  u32x4 ra[DEPTH][C::kIA], rb[DEPTH][C::kIB];
+  const int64_t zoff_x = reinterpret_cast<const char*>(zrow) - reinterpret_cast<const char*>(X);
+  const int64_t zoff_y = reinterpret_cast<const char*>(zrow) - reinterpret_cast<const char*>(dY);
+  auto load_stage = [&](int s, u32x4 (&da)[C::kIA], u32x4 (&db)[C::kIB]) {
     const uint32_t(*pi)[2] = pidx[(s / SG) & 1];
     const int r0 = (s % SG) * BKP;
 #pragma unroll
     for (int v = 0; v < C::kIA; ++v) {
-      const int idx = tid + v * NT;
+      const int idx0 = tid + v * NT;
+      const int idx = idx0 < C::kItemsA ? idx0 : 0;  // surplus threads reload item 0 and store nothing
       const int r = idx / (BM / 8), cv = idx % (BM / 8);
-      uint4 val = make_uint4(0, 0, 0, 0);
-      if (idx < C::kItemsA) {
-        const uint32_t j = pi[r0 + r][1];
-        if (j != kSentinel && m0 + cv * 8 < Ci) val = *reinterpret_cast<const uint4*>(X + int64_t(j) * Ci + m0 + cv * 8);
-      }
-      da[v] = val;
+      const uint32_t j = pi[r0 + r][1];
+      const int64_t off = (j != kSentinel && m0 + cv * 8 < Ci) ? (int64_t(j) * Ci + m0 + cv * 8) * 2 : zoff_x;
+      da[v] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(X) + off);
     }
 #pragma unroll
     for (int v = 0; v < C::kIB; ++v) {
-      const int idx = tid + v * NT;
+      const int idx0 = tid + v * NT;
+      const int idx = idx0 < C::kItemsB ? idx0 : 0;
       const int r = idx / (BN / 8), cv = idx % (BN / 8);
-      uint4 val = make_uint4(0, 0, 0, 0);
-      if (idx < C::kItemsB) {
-        const uint32_t i = pi[r0 + r][0];
-        if (i != kSentinel && c0 + cv * 8 < Co) val = *reinterpret_cast<const uint4*>(dY + int64_t(i) * Co + c0 + cv * 8);
-      }
-      db[v] = val;
+      const uint32_t i = pi[r0 + r][0];
+      const int64_t off = (i != kSentinel && c0 + cv * 8 < Co) ? (int64_t(i) * Co + c0 + cv * 8) * 2 : zoff_y;
+      db[v] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(dY) + off);
     }
   };
-  auto store_stage = [&](int buf, const uint4 (&da)[C::kIA], const uint4 (&db)[C::kIB]) {
+  auto store_stage = [&](int buf, const u32x4 (&da)[C::kIA], const u32x4 (&db)[C::kIB]) {
     char* sa = lds_a + buf * C::kLdsA;
     char* sb = lds_b + buf * C::kLdsB;
 #pragma unroll
@@ -830,7 +833,7 @@ __global__ void __launch_bounds__(64 * NWM * NWN)
       const int idx = tid + v * NT;
       if (idx < C::kItemsA) {
         const int r = idx / (BM / 8), cv = idx % (BM / 8);
-        *reinterpret_cast<uint4*>(sa + (size_t(r) * C::kLdA + cv * 8) * 2) = da[v];
+        *reinterpret_cast<u32x4*>(sa + (size_t(r) * C::kLdA + cv * 8) * 2) = da[v];
       }
     }
 #pragma unroll
@@ -838,7 +841,7 @@ __global__ void __launch_bounds__(64 * NWM * NWN)
       const int idx = tid + v * NT;
       if (idx < C::kItemsB) {
         const int r = idx / (BN / 8), cv = idx % (BN / 8);
-        *reinterpret_cast<uint4*>(sb + (size_t(r) * C::kLdB + cv * 8) * 2) = db[v];
+        *reinterpret_cast<u32x4*>(sb + (size_t(r) * C::kLdB + cv * 8) * 2) = db[v];
       }
     }
   };
@@ -872,23 +875,26 @@ __global__ void __launch_bounds__(64 * NWM * NWN)
   fetch_idx(1);
   __syncthreads();
 #pragma unroll
-  for (int d = 0; d < DEPTH; ++d)
-    if (d < nstages) load_stage(d, ra[d], rb[d]);
+  for (int d = 0; d < DEPTH; ++d) load_stage(d, ra[d], rb[d]);
 
-  for (int s0 = 0; s0 < nstages; s0 += DEPTH) {
+  // whole index groups; a group's first stage always runs (the group count
+  // rounds nstages up), so the index fetch and every row load are unconditional
+  const int ngroups = (nstages + SG - 1) / SG;
+  for (int g = 0; g < ngroups; ++g) {
 #pragma unroll
-    for (int d = 0; d < DEPTH; ++d) {
-      const int s = s0 + d;
-      if (s < nstages) {
-        if (s % SG == 0) {
-          put_idx(s / SG + 1);
-          fetch_idx(s / SG + 2);
-        }
-        store_stage(s & 1, ra[d], rb[d]);
-        __syncthreads();
-        if (s + DEPTH < nstages) load_stage(s + DEPTH, ra[d], rb[d]);
-        compute(s & 1);
+    for (int t = 0; t < SG; ++t) {
+      const int s = g * SG + t;
+      const bool run = s < nstages;
+      if (t == 0) {
+        put_idx(g + 1);
+        fetch_idx(g + 2);
       }
+      if (run) {
+        store_stage(s & 1, ra[t % DEPTH], rb[t % DEPTH]);
+        __syncthreads();
+      }
+      load_stage(s + DEPTH, ra[t % DEPTH], rb[t % DEPTH]);
+      if (run) compute(s & 1);
     }
   }
 
@@ -1176,7 +1182,8 @@ static void launch_igemm(const T* A, const T* Bt, const T* bias, T* out, const u
 
 template <typename T>
 static void launch_wgrad(const T* X, const T* dY, const uint32_t* pi, const uint32_t* pj, const PlanHeader* h,
-                         const uint32_t* pseg, float* partial, int Ci, int Co, const BwdShape& b, hipStream_t s) {
+                         const uint32_t* pseg, const T* zrow, float* partial, int Ci, int Co, const BwdShape& b,
+                         hipStream_t s) {
   dim3 grid(unsigned(b.max_chunks), kV, unsigned(b.mt * b.nt));
   if constexpr (sizeof(T) == 2) {
     const dim3 grid1(b.rows_bpc > 0 ? xcd_group_grid(b.max_chunks, kV * b.mt * b.nt)
@@ -1184,7 +1191,7 @@ static void launch_wgrad(const T* X, const T* dY, const uint32_t* pi, const uint
 #define SSC_WTR(FM, FN, NWM, NWN)                                                                        \
   wgrad_tr<T, FM, FN, NWM, NWN, 32, 2><<<grid1, 64 * NWM * NWN, 0, s>>>(X, dY, pi, pj, h, partial, Ci, Co, \
                                                                        b.chunk_len, b.max_chunks, b.mt, b.nt, \
-                                                                       pseg, b.pblk, b.rows_bpc)
+                                                                       pseg, b.pblk, b.rows_bpc, zrow)
     if (b.bm == 256) SSC_WTR(2, 4, 4, 2);
     else if (b.bm == 128) SSC_WTR(2, 2, 2, 2);
     else if (b.bm == 64) SSC_WTR(1, 1, 2, 2);
@@ -1257,7 +1264,8 @@ static int run_bwd(const char* plan, const uint32_t* nmap, const int32_t* perm, 
     float* part = reinterpret_cast<float*>(ws + W.partial);
     launch_wgrad<T>(static_cast<const T*>(feats), dY, reinterpret_cast<const uint32_t*>(plan + L.pair_i),
                     reinterpret_cast<const uint32_t*>(plan + L.pair_j), h,
-                    reinterpret_cast<const uint32_t*>(plan + L.pseg), part, Ci, Co, b, s);
+                    reinterpret_cast<const uint32_t*>(plan + L.pseg), reinterpret_cast<const T*>(plan + L.zrow),
+                    part, Ci, Co, b, s);
     const int64_t cico = int64_t(Ci) * Co;
     dim3 rg(unsigned((cico + 255) / 256), kV);
     wgrad_reduce<T><<<rg, 256, 0, s>>>(part, h, static_cast<T*>(dweight), cico, b.chunk_len, b.max_chunks,
