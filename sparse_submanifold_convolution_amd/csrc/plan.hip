@@ -189,7 +189,8 @@ template <typename KeyT>
 __global__ void __launch_bounds__(256) plan_prepare(PlanHeader* h, int64_t n, int B, int X, int Y, int Z,
                                                    int key_bits, int zbits, uint64_t capacity,
                                                    uint32_t* __restrict__ nmap, Slot<KeyT>* __restrict__ table,
-                                                   uint4* __restrict__ zrow) {
+                                                   uint4* __restrict__ zrow, uint32_t* __restrict__ hzero,
+                                                   int64_t hzero_len) {
   if (blockIdx.x == 0) {
     if (threadIdx.x == 0) {
       h->magic = kPlanMagic;
@@ -211,6 +212,7 @@ __global__ void __launch_bounds__(256) plan_prepare(PlanHeader* h, int64_t n, in
   const int64_t stride = int64_t(gridDim.x) * blockDim.x;
   const int64_t t0 = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   for (int64_t i = t0; i < int64_t(kZeroRowBytes / 16); i += stride) zrow[i] = make_uint4(0, 0, 0, 0);
+  for (int64_t i = t0; i < hzero_len; i += stride) hzero[i] = 0;
   for (int64_t i = t0; i < n * kV; i += stride) nmap[i] = kSentinel;
   for (int64_t i = t0; i < int64_t(capacity); i += stride) table[i].key = empty_key<KeyT>();
 }
@@ -309,10 +311,18 @@ __device__ __forceinline__ void store_rows(uint32_t* rows, const uint32_t (&v)[k
 __global__ void __launch_bounds__(256) row_scan(const int4* __restrict__ coords, const uint32_t* __restrict__ nmap,
                                                 int64_t n, int B, int X, int Y, int Z, int axis_bits, int zbits,
                                                 uint64_t* __restrict__ sort_key, uint32_t* __restrict__ pcnt,
-                                                int64_t pblk) {
+                                                int64_t pblk, uint32_t* __restrict__ h0, uint32_t* __restrict__ h1,
+                                                int64_t nsb) {
   __shared__ uint32_t rows[256 * kV];
   __shared__ uint32_t cnt[32];
+  __shared__ uint32_t dcnt[256];
   if (threadIdx.x < 32) cnt[threadIdx.x] = 0;
+  dcnt[threadIdx.x] = 0;
+  if (h1) {
+    // the direct sort's next histogram starts at zero
+    for (int64_t e = int64_t(blockIdx.x) * 256 + threadIdx.x; e < nsb * 256; e += int64_t(gridDim.x) * 256)
+      h1[e] = 0;
+  }
   uint32_t local[kV];
 #pragma unroll
   for (int k = 0; k < kV; ++k) local[k] = 0;
@@ -341,6 +351,7 @@ __global__ void __launch_bounds__(256) row_scan(const int4* __restrict__ coords,
         key = (uint64_t(mask) << zbits) | z;
       }
       sort_key[i] = key;
+      if (h0) atomicAdd(&dcnt[uint32_t(key) & 255u], 1u);
     }
   }
 #pragma unroll
@@ -352,6 +363,12 @@ __global__ void __launch_bounds__(256) row_scan(const int4* __restrict__ coords,
   __syncthreads();
   if (threadIdx.x < kV) pcnt[int64_t(threadIdx.x) * pblk + blockIdx.x] = cnt[threadIdx.x];
   if (blockIdx.x == 0 && threadIdx.x == 0) pcnt[kV * pblk] = 0;
+  if (h0) {
+    // the direct sort's first-pass digit counts; these 256 rows lie in one sort block
+    const int64_t sb = int64_t(blockIdx.x) * kPairRows / kSortBlockKeys;
+    const uint32_t c = dcnt[threadIdx.x];
+    if (c) atomicAdd(&h0[int64_t(threadIdx.x) * nsb + sb], c);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -377,15 +394,30 @@ __global__ void __launch_bounds__(kSortThreads) radix_hist(const uint64_t* __res
 // Keys of one workgroup are taken in rounds of 256 in index order; inside a
 // round, lanes with equal digits are ranked by a 64-lane ballot match and waves
 // are ranked by their counts, so equal digits keep their input order.
+//
+// FUSE (direct sorts only): instead of a separate histogram kernel before
+// every pass, this pass counts the next pass's digits per destination block
+// in an LDS table as it places its keys (one global atomic per non-zero entry
+// at the end), and clears the histogram the pass after next will fill.  Three
+// histograms rotate: a pass reads one, fills the next, clears the third.
+template <bool FUSE>
 __global__ void __launch_bounds__(kSortThreads)
     radix_scatter(const uint64_t* __restrict__ keys_in, const uint32_t* __restrict__ vals_in,
                   uint64_t* __restrict__ keys_out, uint32_t* __restrict__ vals_out, int64_t n, int shift,
                   const uint32_t* __restrict__ offsets, int64_t nblk, int first, int last,
-                  int32_t* __restrict__ perm, uint32_t* __restrict__ smask, int zbits, int direct) {
+                  int32_t* __restrict__ perm, uint32_t* __restrict__ smask, int zbits, int direct,
+                  uint32_t* __restrict__ hnext, uint32_t* __restrict__ hclear) {
   __shared__ uint32_t base[256];
   __shared__ uint32_t wcnt[kSortThreads / 64][256];
+  __shared__ uint32_t nxt[FUSE ? kSortDirectBlocks * 256 : 1];
   const int tid = threadIdx.x;
   const int wave = tid / 64;
+  if constexpr (FUSE) {
+    for (int64_t e = tid; e < nblk * 256; e += kSortThreads) nxt[e] = 0;
+    if (hclear)
+      for (int64_t e = int64_t(blockIdx.x) * kSortThreads + tid; e < nblk * 256; e += int64_t(gridDim.x) * kSortThreads)
+        hclear[e] = 0;
+  }
   // every round's keys and values are loaded before anything else
   const int64_t blk0 = int64_t(blockIdx.x) * kSortBlockKeys;
   uint64_t kk[kSortItems];
@@ -447,6 +479,8 @@ __global__ void __launch_bounds__(kSortThreads)
     if (valid) {
       uint32_t pos = base[d] + rank;
       for (int w = 0; w < wave; ++w) pos += wcnt[w][d];
+      if (FUSE && !last)
+        atomicAdd(&nxt[((key >> (shift + 8)) & 255u) * nblk + pos / kSortBlockKeys], 1u);
       if (last) {
         perm[pos] = int32_t(val);
         smask[pos] = uint32_t(key >> zbits);
@@ -461,6 +495,13 @@ __global__ void __launch_bounds__(kSortThreads)
     for (int w = 0; w < kSortThreads / 64; ++w) add += wcnt[w][tid];
     base[tid] += add;
     __syncthreads();
+  }
+  if constexpr (FUSE) {
+    if (!last) {
+      __syncthreads();
+      for (int64_t e = tid; e < nblk * 256; e += kSortThreads)
+        if (nxt[e]) atomicAdd(&hnext[e], nxt[e]);
+    }
   }
 }
 
@@ -660,7 +701,7 @@ extern "C" int ssc_build_neighbor_map(const int32_t* coords, int64_t n, int32_t 
   if (n == 0) {
     // header only (the key fill touches the plan's own table region)
     plan_prepare<uint32_t><<<1, 256, 0, s>>>(h, 0, B, X, Y, Z, kb, zbits, L.capacity, nullptr,
-                                             reinterpret_cast<Slot<uint32_t>*>(base + L.table), zrow);
+                                             reinterpret_cast<Slot<uint32_t>*>(base + L.table), zrow, nullptr, 0);
     return hipGetLastError() == hipSuccess ? SSC_OK : SSC_ERR_HIP;
   }
 
@@ -677,41 +718,59 @@ extern "C" int ssc_build_neighbor_map(const int32_t* coords, int64_t n, int32_t 
   const int4* c4 = reinterpret_cast<const int4*>(coords);
 
   const int64_t pblk = L.pair_blocks;
+  const int64_t nblk = L.sort_blocks;
+  // few sort blocks: the scatter passes build each other's histograms (radix_scatter<true>)
+  const int direct = nblk <= kSortDirectBlocks ? 1 : 0;
+  uint32_t* h0 = direct ? hist : nullptr;
+  const int64_t h0_len = direct ? nblk * 256 : 0;
   const unsigned prep_blocks = grid1d((n * kV > int64_t(L.capacity) ? n * kV : int64_t(L.capacity)) / 4, 256);
   const unsigned prep = prep_blocks < 2048 ? prep_blocks : 2048;
   if (kb == 64) {
     Slot<uint64_t>* table = reinterpret_cast<Slot<uint64_t>*>(base + L.table);
-    plan_prepare<uint64_t><<<prep, 256, 0, s>>>(h, n, B, X, Y, Z, kb, zbits, L.capacity, nmap, table, zrow);
+    plan_prepare<uint64_t><<<prep, 256, 0, s>>>(h, n, B, X, Y, Z, kb, zbits, L.capacity, nmap, table, zrow, h0,
+                                                h0_len);
     hash_insert<uint64_t><<<grid1d(n, 256), 256, 0, s>>>(c4, n, B, X, Y, Z, table, L.capacity,
                                                          &h->status_bits);
     probe_half<uint64_t><<<grid1d(n * kCentre, 256), 256, 0, s>>>(c4, n, B, X, Y, Z, table, L.capacity,
                                                                   nmap);
   } else {
     Slot<uint32_t>* table = reinterpret_cast<Slot<uint32_t>*>(base + L.table);
-    plan_prepare<uint32_t><<<prep, 256, 0, s>>>(h, n, B, X, Y, Z, kb, zbits, L.capacity, nmap, table, zrow);
+    plan_prepare<uint32_t><<<prep, 256, 0, s>>>(h, n, B, X, Y, Z, kb, zbits, L.capacity, nmap, table, zrow, h0,
+                                                h0_len);
     hash_insert<uint32_t><<<grid1d(n, 256), 256, 0, s>>>(c4, n, B, X, Y, Z, table, L.capacity,
                                                          &h->status_bits);
     probe_half<uint32_t><<<grid1d(n * kCentre, 256), 256, 0, s>>>(c4, n, B, X, Y, Z, table, L.capacity,
                                                                   nmap);
   }
-  row_scan<<<unsigned(pblk), 256, 0, s>>>(c4, nmap, n, B, X, Y, Z, axis_bits, zbits, key0, pcnt, pblk);
+  row_scan<<<unsigned(pblk), 256, 0, s>>>(c4, nmap, n, B, X, Y, Z, axis_bits, zbits, key0, pcnt, pblk, h0,
+                                          direct ? hist + nblk * 256 : nullptr, nblk);
 
   // radix sort over the key's kV + zbits low bits
   const int bits = kV + zbits;
   const int passes = (bits + 7) / 8;
-  const int64_t nblk = L.sort_blocks;
   const uint64_t* kin = key0;
   const uint32_t* vin = val0;
   uint64_t* kout = key1;
   uint32_t* vout = val1;
-  const int direct = nblk <= kSortDirectBlocks ? 1 : 0;
   for (int p = 0; p < passes; ++p) {
     const int shift = 8 * p;
-    radix_hist<<<unsigned(nblk), kSortThreads, 0, s>>>(kin, n, shift, hist, nblk);
-    if (!direct) launch_scan(hist, nblk * 256 + 1, scan_tmp, s);
-    radix_scatter<<<unsigned(nblk), kSortThreads, 0, s>>>(kin, vin, kout, vout, n, shift, hist, nblk,
-                                                           p == 0 ? 1 : 0, p == passes - 1 ? 1 : 0, perm,
-                                                           smask, zbits, direct);
+    const int last = p == passes - 1 ? 1 : 0;
+    if (direct) {
+      // histograms rotate: row_scan filled hist[0] for pass 0; pass p reads
+      // hist[p % 3], fills hist[(p + 1) % 3] and clears hist[(p + 2) % 3]
+      uint32_t* hcur = hist + (p % 3) * nblk * 256;
+      uint32_t* hnext = hist + ((p + 1) % 3) * nblk * 256;
+      uint32_t* hclr = hist + ((p + 2) % 3) * nblk * 256;
+      radix_scatter<true><<<unsigned(nblk), kSortThreads, 0, s>>>(kin, vin, kout, vout, n, shift, hcur, nblk,
+                                                                  p == 0 ? 1 : 0, last, perm, smask, zbits, 1,
+                                                                  hnext, last ? nullptr : hclr);
+    } else {
+      radix_hist<<<unsigned(nblk), kSortThreads, 0, s>>>(kin, n, shift, hist, nblk);
+      launch_scan(hist, nblk * 256 + 1, scan_tmp, s);
+      radix_scatter<false><<<unsigned(nblk), kSortThreads, 0, s>>>(kin, vin, kout, vout, n, shift, hist, nblk,
+                                                                   p == 0 ? 1 : 0, last, perm, smask, zbits, 0,
+                                                                   nullptr, nullptr);
+    }
     const uint64_t* tk = kout;
     const uint32_t* tv = vout;
     kout = const_cast<uint64_t*>(kin);

@@ -28,6 +28,7 @@ constexpr int kSortBlockKeys = kSortThreads * kSortItems;
 constexpr int kSortDirectBlocks = 64;
 // pair-list build: rows per workgroup
 constexpr int kPairRows = 256;
+static_assert(kSortBlockKeys % kPairRows == 0, "a row_scan block must lie in one sort block");
 // up to this many pair-list blocks, pair_scatter sums the block counts itself
 constexpr int kPairDirectBlocks = 256;
 // bytes of the plan's all-zero row: the GEMM loads it in place of a missing
@@ -116,7 +117,13 @@ inline PlanLayout plan_layout(int64_t n, int key_bits) {
   L.key1 = take(size_t(n) * 8);
   L.val0 = take(size_t(n) * 4);
   L.val1 = take(size_t(n) * 4);
-  L.hist = take((size_t(L.sort_blocks) * 256 + 1) * 4);
+  {
+    // multi-block sort: one [256][blocks] histogram (+1 for the scan total);
+    // direct sort (few blocks): three rotating ones, see the plan builder
+    const size_t one = size_t(L.sort_blocks) * 256;
+    const size_t need = L.sort_blocks <= kSortDirectBlocks ? 3 * one : one + 1;
+    L.hist = take((need > one + 1 ? need : one + 1) * 4);
+  }
   L.pcnt = take((size_t(L.pair_blocks) * kV + 1) * 4);
   size_t scan_len = size_t(L.sort_blocks) * 256 + 1;
   if (size_t(L.pair_blocks) * kV + 1 > scan_len) scan_len = size_t(L.pair_blocks) * kV + 1;
