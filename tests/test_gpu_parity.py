@@ -271,8 +271,12 @@ def test_config5_sampled(ssc):
     _sampled_parity(ssc, 5)
 
 
-def test_graph_replay_matches_eager(ssc):
-    """A captured step (build + fwd + bwd) replayed several times, with eager work in between, matches eager runs."""
+@pytest.mark.parametrize("two_streams", [False, True], ids=["one_stream", "two_streams"])
+def test_graph_replay_matches_eager(ssc, two_streams):
+    """A captured step (build + fwd + bwd) replayed several times, with eager work in between, matches eager runs.
+
+    two_streams: the input gradient and the weight/bias gradients are captured on two streams (as the
+    benchmark does), sharing one workspace."""
     w = WL.random_workload(41, 2, (14, 13, 12), 0.3, 64, 64, "f16", random_bias=True)
     print(f"[case] graph replay n={w.n}", flush=True)
     dev = DEV
@@ -295,8 +299,17 @@ def test_graph_replay_matches_eager(ssc):
                                      ssc.binding._ptr(plan.perm), ssc.binding._ptr(plan.buf), nbytes, st)
         assert r == 0
         ssc.subm_conv3d_fwd(plan, X, W, b, out=out, ws=ws)
-        ssc.subm_conv3d_bwd(plan, X, W, dY, ws=ws, outs=(dX, dW, db))
+        if two_streams:
+            cur = torch.cuda.current_stream(dev)
+            grad_side.wait_stream(cur)
+            ssc.subm_conv3d_bwd(plan, X, W, dY, ws=ws, outs=(dX, None, None))
+            with torch.cuda.stream(grad_side):
+                ssc.subm_conv3d_bwd(plan, X, W, dY, ws=ws, outs=(None, dW, db))
+            cur.wait_stream(grad_side)
+        else:
+            ssc.subm_conv3d_bwd(plan, X, W, dY, ws=ws, outs=(dX, dW, db))
 
+    grad_side = torch.cuda.Stream(dev)
     side = torch.cuda.Stream(dev)
     side.wait_stream(torch.cuda.current_stream(dev))
     with torch.cuda.stream(side):
