@@ -312,7 +312,7 @@ __global__ void __launch_bounds__(256) row_scan(const int4* __restrict__ coords,
                                                 int64_t n, int B, int X, int Y, int Z, int axis_bits, int zbits,
                                                 uint64_t* __restrict__ sort_key, uint32_t* __restrict__ pcnt,
                                                 int64_t pblk, uint32_t* __restrict__ h0, uint32_t* __restrict__ h1,
-                                                int64_t nsb) {
+                                                int64_t nsb, int sort_block_keys) {
   __shared__ uint32_t rows[256 * kV];
   __shared__ uint32_t cnt[32];
   __shared__ uint32_t dcnt[256];
@@ -365,7 +365,7 @@ __global__ void __launch_bounds__(256) row_scan(const int4* __restrict__ coords,
   if (blockIdx.x == 0 && threadIdx.x == 0) pcnt[kV * pblk] = 0;
   if (h0) {
     // the direct sort's first-pass digit counts; these 256 rows lie in one sort block
-    const int64_t sb = int64_t(blockIdx.x) * kPairRows / kSortBlockKeys;
+    const int64_t sb = int64_t(blockIdx.x) * kPairRows / sort_block_keys;
     const uint32_t c = dcnt[threadIdx.x];
     if (c) atomicAdd(&h0[int64_t(threadIdx.x) * nsb + sb], c);
   }
@@ -375,14 +375,15 @@ __global__ void __launch_bounds__(256) row_scan(const int4* __restrict__ coords,
 // stable LSD radix sort of 64-bit keys with a 32-bit payload
 // ---------------------------------------------------------------------------
 
+template <int ITEMS>
 __global__ void __launch_bounds__(kSortThreads) radix_hist(const uint64_t* __restrict__ keys, int64_t n,
                                                            int shift, uint32_t* __restrict__ hist,
                                                            int64_t nblk) {
   __shared__ uint32_t cnt[256];
   cnt[threadIdx.x] = 0;
   __syncthreads();
-  const int64_t base = int64_t(blockIdx.x) * kSortBlockKeys;
-  for (int q = 0; q < kSortItems; ++q) {
+  const int64_t base = int64_t(blockIdx.x) * kSortThreads * ITEMS;
+  for (int q = 0; q < ITEMS; ++q) {
     const int64_t idx = base + int64_t(q) * kSortThreads + threadIdx.x;
     if (idx < n) atomicAdd(&cnt[(keys[idx] >> shift) & 255u], 1u);
   }
@@ -400,7 +401,7 @@ __global__ void __launch_bounds__(kSortThreads) radix_hist(const uint64_t* __res
 // in an LDS table as it places its keys (one global atomic per non-zero entry
 // at the end), and clears the histogram the pass after next will fill.  Three
 // histograms rotate: a pass reads one, fills the next, clears the third.
-template <bool FUSE>
+template <bool FUSE, int ITEMS>
 __global__ void __launch_bounds__(kSortThreads)
     radix_scatter(const uint64_t* __restrict__ keys_in, const uint32_t* __restrict__ vals_in,
                   uint64_t* __restrict__ keys_out, uint32_t* __restrict__ vals_out, int64_t n, int shift,
@@ -419,11 +420,12 @@ __global__ void __launch_bounds__(kSortThreads)
         hclear[e] = 0;
   }
   // every round's keys and values are loaded before anything else
-  const int64_t blk0 = int64_t(blockIdx.x) * kSortBlockKeys;
-  uint64_t kk[kSortItems];
-  uint32_t vv[kSortItems];
+  constexpr int kBlockKeys = kSortThreads * ITEMS;
+  const int64_t blk0 = int64_t(blockIdx.x) * kBlockKeys;
+  uint64_t kk[ITEMS];
+  uint32_t vv[ITEMS];
 #pragma unroll
-  for (int q = 0; q < kSortItems; ++q) {
+  for (int q = 0; q < ITEMS; ++q) {
     const int64_t idx = blk0 + int64_t(q) * kSortThreads + tid;
     const bool valid = idx < n;
     kk[q] = valid ? keys_in[idx] : 0ull;
@@ -457,7 +459,7 @@ __global__ void __launch_bounds__(kSortThreads)
     base[tid] = offsets[int64_t(tid) * nblk + blockIdx.x];
   }
 #pragma unroll
-  for (int q = 0; q < kSortItems; ++q) {
+  for (int q = 0; q < ITEMS; ++q) {
     const int64_t idx = blk0 + int64_t(q) * kSortThreads + tid;
     const bool valid = idx < n;
     const uint64_t key = kk[q];
@@ -480,7 +482,7 @@ __global__ void __launch_bounds__(kSortThreads)
       uint32_t pos = base[d] + rank;
       for (int w = 0; w < wave; ++w) pos += wcnt[w][d];
       if (FUSE && !last)
-        atomicAdd(&nxt[((key >> (shift + 8)) & 255u) * nblk + pos / kSortBlockKeys], 1u);
+        atomicAdd(&nxt[((key >> (shift + 8)) & 255u) * nblk + pos / kBlockKeys], 1u);
       if (last) {
         perm[pos] = int32_t(val);
         smask[pos] = uint32_t(key >> zbits);
@@ -743,7 +745,7 @@ extern "C" int ssc_build_neighbor_map(const int32_t* coords, int64_t n, int32_t 
                                                                   nmap);
   }
   row_scan<<<unsigned(pblk), 256, 0, s>>>(c4, nmap, n, B, X, Y, Z, axis_bits, zbits, key0, pcnt, pblk, h0,
-                                          direct ? hist + nblk * 256 : nullptr, nblk);
+                                          direct ? hist + nblk * 256 : nullptr, nblk, kSortThreads * L.sort_items);
 
   // radix sort over the key's kV + zbits low bits
   const int bits = kV + zbits;
@@ -761,15 +763,20 @@ extern "C" int ssc_build_neighbor_map(const int32_t* coords, int64_t n, int32_t 
       uint32_t* hcur = hist + (p % 3) * nblk * 256;
       uint32_t* hnext = hist + ((p + 1) % 3) * nblk * 256;
       uint32_t* hclr = hist + ((p + 2) % 3) * nblk * 256;
-      radix_scatter<true><<<unsigned(nblk), kSortThreads, 0, s>>>(kin, vin, kout, vout, n, shift, hcur, nblk,
-                                                                  p == 0 ? 1 : 0, last, perm, smask, zbits, 1,
-                                                                  hnext, last ? nullptr : hclr);
+      if (L.sort_items == kSortItemsSmall)
+        radix_scatter<true, kSortItemsSmall><<<unsigned(nblk), kSortThreads, 0, s>>>(
+            kin, vin, kout, vout, n, shift, hcur, nblk, p == 0 ? 1 : 0, last, perm, smask, zbits, 1, hnext,
+            last ? nullptr : hclr);
+      else
+        radix_scatter<true, kSortItems><<<unsigned(nblk), kSortThreads, 0, s>>>(
+            kin, vin, kout, vout, n, shift, hcur, nblk, p == 0 ? 1 : 0, last, perm, smask, zbits, 1, hnext,
+            last ? nullptr : hclr);
     } else {
-      radix_hist<<<unsigned(nblk), kSortThreads, 0, s>>>(kin, n, shift, hist, nblk);
+      radix_hist<kSortItems><<<unsigned(nblk), kSortThreads, 0, s>>>(kin, n, shift, hist, nblk);
       launch_scan(hist, nblk * 256 + 1, scan_tmp, s);
-      radix_scatter<false><<<unsigned(nblk), kSortThreads, 0, s>>>(kin, vin, kout, vout, n, shift, hist, nblk,
-                                                                   p == 0 ? 1 : 0, last, perm, smask, zbits, 0,
-                                                                   nullptr, nullptr);
+      radix_scatter<false, kSortItems><<<unsigned(nblk), kSortThreads, 0, s>>>(
+          kin, vin, kout, vout, n, shift, hist, nblk, p == 0 ? 1 : 0, last, perm, smask, zbits, 0, nullptr,
+          nullptr);
     }
     const uint64_t* tk = kout;
     const uint32_t* tv = vout;

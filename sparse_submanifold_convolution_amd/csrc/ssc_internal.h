@@ -22,13 +22,16 @@ constexpr uint32_t kBitHashFull = 4u;
 
 // radix sort: keys per workgroup of the histogram / scatter kernels
 constexpr int kSortThreads = 256;
-constexpr int kSortItems = 8;
-constexpr int kSortBlockKeys = kSortThreads * kSortItems;
+constexpr int kSortItems = 8;       // keys per thread of a large sort
+constexpr int kSortItemsSmall = 4;  // of a small one: more, shorter blocks (fewer sequential rounds)
 // up to this many sort blocks, radix_scatter reads the histograms directly
 constexpr int kSortDirectBlocks = 64;
+// sorts of at most kSortSmallKeys keys use kSortItemsSmall (and so the direct path)
+constexpr int64_t kSortSmallKeys = int64_t(kSortDirectBlocks) * kSortThreads * kSortItemsSmall;
+inline int sort_items_for(int64_t n) { return n <= kSortSmallKeys ? kSortItemsSmall : kSortItems; }
 // pair-list build: rows per workgroup
 constexpr int kPairRows = 256;
-static_assert(kSortBlockKeys % kPairRows == 0, "a row_scan block must lie in one sort block");
+static_assert((kSortThreads * kSortItemsSmall) % kPairRows == 0, "a row_scan block must lie in one sort block");
 // up to this many pair-list blocks, pair_scatter sums the block counts itself
 constexpr int kPairDirectBlocks = 256;
 // bytes of the plan's all-zero row: the GEMM loads it in place of a missing
@@ -77,6 +80,7 @@ struct PlanLayout {
   uint64_t capacity = 0;
   int key_bytes = 4;
   int64_t sort_blocks = 0;
+  int sort_items = kSortItems;  // keys per thread of the radix sort
   int64_t pair_blocks = 0;
 };
 
@@ -110,7 +114,8 @@ inline PlanLayout plan_layout(int64_t n, int key_bits) {
   uint64_t want = uint64_t(n) * 2 < 1024 ? 1024 : uint64_t(n) * 2;
   L.capacity = uint64_t(1) << ceil_log2_u64(want);
   L.key_bytes = key_bits == 64 ? 8 : 4;
-  L.sort_blocks = (n + kSortBlockKeys - 1) / kSortBlockKeys;
+  L.sort_items = sort_items_for(n);
+  L.sort_blocks = (n + kSortThreads * L.sort_items - 1) / (kSortThreads * L.sort_items);
   L.pair_blocks = (n + kPairRows - 1) / kPairRows;
   L.table = take(L.capacity * (L.key_bytes == 8 ? 16 : 8));
   L.key0 = take(size_t(n) * 8);
