@@ -392,6 +392,25 @@ __global__ void __launch_bounds__(kSortThreads) radix_hist(const uint64_t* __res
   if (blockIdx.x == 0 && threadIdx.x == 0) hist[256 * nblk] = 0;
 }
 
+__device__ __forceinline__ void pair_scatter_block(int64_t blk, const uint32_t* __restrict__ nmap, int64_t n,
+                                                   const uint32_t* __restrict__ pcnt, int64_t pblk,
+                                                   uint32_t* __restrict__ pair_i, uint32_t* __restrict__ pair_j,
+                                                   int direct, PlanHeader* __restrict__ h,
+                                                   uint32_t* __restrict__ pseg);
+
+// The pair-list scatter (pair_scatter_block) of a small input rides along with
+// the first sort pass: it reads only nmap and row_scan's counts, so the
+// workgroups past the sort blocks do it and one launch is saved.
+struct PairJob {
+  const uint32_t* nmap;
+  const uint32_t* pcnt;
+  int64_t pblk;  // 0: no pair blocks in this launch
+  uint32_t* pair_i;
+  uint32_t* pair_j;
+  PlanHeader* h;
+  uint32_t* pseg;
+};
+
 // Keys of one workgroup are taken in rounds of 256 in index order; inside a
 // round, lanes with equal digits are ranked by a 64-lane ballot match and waves
 // are ranked by their counts, so equal digits keep their input order.
@@ -407,7 +426,14 @@ __global__ void __launch_bounds__(kSortThreads)
                   uint64_t* __restrict__ keys_out, uint32_t* __restrict__ vals_out, int64_t n, int shift,
                   const uint32_t* __restrict__ offsets, int64_t nblk, int first, int last,
                   int32_t* __restrict__ perm, uint32_t* __restrict__ smask, int zbits, int direct,
-                  uint32_t* __restrict__ hnext, uint32_t* __restrict__ hclear) {
+                  uint32_t* __restrict__ hnext, uint32_t* __restrict__ hclear, PairJob pj) {
+  if constexpr (FUSE) {
+    if (int64_t(blockIdx.x) >= nblk) {
+      pair_scatter_block(int64_t(blockIdx.x) - nblk, pj.nmap, n, pj.pcnt, pj.pblk, pj.pair_i, pj.pair_j, 1, pj.h,
+                         pj.pseg);
+      return;
+    }
+  }
   __shared__ uint32_t base[256];
   __shared__ uint32_t wcnt[kSortThreads / 64][256];
   __shared__ uint32_t nxt[FUSE ? kSortDirectBlocks * 256 : 1];
@@ -531,11 +557,11 @@ __global__ void pair_offsets(const uint32_t* __restrict__ pcnt, int64_t pblk, Pl
 
 // pcnt holds scanned offsets (direct = 0) or raw per-block counts (direct = 1:
 // few blocks, each block sums the counts itself and block 0 fills the header).
-__global__ void __launch_bounds__(256) pair_scatter(const uint32_t* __restrict__ nmap, int64_t n,
-                                                    const uint32_t* __restrict__ pcnt, int64_t pblk,
-                                                    uint32_t* __restrict__ pair_i,
-                                                    uint32_t* __restrict__ pair_j, int direct,
-                                                    PlanHeader* __restrict__ h, uint32_t* __restrict__ pseg) {
+__device__ __forceinline__ void pair_scatter_block(int64_t blk, const uint32_t* __restrict__ nmap, int64_t n,
+                                                   const uint32_t* __restrict__ pcnt, int64_t pblk,
+                                                   uint32_t* __restrict__ pair_i, uint32_t* __restrict__ pair_j,
+                                                   int direct, PlanHeader* __restrict__ h,
+                                                   uint32_t* __restrict__ pseg) {
   __shared__ uint32_t base[32];
   __shared__ uint32_t tot[32];
   __shared__ uint32_t wc[kV][4];
@@ -543,7 +569,7 @@ __global__ void __launch_bounds__(256) pair_scatter(const uint32_t* __restrict__
   const int tid = threadIdx.x;
   const int wave = tid / 64;
   static_assert(kPairRows == 256, "one row per thread");
-  const int64_t rbase = int64_t(blockIdx.x) * kPairRows;
+  const int64_t rbase = blk * kPairRows;
   const int64_t here = (n - rbase) < 256 ? (n - rbase) : 256;
   {
     // the rows' loads go out first; the offsets below overlap them
@@ -565,13 +591,13 @@ __global__ void __launch_bounds__(256) pair_scatter(const uint32_t* __restrict__
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           t += c[u];
-          if (b + 8 * u < int64_t(blockIdx.x)) before += c[u];
+          if (b + 8 * u < blk) before += c[u];
         }
       }
       for (; b < pblk; b += 8) {
         const uint32_t c = pcnt[int64_t(k) * pblk + b];
         t += c;
-        if (b < int64_t(blockIdx.x)) before += c;
+        if (b < blk) before += c;
       }
       part_t[k][ph] = t;
       part_b[k][ph] = before;
@@ -591,18 +617,18 @@ __global__ void __launch_bounds__(256) pair_scatter(const uint32_t* __restrict__
       uint32_t off = 0;
       for (int k = 0; k < tid; ++k) off += tot[k];
       base[tid] += off;
-      if (blockIdx.x == 0) {
+      if (blk == 0) {
         h->pair_off[tid] = off;
         h->pair_count[tid] = tot[tid];
         if (tid == kV - 1) h->pair_off[kV] = off + tot[tid];
       }
     }
   } else if (tid < kV) {
-    base[tid] = pcnt[int64_t(tid) * pblk + blockIdx.x];
+    base[tid] = pcnt[int64_t(tid) * pblk + blk];
   }
   __syncthreads();
   // where this block's rows start in each list (the weight gradient chunks by rows)
-  if (tid < kV) pseg[int64_t(tid) * (pblk + 1) + blockIdx.x] = base[tid];
+  if (tid < kV) pseg[int64_t(tid) * (pblk + 1) + blk] = base[tid];
   {
     const int64_t row = rbase + tid;
     const bool in = row < n;
@@ -629,7 +655,15 @@ __global__ void __launch_bounds__(256) pair_scatter(const uint32_t* __restrict__
     if (tid < kV) base[tid] += wc[tid][0] + wc[tid][1] + wc[tid][2] + wc[tid][3];
     __syncthreads();
   }
-  if (blockIdx.x == pblk - 1 && tid < kV) pseg[int64_t(tid) * (pblk + 1) + pblk] = base[tid];
+  if (blk == pblk - 1 && tid < kV) pseg[int64_t(tid) * (pblk + 1) + pblk] = base[tid];
+}
+
+__global__ void __launch_bounds__(256) pair_scatter(const uint32_t* __restrict__ nmap, int64_t n,
+                                                    const uint32_t* __restrict__ pcnt, int64_t pblk,
+                                                    uint32_t* __restrict__ pair_i,
+                                                    uint32_t* __restrict__ pair_j, int direct,
+                                                    PlanHeader* __restrict__ h, uint32_t* __restrict__ pseg) {
+  pair_scatter_block(blockIdx.x, nmap, n, pcnt, pblk, pair_i, pair_j, direct, h, pseg);
 }
 
 // ---------------------------------------------------------------------------
@@ -754,9 +788,16 @@ extern "C" int ssc_build_neighbor_map(const int32_t* coords, int64_t n, int32_t 
   const uint32_t* vin = val0;
   uint64_t* kout = key1;
   uint32_t* vout = val1;
+  const int pdirect = pblk <= kPairDirectBlocks ? 1 : 0;
+  // small inputs: the pair lists are built by extra workgroups of the first pass
+  const bool pairs_ride = direct && pdirect;
+  const PairJob no_pairs{nullptr, nullptr, 0, nullptr, nullptr, nullptr, nullptr};
+  const PairJob pair_job{nmap, pcnt, pblk, pair_i, pair_j, h, reinterpret_cast<uint32_t*>(base + L.pseg)};
   for (int p = 0; p < passes; ++p) {
     const int shift = 8 * p;
     const int last = p == passes - 1 ? 1 : 0;
+    const PairJob pj = (pairs_ride && p == 0) ? pair_job : no_pairs;
+    const unsigned grid = unsigned(nblk + pj.pblk);
     if (direct) {
       // histograms rotate: row_scan filled hist[0] for pass 0; pass p reads
       // hist[p % 3], fills hist[(p + 1) % 3] and clears hist[(p + 2) % 3]
@@ -764,19 +805,19 @@ extern "C" int ssc_build_neighbor_map(const int32_t* coords, int64_t n, int32_t 
       uint32_t* hnext = hist + ((p + 1) % 3) * nblk * 256;
       uint32_t* hclr = hist + ((p + 2) % 3) * nblk * 256;
       if (L.sort_items == kSortItemsSmall)
-        radix_scatter<true, kSortItemsSmall><<<unsigned(nblk), kSortThreads, 0, s>>>(
+        radix_scatter<true, kSortItemsSmall><<<grid, kSortThreads, 0, s>>>(
             kin, vin, kout, vout, n, shift, hcur, nblk, p == 0 ? 1 : 0, last, perm, smask, zbits, 1, hnext,
-            last ? nullptr : hclr);
+            last ? nullptr : hclr, pj);
       else
-        radix_scatter<true, kSortItems><<<unsigned(nblk), kSortThreads, 0, s>>>(
+        radix_scatter<true, kSortItems><<<grid, kSortThreads, 0, s>>>(
             kin, vin, kout, vout, n, shift, hcur, nblk, p == 0 ? 1 : 0, last, perm, smask, zbits, 1, hnext,
-            last ? nullptr : hclr);
+            last ? nullptr : hclr, pj);
     } else {
       radix_hist<kSortItems><<<unsigned(nblk), kSortThreads, 0, s>>>(kin, n, shift, hist, nblk);
       launch_scan(hist, nblk * 256 + 1, scan_tmp, s);
       radix_scatter<false, kSortItems><<<unsigned(nblk), kSortThreads, 0, s>>>(
           kin, vin, kout, vout, n, shift, hist, nblk, p == 0 ? 1 : 0, last, perm, smask, zbits, 0, nullptr,
-          nullptr);
+          nullptr, no_pairs);
     }
     const uint64_t* tk = kout;
     const uint32_t* tv = vout;
@@ -788,13 +829,13 @@ extern "C" int ssc_build_neighbor_map(const int32_t* coords, int64_t n, int32_t 
 
   permute_rows<<<grid1d(n * kV, 256), 256, 0, s>>>(nmap, perm, n, reinterpret_cast<uint32_t*>(base + L.snmap));
 
-  // per-offset pair lists
-  const int pdirect = pblk <= kPairDirectBlocks ? 1 : 0;
+  // per-offset pair lists (already built by the first pass for small inputs)
   if (!pdirect) {
     launch_scan(pcnt, pblk * kV + 1, scan_tmp, s);
     pair_offsets<<<1, 64, 0, s>>>(pcnt, pblk, h);
   }
-  pair_scatter<<<unsigned(pblk), 256, 0, s>>>(nmap, n, pcnt, pblk, pair_i, pair_j, pdirect, h,
+  if (!pairs_ride)
+    pair_scatter<<<unsigned(pblk), 256, 0, s>>>(nmap, n, pcnt, pblk, pair_i, pair_j, pdirect, h,
                                               reinterpret_cast<uint32_t*>(base + L.pseg));
 
   return hipGetLastError() == hipSuccess ? SSC_OK : SSC_ERR_HIP;
