@@ -706,6 +706,107 @@ __device__ __forceinline__ s16x4 lds_tr16(const void* p) {
       (__attribute__((address_space(3))) s16x4*)(const_cast<void*>(p)));
 }
 
+// dbias stage 1: work item (x, y) sums rows [x*rows, (x+1)*rows) of the column
+// vectors [y*cvb, (y+1)*cvb) (16 bytes each) with NT threads.  Thread t takes
+// vector t % cvb and every (NT/cvb)-th row from phase t / cvb, four loads in
+// flight, adding in increasing row order; the phases are then added in order.
+// `red` is NT * (16 / sizeof(T)) floats of LDS.
+template <typename T, int NT>
+__device__ __forceinline__ void colsum_partial_block(int bx, int by, const T* __restrict__ dY, int64_t n, int Co,
+                                                     int64_t rows, int cvb, float* __restrict__ part, float* red) {
+  constexpr int VEC = 16 / int(sizeof(T));
+  const int cv = threadIdx.x % cvb, ph = threadIdx.x / cvb, nph = NT / cvb;
+  const int col = (by * cvb + cv) * VEC;
+  const int64_t r0 = int64_t(bx) * rows;
+  const int64_t r1 = (r0 + rows < n) ? r0 + rows : n;
+  float acc[VEC];
+#pragma unroll
+  for (int q = 0; q < VEC; ++q) acc[q] = 0.f;
+  auto add = [&](const u32x4& v) {
+    const T* e = reinterpret_cast<const T*>(&v);
+#pragma unroll
+    for (int q = 0; q < VEC; ++q) acc[q] += Elt<T>::load(e[q]);
+  };
+  if (col < Co && ph < nph) {
+    const T* base = dY + col;
+    int64_t r = r0 + ph;
+    for (; r + 3 * nph < r1; r += 4 * nph) {
+      u32x4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const u32x4*>(base + (r + u * nph) * Co);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) add(v[u]);
+    }
+    for (; r < r1; r += nph) add(*reinterpret_cast<const u32x4*>(base + r * Co));
+  }
+  if (ph < nph) {
+#pragma unroll
+    for (int q = 0; q < VEC; ++q) red[(ph * cvb + cv) * VEC + q] = acc[q];
+  }
+  __syncthreads();
+  for (int t = threadIdx.x; t < cvb * VEC; t += NT) {
+    const int c = by * cvb * VEC + t;
+    if (c >= Co) break;
+    float sum = 0.f;
+    for (int q = 0; q < nph; ++q) sum += red[q * cvb * VEC + t];
+    part[int64_t(bx) * Co + c] = sum;
+  }
+}
+
+template <typename T>
+__global__ void __launch_bounds__(256) colsum_partial(const T* __restrict__ dY, int64_t n, int Co,
+                                                      int64_t rows, int cvb, float* __restrict__ part) {
+  __shared__ float red[256 * (16 / int(sizeof(T)))];
+  colsum_partial_block<T, 256>(blockIdx.x, blockIdx.y, dY, n, Co, rows, cvb, part, red);
+}
+
+// dbias stage 2: 16 columns per work item, 16 phases each adding every 16th
+// partial (four loads in flight), then the phases in a fixed order.  256 threads.
+template <typename T>
+__device__ __forceinline__ void colsum_final_block(int bx, const float* __restrict__ part, int nb, int Co,
+                                                   T* __restrict__ dbias) {
+  __shared__ float red[16][16];
+  const int cl = threadIdx.x & 15, ph = threadIdx.x >> 4;
+  const int c = bx * 16 + cl;
+  float s = 0.f;
+  if (c < Co) {
+    int b = ph;
+    for (; b + 48 < nb; b += 64) {
+      float v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = part[int64_t(b + 16 * u) * Co + c];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) s += v[u];
+    }
+    for (; b < nb; b += 16) s += part[int64_t(b) * Co + c];
+  }
+  red[ph][cl] = s;
+  __syncthreads();
+  if (ph == 0 && c < Co) {
+    float t = 0.f;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) t += red[q][cl];
+    dbias[c] = Elt<T>::store(t);
+  }
+}
+
+template <typename T>
+__global__ void __launch_bounds__(256) colsum_final(const float* __restrict__ part, int nb, int Co,
+                                                    T* __restrict__ dbias) {
+  colsum_final_block<T>(blockIdx.x, part, nb, Co, dbias);
+}
+
+// dbias stage 1 riding on a weight-gradient launch: workgroups past the
+// weight-gradient grid each sum one (row block, column group) of dY.
+template <typename T>
+struct BiasJob {
+  const T* dY;
+  int64_t n, rows;
+  int Co, cvb, nbx;  // nbx row blocks per column group
+  unsigned first;    // first workgroup index of the job; no job when past the grid
+  float* part;
+};
+
 // Pipeline: pair indices for group g+1 are written to LDS at the first stage
 // of group g (fetched one group earlier into registers); row gathers for stage
 // s+DEPTH are issued during stage s from indices already in LDS; the stage's
@@ -719,13 +820,26 @@ __global__ void __launch_bounds__(64 * NWM * NWN)
     wgrad_tr(const T* __restrict__ X, const T* __restrict__ dY, const uint32_t* __restrict__ pair_i,
              const uint32_t* __restrict__ pair_j, const PlanHeader* __restrict__ hdr, float* __restrict__ partial,
              int Ci, int Co, int64_t chunk_len, int max_chunks, int ntiles_m, int ntiles_n,
-             const uint32_t* __restrict__ pseg, int pblk, int rows_bpc, const T* __restrict__ zrow) {
+             const uint32_t* __restrict__ pseg, int pblk, int rows_bpc, const T* __restrict__ zrow,
+             BiasJob<T> bj) {
   using C = WgradTrCfg<T, FM, FN, NWM, NWN, BKP>;
   using E = Elt<T>;
   using frag_t = typename E::frag_t;
   constexpr int NT = C::kThreads, BM = C::kBM, BN = C::kBN, SG = C::kSG, GP = C::kGP;
   static_assert(DEPTH >= 1 && DEPTH < C::kSG && C::kSG % DEPTH == 0,
                 "prefetch depth must stay inside one index group and divide it");
+
+  __shared__ __align__(16) char lds_a[2 * C::kLdsA];
+  __shared__ __align__(16) char lds_b[2 * C::kLdsB];
+  __shared__ uint32_t pidx[2][GP][2];  // (i, j) per pair; sentinel past the chunk
+
+  if (blockIdx.x >= bj.first) {
+    static_assert(NT * (16 / sizeof(T)) * sizeof(float) <= sizeof(lds_a), "column-sum scratch too small");
+    const int j = int(blockIdx.x - bj.first);
+    colsum_partial_block<T, NT>(j % bj.nbx, j / bj.nbx, bj.dY, bj.n, bj.Co, bj.rows, bj.cvb, bj.part,
+                                reinterpret_cast<float*>(lds_a));
+    return;
+  }
 
   int k, chunk, mn;
   int64_t pbeg, pend;
@@ -760,10 +874,6 @@ __global__ void __launch_bounds__(64 * NWM * NWN)
   }
   const int m0 = (mn / ntiles_n) * BM;
   const int c0 = (mn % ntiles_n) * BN;
-
-  __shared__ __align__(16) char lds_a[2 * C::kLdsA];
-  __shared__ __align__(16) char lds_b[2 * C::kLdsB];
-  __shared__ uint32_t pidx[2][GP][2];  // (i, j) per pair; sentinel past the chunk
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -919,8 +1029,14 @@ __global__ void __launch_bounds__(64 * NWM * NWN)
 template <typename T>
 __global__ void __launch_bounds__(256) wgrad_reduce(const float* __restrict__ partial,
                                                     const PlanHeader* __restrict__ hdr, T* __restrict__ dW,
-                                                    int64_t cico, int64_t chunk_len, int max_chunks, int rowmode) {
+                                                    int64_t cico, int64_t chunk_len, int max_chunks, int rowmode,
+                                                    const float* __restrict__ bias_part, int bias_nb, int Co,
+                                                    T* __restrict__ dbias) {
   const int k = blockIdx.y;
+  if (k == kV) {  // row kV of the grid: dbias stage 2, when the stage-1 partials ride along
+    if (int(blockIdx.x) * 16 < Co) colsum_final_block<T>(blockIdx.x, bias_part, bias_nb, Co, dbias);
+    return;
+  }
   const int64_t e = int64_t(blockIdx.x) * 256 + threadIdx.x;
   if (e >= cico) return;
   const int64_t pk = hdr->pair_count[k];
@@ -929,82 +1045,6 @@ __global__ void __launch_bounds__(256) wgrad_reduce(const float* __restrict__ pa
   float s = 0.f;
   for (int c = 0; c < nch; ++c) s += src[int64_t(c) * cico];
   dW[int64_t(k) * cico + e] = Elt<T>::store(s);
-}
-
-// dbias stage 1: workgroup (x, y) sums rows [x*rows, (x+1)*rows) of the
-// column vectors [y*cvb, (y+1)*cvb) (16 bytes each).  Thread t takes vector
-// t % cvb and every (256/cvb)-th row from phase t / cvb, four loads in
-// flight, adding in increasing row order; the phases are then added in order.
-template <typename T>
-__global__ void __launch_bounds__(256) colsum_partial(const T* __restrict__ dY, int64_t n, int Co,
-                                                      int64_t rows, int cvb, float* __restrict__ part) {
-  constexpr int VEC = 16 / int(sizeof(T));
-  __shared__ float red[256 * VEC];
-  const int cv = threadIdx.x % cvb, ph = threadIdx.x / cvb, nph = 256 / cvb;
-  const int col = (blockIdx.y * cvb + cv) * VEC;
-  const int64_t r0 = int64_t(blockIdx.x) * rows;
-  const int64_t r1 = (r0 + rows < n) ? r0 + rows : n;
-  float acc[VEC];
-#pragma unroll
-  for (int q = 0; q < VEC; ++q) acc[q] = 0.f;
-  auto add = [&](const u32x4& v) {
-    const T* e = reinterpret_cast<const T*>(&v);
-#pragma unroll
-    for (int q = 0; q < VEC; ++q) acc[q] += Elt<T>::load(e[q]);
-  };
-  if (col < Co && ph < nph) {
-    const T* base = dY + col;
-    int64_t r = r0 + ph;
-    for (; r + 3 * nph < r1; r += 4 * nph) {
-      u32x4 v[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const u32x4*>(base + (r + u * nph) * Co);
-#pragma unroll
-      for (int u = 0; u < 4; ++u) add(v[u]);
-    }
-    for (; r < r1; r += nph) add(*reinterpret_cast<const u32x4*>(base + r * Co));
-  }
-  if (ph < nph) {
-#pragma unroll
-    for (int q = 0; q < VEC; ++q) red[(ph * cvb + cv) * VEC + q] = acc[q];
-  }
-  __syncthreads();
-  const int c = blockIdx.y * cvb * VEC + threadIdx.x;
-  if (threadIdx.x < cvb * VEC && c < Co) {
-    float sum = 0.f;
-    for (int q = 0; q < nph; ++q) sum += red[q * cvb * VEC + threadIdx.x];
-    part[int64_t(blockIdx.x) * Co + c] = sum;
-  }
-}
-
-// dbias stage 2: 16 columns per workgroup, 16 phases each adding every 16th
-// partial (four loads in flight), then the phases in a fixed order.
-template <typename T>
-__global__ void __launch_bounds__(256) colsum_final(const float* __restrict__ part, int nb, int Co,
-                                                    T* __restrict__ dbias) {
-  __shared__ float red[16][16];
-  const int cl = threadIdx.x & 15, ph = threadIdx.x >> 4;
-  const int c = blockIdx.x * 16 + cl;
-  float s = 0.f;
-  if (c < Co) {
-    int b = ph;
-    for (; b + 48 < nb; b += 64) {
-      float v[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) v[u] = part[int64_t(b + 16 * u) * Co + c];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) s += v[u];
-    }
-    for (; b < nb; b += 16) s += part[int64_t(b) * Co + c];
-  }
-  red[ph][cl] = s;
-  __syncthreads();
-  if (ph == 0 && c < Co) {
-    float t = 0.f;
-#pragma unroll
-    for (int q = 0; q < 16; ++q) t += red[q][cl];
-    dbias[c] = Elt<T>::store(t);
-  }
 }
 
 template <typename T>
@@ -1180,23 +1220,43 @@ static void launch_igemm(const T* A, const T* Bt, const T* bias, T* out, const u
   else igemm_pick_rows<T, 1>(A, Bt, bias, out, nmap, perm, smask, zrow, n, K, N, flip, partial, s);
 }
 
+// dbias stage 1 geometry: column vectors (16 bytes) per work item, all of them
+// up to 32, as a power of two
+static inline int colsum_cvb(int Co, int esize) {
+  const int nvec = Co / (16 / esize);
+  int cvb = 1;
+  while (cvb < nvec && cvb < 32) cvb *= 2;
+  return cvb;
+}
+static inline int colsum_groups(int Co, int esize) {
+  const int nvec = Co / (16 / esize), cvb = colsum_cvb(Co, esize);
+  return (nvec + cvb - 1) / cvb;
+}
+
+// Launches the weight-gradient partials.  With `bias_part` set (16-bit types),
+// dbias stage 1 runs in the same launch, as extra workgroups after the grid;
+// returns whether it did.
 template <typename T>
-static void launch_wgrad(const T* X, const T* dY, const uint32_t* pi, const uint32_t* pj, const PlanHeader* h,
-                         const uint32_t* pseg, const T* zrow, float* partial, int Ci, int Co, const BwdShape& b,
-                         hipStream_t s) {
+static bool launch_wgrad(const T* X, const T* dY, const uint32_t* pi, const uint32_t* pj, const PlanHeader* h,
+                         const uint32_t* pseg, const T* zrow, float* partial, int64_t n, int Ci, int Co,
+                         const BwdShape& b, float* bias_part, hipStream_t s) {
   dim3 grid(unsigned(b.max_chunks), kV, unsigned(b.mt * b.nt));
   if constexpr (sizeof(T) == 2) {
-    const dim3 grid1(b.rows_bpc > 0 ? xcd_group_grid(b.max_chunks, kV * b.mt * b.nt)
-                                    : xcd_group_grid(kV * b.max_chunks, b.mt * b.nt));
+    const unsigned nwg = b.rows_bpc > 0 ? xcd_group_grid(b.max_chunks, kV * b.mt * b.nt)
+                                        : xcd_group_grid(kV * b.max_chunks, b.mt * b.nt);
+    BiasJob<T> bj{dY, n, b.bias_rows, Co, colsum_cvb(Co, 2), b.bias_blocks, nwg, bias_part};
+    const unsigned nbias = bias_part ? unsigned(b.bias_blocks) * unsigned(colsum_groups(Co, 2)) : 0u;
+    const dim3 grid1(nwg + nbias);
 #define SSC_WTR(FM, FN, NWM, NWN)                                                                        \
   wgrad_tr<T, FM, FN, NWM, NWN, 32, 2><<<grid1, 64 * NWM * NWN, 0, s>>>(X, dY, pi, pj, h, partial, Ci, Co, \
                                                                        b.chunk_len, b.max_chunks, b.mt, b.nt, \
-                                                                       pseg, b.pblk, b.rows_bpc, zrow)
+                                                                       pseg, b.pblk, b.rows_bpc, zrow, bj)
     if (b.bm == 256) SSC_WTR(2, 4, 4, 2);
     else if (b.bm == 128) SSC_WTR(2, 2, 2, 2);
     else if (b.bm == 64) SSC_WTR(1, 1, 2, 2);
     else SSC_WTR(1, 1, 1, 1);
 #undef SSC_WTR
+    return bias_part != nullptr;
   } else {
   if (b.bm == 128 && b.bn == 128)
     wgrad<T, 128, 128, 32, 2, 2><<<grid, 256, 0, s>>>(X, dY, pi, pj, h, partial, Ci, Co, b.chunk_len,
@@ -1226,6 +1286,7 @@ static void launch_wgrad(const T* X, const T* dY, const uint32_t* pi, const uint
     wgrad<T, 128, 32, 32, 2, 1><<<grid, 128, 0, s>>>(X, dY, pi, pj, h, partial, Ci, Co, b.chunk_len,
                                                       b.max_chunks, b.nt);
   }
+  return false;
 }
 
 template <typename T>
@@ -1260,26 +1321,31 @@ static int run_bwd(const char* plan, const uint32_t* nmap, const int32_t* perm, 
                     reinterpret_cast<const uint32_t*>(plan + L.smask), reinterpret_cast<const T*>(plan + L.zrow),
                     n, Co, Ci, 1, reinterpret_cast<float*>(ws + W.split), s);
   }
+  float* bpart = reinterpret_cast<float*>(ws + W.bias);
+  bool bias_done = false;
   if (dweight) {
     float* part = reinterpret_cast<float*>(ws + W.partial);
-    launch_wgrad<T>(static_cast<const T*>(feats), dY, reinterpret_cast<const uint32_t*>(plan + L.pair_i),
-                    reinterpret_cast<const uint32_t*>(plan + L.pair_j), h,
-                    reinterpret_cast<const uint32_t*>(plan + L.pseg), reinterpret_cast<const T*>(plan + L.zrow),
-                    part, Ci, Co, b, s);
+    const bool ride = launch_wgrad<T>(static_cast<const T*>(feats), dY,
+                                      reinterpret_cast<const uint32_t*>(plan + L.pair_i),
+                                      reinterpret_cast<const uint32_t*>(plan + L.pair_j), h,
+                                      reinterpret_cast<const uint32_t*>(plan + L.pseg),
+                                      reinterpret_cast<const T*>(plan + L.zrow), part, n, Ci, Co, b,
+                                      dbias ? bpart : nullptr, s);
+    // with the stage-1 partials written by that launch, stage 2 is one more grid row here
     const int64_t cico = int64_t(Ci) * Co;
-    dim3 rg(unsigned((cico + 255) / 256), kV);
+    int64_t rx = (cico + 255) / 256;
+    if (ride && (Co + 15) / 16 > rx) rx = (Co + 15) / 16;
+    dim3 rg(unsigned(rx), kV + (ride ? 1 : 0));
     wgrad_reduce<T><<<rg, 256, 0, s>>>(part, h, static_cast<T*>(dweight), cico, b.chunk_len, b.max_chunks,
-                                       b.rows_bpc > 0 ? 1 : 0);
+                                       b.rows_bpc > 0 ? 1 : 0, bpart, b.bias_blocks, Co,
+                                       static_cast<T*>(dbias));
+    bias_done = ride;
   }
-  if (dbias) {
-    float* part = reinterpret_cast<float*>(ws + W.bias);
-    // column vectors per workgroup: all of them up to 32, as a power of two
-    const int vec = 16 / int(sizeof(T)), nvec = Co / vec;
-    int cvb = 1;
-    while (cvb < nvec && cvb < 32) cvb *= 2;
-    colsum_partial<T><<<dim3(unsigned(b.bias_blocks), unsigned((nvec + cvb - 1) / cvb)), 256, 0, s>>>(
-        dY, n, Co, b.bias_rows, cvb, part);
-    colsum_final<T><<<unsigned((Co + 15) / 16), 256, 0, s>>>(part, b.bias_blocks, Co, static_cast<T*>(dbias));
+  if (dbias && !bias_done) {
+    const int cvb = colsum_cvb(Co, int(sizeof(T)));
+    colsum_partial<T><<<dim3(unsigned(b.bias_blocks), unsigned(colsum_groups(Co, int(sizeof(T))))), 256, 0, s>>>(
+        dY, n, Co, b.bias_rows, cvb, bpart);
+    colsum_final<T><<<unsigned((Co + 15) / 16), 256, 0, s>>>(bpart, b.bias_blocks, Co, static_cast<T*>(dbias));
   }
   return SSC_OK;
 }
