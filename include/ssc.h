@@ -208,6 +208,52 @@ int ssc_encode_seq(const int32_t* coords, int64_t n, int32_t B, int32_t X, int32
 int ssc_decode_seq(const void* codes, int64_t n, int32_t B, int32_t X, int32_t Y, int32_t Z,
                    int32_t mode, int32_t code_width, int32_t* coords, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Sparse grid sampling: trilinear interpolation of the features of a voxel
+ * set at continuous points (the report's sparse grid_sample operator, whose
+ * forward and backward kernels are index-weighted sums; section two, the
+ * ops.grid_sample and kernels.triton.grid_sample module rows and the
+ * indice_weighed_sum_fwd / bwd key-function row; trilinear is the mode the
+ * extension section names).
+ *
+ * A point is a float row [b, x, y, z] in voxel-index units: voxel
+ * [b, x, y, z] sits at the integer point (x, y, z) of sample b.  With
+ * x0 = floor(x) and t = x - x0 (likewise y, z), corner j = 4 dx + 2 dy + dz
+ * (dx, dy, dz in {0, 1}) is the cell (x0 + dx, y0 + dy, z0 + dz) with weight
+ * w_j = wx * wy * wz, wx = t if dx else 1 - t, and
+ *   out[m]    = sum_j w_j * feats[row of corner j]      (fwd)
+ *   dfeats[i] = sum over (m, j) whose corner is voxel i of w_j * dout[m]  (bwd)
+ * A corner off the grid or not among the voxels adds nothing (no
+ * renormalisation); a point whose b is not an integer in [0, B) or whose
+ * coordinates are not finite samples zero.  Gradients with respect to the
+ * points are not computed.
+ *
+ * plan      a plan from ssc_build_neighbor_map over the same n voxels with
+ *           the same B, X, Y, Z and key_bits: its voxel hash table is read.
+ * C         channels; C * element bytes must be a multiple of 16, C <= 4096.
+ * points    [m][4] float32, 16-byte aligned; m <= SSC_MAX_POINTS.
+ * Accumulation is fp32 in corner order (fwd) and outputs are rounded to
+ * nearest even.  The backward pass adds into an fp32 image of dfeats with
+ * float atomics, so its summation order (and last bits) can vary from run
+ * to run; for 16-bit types that image lives in the workspace.
+ * ------------------------------------------------------------------------ */
+#define SSC_MAX_POINTS (1LL << 30)
+
+/* Workspace bytes for ssc_grid_sample_bwd (at least 256); 0 for invalid
+ * arguments. */
+size_t ssc_grid_sample_workspace_bytes(int64_t n, int32_t C, int32_t dtype);
+
+/* out [m][C] (dtype), overwritten; feats [n][C].  n == 0 writes zeros. */
+int ssc_grid_sample_fwd(const void* plan, int64_t n, int32_t B, int32_t X, int32_t Y, int32_t Z,
+                        int32_t key_bits, int32_t C, int32_t dtype, const void* feats, const float* points,
+                        int64_t m, void* out, void* stream);
+
+/* dfeats [n][C] (dtype), overwritten; dout [m][C].  m == 0 writes zeros. */
+int ssc_grid_sample_bwd(const void* plan, int64_t n, int32_t B, int32_t X, int32_t Y, int32_t Z,
+                        int32_t key_bits, int32_t C, int32_t dtype, const float* points, int64_t m,
+                        const void* dout, void* dfeats, void* workspace, size_t workspace_bytes,
+                        void* stream);
+
 /* Static, human-readable name of a status code (host only). */
 const char* ssc_status_string(int status);
 

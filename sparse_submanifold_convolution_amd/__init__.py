@@ -4,10 +4,12 @@ The compute path is libssc.so (hand-written HIP for gfx950, C ABI in
 include/ssc.h); ``binding`` marshals torch tensors into it.  ``workloads``
 draws the seeded synthetic inputs.
 """
-from .binding import (Plan, SSCError, build_neighbor_map, conv_workspace_bytes, decode_seq, encode_seq, lib,
-                      lib_path, plan_bytes, plan_pair_counts, plan_status, seq_code_width, status_string,
-                      subm_conv3d, subm_conv3d_bwd, subm_conv3d_fwd, workspace)
+from .binding import (Plan, SSCError, build_neighbor_map, conv_workspace_bytes, decode_seq, encode_seq,
+                      grid_sample, grid_sample_bwd, grid_sample_fwd, grid_sample_workspace_bytes, lib, lib_path,
+                      plan_bytes, plan_pair_counts, plan_status, seq_code_width, status_string, subm_conv3d,
+                      subm_conv3d_bwd, subm_conv3d_fwd, workspace)
 
-__all__ = ["Plan", "SSCError", "build_neighbor_map", "conv_workspace_bytes", "decode_seq", "encode_seq", "lib",
+__all__ = ["Plan", "SSCError", "build_neighbor_map", "conv_workspace_bytes", "decode_seq", "encode_seq",
+           "grid_sample", "grid_sample_bwd", "grid_sample_fwd", "grid_sample_workspace_bytes", "lib",
            "lib_path", "plan_bytes", "plan_pair_counts", "plan_status", "seq_code_width", "status_string",
            "subm_conv3d", "subm_conv3d_bwd", "subm_conv3d_fwd", "workspace"]

@@ -35,6 +35,11 @@ SIGNATURES = {
     "ssc_seq_code_width": (_I32, [_I32, _I32, _I32, _I32]),
     "ssc_encode_seq": (ctypes.c_int, [_VP, _I64, _I32, _I32, _I32, _I32, _I32, _VP, _I32, _VP]),
     "ssc_decode_seq": (ctypes.c_int, [_VP, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _VP, _VP]),
+    "ssc_grid_sample_workspace_bytes": (_SZ, [_I64, _I32, _I32]),
+    "ssc_grid_sample_fwd": (ctypes.c_int, [_VP, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _VP, _VP, _I64,
+                                           _VP, _VP]),
+    "ssc_grid_sample_bwd": (ctypes.c_int, [_VP, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _VP, _I64, _VP,
+                                           _VP, _VP, _SZ, _VP]),
 }
 
 SEQ_MODES = {"z_order": 0, "hilbert": 1}
@@ -287,3 +292,75 @@ def decode_seq(codes: torch.Tensor, shape, mode: str = "z_order") -> torch.Tenso
     _check("ssc_decode_seq", lib().ssc_decode_seq(_ptr(codes), n, *grid, _mode(mode), width, _ptr(coords),
                                                   _stream(dev)))
     return coords
+
+
+# ---------------------------------------------------------------------------
+# sparse grid sampling
+# ---------------------------------------------------------------------------
+
+def grid_sample_workspace_bytes(n: int, c: int, dtype: torch.dtype) -> int:
+    return int(lib().ssc_grid_sample_workspace_bytes(int(n), int(c), DTYPE_CODE[dtype]))
+
+
+def grid_sample_fwd(plan: Plan, feats: torch.Tensor, points: torch.Tensor,
+                    out: torch.Tensor | None = None) -> torch.Tensor:
+    """ssc_grid_sample_fwd: trilinear samples [m, C] of the plan's voxel features at float32 [m, 4] points."""
+    dev, dt, n = plan.device, feats.dtype, plan.n
+    c, m = int(feats.shape[1]), int(points.shape[0])
+    _need(feats, "feats", dt, (n, c), dev)
+    _need(points, "points", torch.float32, (m, 4), dev)
+    if dt not in DTYPE_CODE:
+        raise SSCError("ssc_grid_sample_fwd", 2)
+    if out is None:
+        out = torch.empty((m, c), dtype=dt, device=dev)
+    _need(out, "out", dt, (m, c), dev)
+    B, X, Y, Z = plan.shape
+    _check("ssc_grid_sample_fwd",
+           lib().ssc_grid_sample_fwd(_ptr(plan.buf), n, B, X, Y, Z, plan.key_bits, c, DTYPE_CODE[dt], _ptr(feats),
+                                     _ptr(points), m, _ptr(out), _stream(dev)))
+    return out
+
+
+def grid_sample_bwd(plan: Plan, points: torch.Tensor, dout: torch.Tensor, dfeats: torch.Tensor | None = None,
+                    ws: torch.Tensor | None = None) -> torch.Tensor:
+    """ssc_grid_sample_bwd: the feature gradient [n, C] of grid_sample_fwd for output gradient dout [m, C]."""
+    dev, dt, n = plan.device, dout.dtype, plan.n
+    c, m = int(dout.shape[1]), int(points.shape[0])
+    _need(points, "points", torch.float32, (m, 4), dev)
+    _need(dout, "dout", dt, (m, c), dev)
+    if dt not in DTYPE_CODE:
+        raise SSCError("ssc_grid_sample_bwd", 2)
+    if dfeats is None:
+        dfeats = torch.empty((n, c), dtype=dt, device=dev)
+    _need(dfeats, "dfeats", dt, (n, c), dev)
+    if ws is None:
+        nbytes = grid_sample_workspace_bytes(n, c, dt)
+        if nbytes == 0:
+            raise SSCError("ssc_grid_sample_workspace_bytes", 2)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    B, X, Y, Z = plan.shape
+    _check("ssc_grid_sample_bwd",
+           lib().ssc_grid_sample_bwd(_ptr(plan.buf), n, B, X, Y, Z, plan.key_bits, c, DTYPE_CODE[dt], _ptr(points),
+                                     m, _ptr(dout), _ptr(dfeats), _ptr(ws), ws.numel(), _stream(dev)))
+    return dfeats
+
+
+class GridSampleFunction(torch.autograd.Function):
+    """autograd wrapper: gradient with respect to the voxel features only."""
+
+    @staticmethod
+    def forward(ctx, feats, points, plan):
+        ctx.plan = plan
+        ctx.save_for_backward(points)
+        return grid_sample_fwd(plan, feats.contiguous(), points.contiguous())
+
+    @staticmethod
+    def backward(ctx, dout):
+        (points,) = ctx.saved_tensors
+        d = grid_sample_bwd(ctx.plan, points, dout.contiguous()) if ctx.needs_input_grad[0] else None
+        return d, None, None
+
+
+def grid_sample(feats: torch.Tensor, plan: Plan, points: torch.Tensor) -> torch.Tensor:
+    """Differentiable trilinear sampling of the voxel features at [m, 4] float32 points (b, x, y, z)."""
+    return GridSampleFunction.apply(feats, points, plan)

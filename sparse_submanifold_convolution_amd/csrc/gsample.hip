@@ -1,0 +1,366 @@
+// Sparse grid sampling on gfx950: trilinear weighted sums of voxel feature
+// rows at continuous points, and the transposed sums for the feature gradient.
+//
+// The FlexGEMM pages list a sparse grid_sample operator whose forward and
+// backward kernels are index-weighted sums (contributor report, section two:
+// the ops.grid_sample and kernels.triton.grid_sample module rows and the
+// indice_weighed_sum_fwd / bwd key-function row), with trilinear
+// interpolation as the existing mode (the extension section).  Readings used
+// here: a point is a float row [b, x, y, z] in voxel-index units (voxel
+// [b, x, y, z] sits at the integer point); with x0 = floor(x), t = x - x0,
+// corner j = 4 dx + 2 dy + dz is (x0 + dx, y0 + dy, z0 + dz) with weight
+// wx * wy * wz, wx = t if dx else 1 - t; a corner that is off the grid or not
+// an active voxel adds nothing and the other weights are not renormalised; a
+// point whose batch value is not an integer in [0, B) or whose coordinates
+// are not finite samples zero.
+//
+// Design.  A group of L lanes (8..64, a power of two) owns one point: its
+// first 8 lanes look up the 8 corners in the plan's voxel hash table at the
+// same time and the group shares rows and weights through lane shuffles;
+// then each lane streams 16-byte vectors of the 8 corner rows (an absent
+// corner reads the plan's zero row, so the loads carry no branch) and
+// accumulates in fp32 in corner order.  The backward pass adds weight * dout
+// into an fp32 image of dfeats with hardware float atomics, then rounds it to
+// the element type; its summation order is therefore not fixed.
+
+#include <hip/hip_runtime.h>
+
+#include "hash.h"
+#include "ssc_internal.h"
+
+namespace ssc {
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte vectors of one element type: VEC elements, unpacked to fp32 and
+// packed back with round-to-nearest-even
+template <int DT>
+struct GsVec;
+
+template <>
+struct GsVec<SSC_F32> {
+  static constexpr int kVec = 4;
+  __device__ static void unpack(const u32x4& v, float (&f)[4]) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) f[e] = __uint_as_float(v[e]);
+  }
+  __device__ static u32x4 pack(const float (&f)[4]) {
+    u32x4 v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = __float_as_uint(f[e]);
+    return v;
+  }
+};
+
+template <>
+struct GsVec<SSC_F16> {
+  static constexpr int kVec = 8;
+  __device__ static float lo(uint32_t u, int h) {
+    return float(__builtin_bit_cast(_Float16, uint16_t(h ? (u >> 16) : (u & 0xffffu))));
+  }
+  __device__ static void unpack(const u32x4& v, float (&f)[8]) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[e] = lo(v[e / 2], e & 1);
+  }
+  __device__ static u32x4 pack(const float (&f)[8]) {
+    u32x4 v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      v[e] = uint32_t(__builtin_bit_cast(uint16_t, _Float16(f[2 * e]))) |
+             (uint32_t(__builtin_bit_cast(uint16_t, _Float16(f[2 * e + 1]))) << 16);
+    return v;
+  }
+};
+
+template <>
+struct GsVec<SSC_BF16> {
+  static constexpr int kVec = 8;
+  __device__ static void unpack(const u32x4& v, float (&f)[8]) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[e] = bf16_to_f32(uint16_t((e & 1) ? (v[e / 2] >> 16) : (v[e / 2] & 0xffffu)));
+  }
+  __device__ static u32x4 pack(const float (&f)[8]) {
+    u32x4 v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      v[e] = uint32_t(f32_to_bf16_rne(f[2 * e])) | (uint32_t(f32_to_bf16_rne(f[2 * e + 1])) << 16);
+    return v;
+  }
+};
+
+struct GsGrid {
+  int B, X, Y, Z;
+};
+
+// Corner j of point p: its voxel row (or the sentinel) and its weight (0 when
+// the corner is absent).
+template <typename KeyT>
+__device__ __forceinline__ void corner_lookup(const float4 p, int j, const GsGrid g,
+                                              const Slot<KeyT>* __restrict__ table, uint64_t capacity,
+                                              uint32_t* row, float* w) {
+  *row = kSentinel;
+  *w = 0.f;
+  // NaN fails every comparison below, so it lands here too
+  if (!(p.x >= 0.f && p.x < float(g.B) && p.x == floorf(p.x))) return;
+  if (!(p.y > -1.f && p.y < float(g.X) && p.z > -1.f && p.z < float(g.Y) && p.w > -1.f && p.w < float(g.Z)))
+    return;
+  const float fx = floorf(p.y), fy = floorf(p.z), fz = floorf(p.w);
+  const int dx = (j >> 2) & 1, dy = (j >> 1) & 1, dz = j & 1;
+  const int cx = int(fx) + dx, cy = int(fy) + dy, cz = int(fz) + dz;
+  if (cx < 0 || cx >= g.X || cy < 0 || cy >= g.Y || cz < 0 || cz >= g.Z) return;
+  const float tx = p.y - fx, ty = p.z - fy, tz = p.w - fz;
+  const float wx = dx ? tx : 1.f - tx, wy = dy ? ty : 1.f - ty, wz = dz ? tz : 1.f - tz;
+  const uint32_t r = hash_lookup<KeyT>(table, capacity, KeyT(pack_key(int(p.x), cx, cy, cz, g.X, g.Y, g.Z)));
+  if (r == kSentinel) return;
+  *row = r;
+  *w = (wx * wy) * wz;
+}
+
+// The 8 corners of the group's point, shared from the group's first 8 lanes.
+template <typename KeyT, int L>
+__device__ __forceinline__ void group_corners(const float4* __restrict__ pts, int64_t p, const GsGrid g,
+                                              const Slot<KeyT>* __restrict__ table, uint64_t capacity,
+                                              uint32_t (&rows)[8], float (&ws)[8]) {
+  static_assert(L >= 8 && L <= 64 && (L & (L - 1)) == 0, "a group is 8..64 lanes, a power of two");
+  const int q = threadIdx.x % L;
+  uint32_t row = kSentinel;
+  float w = 0.f;
+  if (q < 8) corner_lookup<KeyT>(pts[p], q, g, table, capacity, &row, &w);
+  const int first = int(threadIdx.x % 64) - q;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    rows[j] = uint32_t(__shfl(int(row), first + j, 64));
+    ws[j] = __shfl(w, first + j, 64);
+  }
+}
+
+template <int DT, typename KeyT, int L>
+__global__ void __launch_bounds__(256) gs_fwd(const u32x4* __restrict__ feats, const float4* __restrict__ pts,
+                                              int64_t m, int nvec, const GsGrid g,
+                                              const Slot<KeyT>* __restrict__ table, uint64_t capacity,
+                                              const u32x4* __restrict__ zrow, u32x4* __restrict__ out) {
+  using V = GsVec<DT>;
+  constexpr int kG = 256 / L;
+  const int64_t p = int64_t(blockIdx.x) * kG + threadIdx.x / L;
+  if (p >= m) return;  // uniform over the group
+  uint32_t rows[8];
+  float ws[8];
+  group_corners<KeyT, L>(pts, p, g, table, capacity, rows, ws);
+  for (int v = int(threadIdx.x % L); v < nvec; v += L) {
+    u32x4 x[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      x[j] = *(rows[j] != kSentinel ? feats + int64_t(rows[j]) * nvec + v : zrow + v);
+    float acc[V::kVec];
+#pragma unroll
+    for (int e = 0; e < V::kVec; ++e) acc[e] = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float f[V::kVec];
+      V::unpack(x[j], f);
+#pragma unroll
+      for (int e = 0; e < V::kVec; ++e) acc[e] = fmaf(ws[j], f[e], acc[e]);
+    }
+    out[p * nvec + v] = V::pack(acc);
+  }
+}
+
+template <int DT, typename KeyT, int L>
+__global__ void __launch_bounds__(256) gs_bwd(const u32x4* __restrict__ dout, const float4* __restrict__ pts,
+                                              int64_t m, int nvec, const GsGrid g,
+                                              const Slot<KeyT>* __restrict__ table, uint64_t capacity,
+                                              float* __restrict__ acc) {
+  using V = GsVec<DT>;
+  constexpr int kG = 256 / L;
+  const int64_t p = int64_t(blockIdx.x) * kG + threadIdx.x / L;
+  if (p >= m) return;
+  uint32_t rows[8];
+  float ws[8];
+  group_corners<KeyT, L>(pts, p, g, table, capacity, rows, ws);
+  const int64_t C = int64_t(nvec) * V::kVec;
+  for (int v = int(threadIdx.x % L); v < nvec; v += L) {
+    float d[V::kVec];
+    V::unpack(dout[p * nvec + v], d);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (rows[j] == kSentinel) continue;
+      float* dst = acc + int64_t(rows[j]) * C + int64_t(v) * V::kVec;
+#pragma unroll
+      for (int e = 0; e < V::kVec; ++e) unsafeAtomicAdd(dst + e, ws[j] * d[e]);
+    }
+  }
+}
+
+// zero `count` 16-byte vectors (a kernel, not a memset, so the call can be
+// captured into a graph)
+__global__ void __launch_bounds__(256) gs_zero(u32x4* __restrict__ p, int64_t count) {
+  const u32x4 z = {0u, 0u, 0u, 0u};
+  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < count; i += int64_t(gridDim.x) * 256) p[i] = z;
+}
+
+// dfeats = the fp32 sums rounded to the element type, 16 bytes out per thread
+template <int DT>
+__global__ void __launch_bounds__(256) gs_round(const float4* __restrict__ acc, int64_t nvec_total,
+                                                u32x4* __restrict__ dst) {
+  using V = GsVec<DT>;
+  static_assert(V::kVec == 8, "16-bit element types only");
+  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < nvec_total; i += int64_t(gridDim.x) * 256) {
+    const float4 a = acc[2 * i], b = acc[2 * i + 1];
+    const float f[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    dst[i] = V::pack(f);
+  }
+}
+
+unsigned stream_grid(int64_t count) {
+  const int64_t b = (count + 255) / 256;
+  return unsigned(b < 1 ? 1 : (b > 4096 ? 4096 : b));
+}
+
+int group_lanes(int nvec) { return nvec <= 8 ? 8 : nvec <= 16 ? 16 : nvec <= 32 ? 32 : 64; }
+
+template <int DT, typename KeyT>
+void launch_fwd(const void* feats, const float* pts, int64_t m, int nvec, GsGrid g, const Slot<KeyT>* table,
+                uint64_t capacity, const void* zrow, void* out, hipStream_t s) {
+  const int L = group_lanes(nvec);
+  const unsigned grid = unsigned((m + (256 / L) - 1) / (256 / L));
+  const u32x4* f = static_cast<const u32x4*>(feats);
+  const float4* p = reinterpret_cast<const float4*>(pts);
+  const u32x4* z = static_cast<const u32x4*>(zrow);
+  u32x4* o = static_cast<u32x4*>(out);
+  if (L == 8) gs_fwd<DT, KeyT, 8><<<grid, 256, 0, s>>>(f, p, m, nvec, g, table, capacity, z, o);
+  else if (L == 16) gs_fwd<DT, KeyT, 16><<<grid, 256, 0, s>>>(f, p, m, nvec, g, table, capacity, z, o);
+  else if (L == 32) gs_fwd<DT, KeyT, 32><<<grid, 256, 0, s>>>(f, p, m, nvec, g, table, capacity, z, o);
+  else gs_fwd<DT, KeyT, 64><<<grid, 256, 0, s>>>(f, p, m, nvec, g, table, capacity, z, o);
+}
+
+template <int DT, typename KeyT>
+void launch_bwd(const void* dout, const float* pts, int64_t m, int nvec, GsGrid g, const Slot<KeyT>* table,
+                uint64_t capacity, float* acc, hipStream_t s) {
+  const int L = group_lanes(nvec);
+  const unsigned grid = unsigned((m + (256 / L) - 1) / (256 / L));
+  const u32x4* d = static_cast<const u32x4*>(dout);
+  const float4* p = reinterpret_cast<const float4*>(pts);
+  if (L == 8) gs_bwd<DT, KeyT, 8><<<grid, 256, 0, s>>>(d, p, m, nvec, g, table, capacity, acc);
+  else if (L == 16) gs_bwd<DT, KeyT, 16><<<grid, 256, 0, s>>>(d, p, m, nvec, g, table, capacity, acc);
+  else if (L == 32) gs_bwd<DT, KeyT, 32><<<grid, 256, 0, s>>>(d, p, m, nvec, g, table, capacity, acc);
+  else gs_bwd<DT, KeyT, 64><<<grid, 256, 0, s>>>(d, p, m, nvec, g, table, capacity, acc);
+}
+
+template <int DT>
+void dispatch_fwd(int kb, const char* plan, const PlanLayout& L, const void* feats, const float* pts, int64_t m,
+                  int nvec, GsGrid g, void* out, hipStream_t s) {
+  const void* zrow = plan + L.zrow;
+  if (kb == 64)
+    launch_fwd<DT, uint64_t>(feats, pts, m, nvec, g, reinterpret_cast<const Slot<uint64_t>*>(plan + L.table),
+                             L.capacity, zrow, out, s);
+  else
+    launch_fwd<DT, uint32_t>(feats, pts, m, nvec, g, reinterpret_cast<const Slot<uint32_t>*>(plan + L.table),
+                             L.capacity, zrow, out, s);
+}
+
+template <int DT>
+void dispatch_bwd(int kb, const char* plan, const PlanLayout& L, const void* dout, const float* pts, int64_t m,
+                  int nvec, GsGrid g, float* acc, hipStream_t s) {
+  if (kb == 64)
+    launch_bwd<DT, uint64_t>(dout, pts, m, nvec, g, reinterpret_cast<const Slot<uint64_t>*>(plan + L.table),
+                             L.capacity, acc, s);
+  else
+    launch_bwd<DT, uint32_t>(dout, pts, m, nvec, g, reinterpret_cast<const Slot<uint32_t>*>(plan + L.table),
+                             L.capacity, acc, s);
+}
+
+int esize(int32_t dtype) { return dtype == SSC_F32 ? 4 : 2; }
+
+// checks shared by both passes; on success *kb is the plan's key width
+int gs_check(const void* plan, int64_t n, int32_t B, int32_t X, int32_t Y, int32_t Z, int32_t key_bits, int32_t C,
+             int32_t dtype, int64_t m, int* kb) {
+  if (!plan || !aligned16(plan)) return SSC_ERR_INVALID_ARG;
+  if (n < 0 || n > SSC_MAX_VOXELS || m < 0 || m > SSC_MAX_POINTS) return SSC_ERR_INVALID_ARG;
+  if (!grid_ok(B, X, Y, Z)) return SSC_ERR_INVALID_ARG;
+  if (key_bits != 0 && key_bits != 32 && key_bits != 64) return SSC_ERR_INVALID_ARG;
+  if (dtype != SSC_F32 && dtype != SSC_F16 && dtype != SSC_BF16) return SSC_ERR_UNSUPPORTED;
+  if (C <= 0 || C > 4096 || (int64_t(C) * esize(dtype)) % 16 != 0) return SSC_ERR_UNSUPPORTED;
+  *kb = effective_key_bits(B, X, Y, Z, key_bits);
+  return *kb < 0 ? SSC_ERR_UNSUPPORTED : SSC_OK;
+}
+
+}  // namespace
+
+}  // namespace ssc
+
+using namespace ssc;
+
+extern "C" size_t ssc_grid_sample_workspace_bytes(int64_t n, int32_t C, int32_t dtype) {
+  if (n < 0 || n > SSC_MAX_VOXELS || C <= 0 || C > 4096) return 0;
+  if (dtype != SSC_F32 && dtype != SSC_F16 && dtype != SSC_BF16) return 0;
+  if ((int64_t(C) * esize(dtype)) % 16 != 0) return 0;
+  const size_t need = dtype == SSC_F32 ? 0 : size_t(n) * size_t(C) * 4;
+  return need < 256 ? 256 : align_up(need, 256);
+}
+
+extern "C" int ssc_grid_sample_fwd(const void* plan, int64_t n, int32_t B, int32_t X, int32_t Y, int32_t Z,
+                                   int32_t key_bits, int32_t C, int32_t dtype, const void* feats,
+                                   const float* points, int64_t m, void* out, void* stream) {
+  int kb = 0;
+  const int st = gs_check(plan, n, B, X, Y, Z, key_bits, C, dtype, m, &kb);
+  if (st != SSC_OK) return st;
+  if (m == 0) return SSC_OK;
+  if (!points || !out || !aligned16(points) || !aligned16(out)) return SSC_ERR_INVALID_ARG;
+  if (n > 0 && (!feats || !aligned16(feats))) return SSC_ERR_INVALID_ARG;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int nvec = int(int64_t(C) * esize(dtype) / 16);
+  (void)hipGetLastError();
+  if (n == 0) {
+    // no voxels: every sample is zero
+    gs_zero<<<stream_grid(m * nvec), 256, 0, s>>>(static_cast<u32x4*>(out), m * nvec);
+    return hipGetLastError() == hipSuccess ? SSC_OK : SSC_ERR_HIP;
+  }
+  const PlanLayout L = plan_layout(n, kb);
+  const char* pl = static_cast<const char*>(plan);
+  const GsGrid g{B, X, Y, Z};
+  if (dtype == SSC_F32) dispatch_fwd<SSC_F32>(kb, pl, L, feats, points, m, nvec, g, out, s);
+  else if (dtype == SSC_F16) dispatch_fwd<SSC_F16>(kb, pl, L, feats, points, m, nvec, g, out, s);
+  else dispatch_fwd<SSC_BF16>(kb, pl, L, feats, points, m, nvec, g, out, s);
+  return hipGetLastError() == hipSuccess ? SSC_OK : SSC_ERR_HIP;
+}
+
+extern "C" int ssc_grid_sample_bwd(const void* plan, int64_t n, int32_t B, int32_t X, int32_t Y, int32_t Z,
+                                   int32_t key_bits, int32_t C, int32_t dtype, const float* points, int64_t m,
+                                   const void* dout, void* dfeats, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+  int kb = 0;
+  const int st = gs_check(plan, n, B, X, Y, Z, key_bits, C, dtype, m, &kb);
+  if (st != SSC_OK) return st;
+  if (n == 0) return SSC_OK;
+  if (!dfeats || !aligned16(dfeats)) return SSC_ERR_INVALID_ARG;
+  if (m > 0 && (!points || !dout || !aligned16(points) || !aligned16(dout))) return SSC_ERR_INVALID_ARG;
+  const bool narrow = dtype != SSC_F32;
+  if (narrow && (!workspace || !aligned16(workspace))) return SSC_ERR_INVALID_ARG;
+  if (workspace_bytes < ssc_grid_sample_workspace_bytes(n, C, dtype) && narrow) return SSC_ERR_WORKSPACE;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int nvec = int(int64_t(C) * esize(dtype) / 16);
+  float* acc = narrow ? static_cast<float*>(workspace) : static_cast<float*>(dfeats);
+  const int64_t acc_vecs = n * int64_t(C) / 4;
+  (void)hipGetLastError();
+  gs_zero<<<stream_grid(acc_vecs), 256, 0, s>>>(reinterpret_cast<u32x4*>(acc), acc_vecs);
+  if (m > 0) {
+    const PlanLayout L = plan_layout(n, kb);
+    const char* pl = static_cast<const char*>(plan);
+    const GsGrid g{B, X, Y, Z};
+    if (dtype == SSC_F32) dispatch_bwd<SSC_F32>(kb, pl, L, dout, points, m, nvec, g, acc, s);
+    else if (dtype == SSC_F16) dispatch_bwd<SSC_F16>(kb, pl, L, dout, points, m, nvec, g, acc, s);
+    else dispatch_bwd<SSC_BF16>(kb, pl, L, dout, points, m, nvec, g, acc, s);
+  }
+  if (narrow) {
+    const int64_t out_vecs = n * int64_t(nvec);
+    if (dtype == SSC_F16)
+      gs_round<SSC_F16><<<stream_grid(out_vecs), 256, 0, s>>>(reinterpret_cast<const float4*>(acc), out_vecs,
+                                                              static_cast<u32x4*>(dfeats));
+    else
+      gs_round<SSC_BF16><<<stream_grid(out_vecs), 256, 0, s>>>(reinterpret_cast<const float4*>(acc), out_vecs,
+                                                               static_cast<u32x4*>(dfeats));
+  }
+  return hipGetLastError() == hipSuccess ? SSC_OK : SSC_ERR_HIP;
+}

@@ -249,3 +249,32 @@ def values_for(coords: np.ndarray, shape: tuple, seed: int, ci: int, co: int, dt
     bias = normal(rng, (co,), dtype) if random_bias else torch.zeros(co, dtype=DTYPES[dtype])
     return Workload(0, "given coords", np.ascontiguousarray(coords, dtype=np.int32), tuple(shape),
                     ci, co, dtype, 0, feats, weight, bias, dout)
+
+
+# ----------------------------------------------------------------------------
+# query points for sparse grid sampling
+# ----------------------------------------------------------------------------
+
+def sample_points(coords: np.ndarray, shape: tuple, m: int, seed: int, near: float = 0.9) -> np.ndarray:
+    """Seeded float32 [m, 4] query rows (b, x, y, z) for sparse grid sampling.
+
+    A fraction `near` of the points sit within one cell of an active voxel
+    (the voxel's position plus a uniform offset in [-1, 1)^3, same sample);
+    the rest are uniform over the sample-and-box [0, B) x [-1, X] x [-1, Y] x
+    [-1, Z], so some fall partly or wholly off the grid.  Points only: no
+    lookups or weights are computed here.
+    """
+    rng = np.random.default_rng(seed)
+    B, X, Y, Z = (int(s) for s in shape)
+    out = np.empty((m, 4), np.float32)
+    k = int(round(m * near)) if len(coords) else 0
+    if k:
+        pick = coords[rng.integers(0, len(coords), k)].astype(np.float64)
+        pick[:, 1:] += rng.uniform(-1.0, 1.0, (k, 3))
+        out[:k] = pick
+    r = m - k
+    if r:
+        out[k:, 0] = rng.integers(0, B, r)
+        for a, d in enumerate((X, Y, Z)):
+            out[k:, 1 + a] = rng.uniform(-1.0, d, r)
+    return out

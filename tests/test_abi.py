@@ -129,3 +129,27 @@ def test_seq_rejections(L):
     assert dec(k, 10, 1, 8, 8, 8, 0, 32, None, None) == bad_arg
     assert dec(k, 10, 1, 8, 8, 8, 0, 32, ctypes.c_void_p(FAKE.value + 8), None) == bad_arg
     assert dec(k, 0, 1, 8, 8, 8, 0, 64, c, None) == ok
+
+
+def test_grid_sample_workspace_and_rejections(L):
+    ws = L.ssc_grid_sample_workspace_bytes
+    assert ws(100, 64, 1) == 100 * 64 * 4 and ws(100, 64, 2) == 100 * 64 * 4
+    assert ws(100, 64, 0) == 256 and ws(0, 64, 1) == 256
+    assert ws(100, 12, 1) == 0 and ws(100, 6, 0) == 0 and ws(100, 64, 7) == 0 and ws(-1, 64, 0) == 0
+    assert ws(100, 8192, 1) == 0
+    f = L.ssc_grid_sample_fwd
+    pts = ctypes.c_void_p(FAKE.value + 4096)
+    assert f(None, 100, 1, 8, 8, 8, 0, 64, 1, FAKE, pts, 10, FAKE, None) == 1          # plan NULL
+    assert f(FAKE, 100, 1, 8, 8, 8, 0, 64, 5, FAKE, pts, 10, FAKE, None) == 2          # dtype
+    assert f(FAKE, 100, 1, 8, 8, 8, 0, 12, 1, FAKE, pts, 10, FAKE, None) == 2          # 24-byte rows
+    assert f(FAKE, 100, 1, 8, 8, 8, 48, 64, 1, FAKE, pts, 10, FAKE, None) == 1         # key_bits
+    assert f(FAKE, 100, 0, 8, 8, 8, 0, 64, 1, FAKE, pts, 10, FAKE, None) == 1          # B = 0
+    assert f(FAKE, 100, 1, 8, 8, 8, 0, 64, 1, FAKE, pts, -1, FAKE, None) == 1          # m < 0
+    assert f(FAKE, 100, 1, 8, 8, 8, 0, 64, 1, FAKE, ctypes.c_void_p(FAKE.value + 4), 10, FAKE, None) == 1
+    assert f(FAKE, 100, 1, 8, 8, 8, 0, 64, 1, None, pts, 10, FAKE, None) == 1          # feats NULL
+    assert f(FAKE, 100, 2, 2048, 2048, 2048, 32, 64, 1, FAKE, pts, 10, FAKE, None) == 2  # 32-bit keys too narrow
+    b = L.ssc_grid_sample_bwd
+    assert b(FAKE, 100, 1, 8, 8, 8, 0, 64, 1, pts, 10, FAKE, FAKE, FAKE, 64, None) == 3   # workspace small
+    assert b(FAKE, 100, 1, 8, 8, 8, 0, 64, 1, pts, 10, FAKE, FAKE, None, 1 << 30, None) == 1
+    assert b(FAKE, 100, 1, 8, 8, 8, 0, 64, 1, pts, 10, None, FAKE, FAKE, 1 << 30, None) == 1  # dout NULL
+    assert b(FAKE, 100, 1, 8, 8, 8, 0, 64, 1, pts, 10, FAKE, None, FAKE, 1 << 30, None) == 1  # dfeats NULL
