@@ -48,6 +48,9 @@ def parse():
     p.add_argument("--serialize", action="store_true",
                    help="only time encode_seq + decode_seq (z-order and Hilbert) on the workload's "
                         "coordinates; prints its own JSON line")
+    p.add_argument("--grid-sample", action="store_true",
+                   help="only time sparse grid sampling (fwd + feature gradient) at one point per voxel of "
+                        "the workload; prints its own JSON line")
     return p.parse_args()
 
 
@@ -195,6 +198,107 @@ def serialize_bench(args) -> None:
     }), flush=True)
 
 
+def grid_sample_bench(args) -> None:
+    """Sparse trilinear grid sampling, forward + feature gradient, inputs resident in HBM.
+
+    Points: one per voxel of the workload, 90 % within a cell of an active voxel and 10 % anywhere
+    in the box; dout ~ N(0, 1).  Each pass is captured in a HIP graph of `reps` calls and replayed.
+    """
+    import numpy as np
+    import torch
+    import sparse_submanifold_convolution_amd as ssc
+    from sparse_submanifold_convolution_amd import workloads as WL
+
+    dev = torch.device("cuda:0")
+    w = WL.make_workload(args.config)
+    m = w.n
+    pts_np = WL.sample_points(w.coords, w.shape, m, args.config)
+    plan = ssc.build_neighbor_map(torch.from_numpy(w.coords).to(dev), w.shape, key_bits=w.key_bits)
+    F = w.feats.to(dev)
+    P = torch.from_numpy(pts_np).to(dev)
+    dout = WL.normal(np.random.default_rng(1000 + args.config), (m, w.ci), w.dtype).to(dev)
+    out = torch.empty((m, w.ci), dtype=F.dtype, device=dev)
+    dF = torch.empty_like(F)
+    ws = torch.empty(ssc.grid_sample_workspace_bytes(w.n, m), dtype=torch.uint8, device=dev)
+    reps = 10
+    side = torch.cuda.Stream(dev)
+
+    def timed(fn):
+        side.wait_stream(torch.cuda.current_stream(dev))
+        with torch.cuda.stream(side):
+            fn()
+        torch.cuda.current_stream(dev).wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(reps):
+                fn()
+        for _ in range(max(1, args.warmup)):
+            g.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        best = 1e30
+        for _ in range(args.steps):
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            best = min(best, e0.elapsed_time(e1) / reps)
+        return best
+
+    t_fwd = timed(lambda: ssc.grid_sample_fwd(plan, F, P, out=out))
+    t_bwd = timed(lambda: ssc.grid_sample_bwd(plan, P, dout, dfeats=dF, ws=ws))
+    ms = t_fwd + t_bwd
+    s = F.element_size()
+    slot = 16 if plan_key_width(w) == 64 else 8
+    # gs_fwd, algorithmic bytes per launch: the points, the output rows, every voxel row once and
+    # one hash slot per corner lookup
+    fwd_bytes = m * 16 + s * w.ci * m + s * w.ci * w.n + 8 * slot * m
+    ach = fwd_bytes / (t_fwd * 1e-3) / 1e9
+    res = {
+        "metric": "points/s, sparse trilinear grid_sample fwd + feature gradient, 1 MI355X",
+        "value": m / (ms * 1e-3), "unit": "points/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": f"config {args.config} voxels: {w.desc}; one point per voxel",
+                   "voxels": w.n, "points": m, "channels": w.ci,
+                   "launch": f"graph of {reps} calls per pass, best replay", "parallelism": "single GPU"},
+        "per_pass_ms": {"fwd": t_fwd, "bwd": t_bwd},
+        "roofline": {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": ach / PEAK_HBM_GBS, "traffic": None, "kernel": "gs_fwd",
+                     "avg_launch_ms": t_fwd, "alg_bytes_per_launch": fwd_bytes},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = grid_sample_cpu_baseline(w, pts_np, dout.cpu(), args.cpu_budget_s)
+    print(json.dumps(res), flush=True)
+
+
+def plan_key_width(w) -> int:
+    """Key width the plan of workload w uses (the build's rule: 32 bits when the grid volume fits)."""
+    if w.key_bits:
+        return w.key_bits
+    B, X, Y, Z = w.shape
+    return 32 if B * X * Y * Z <= 0xFFFFFFFF else 64
+
+
+def grid_sample_cpu_baseline(w, pts, dout, budget_s: float) -> dict:
+    """The grid-sampling oracle (float64 numpy) on a bounded sample of the points, whole voxel set."""
+    from oracle import grid_sample as G
+    k = min(len(pts), 200000)
+    reps, t_total = 0, 0.0
+    while reps == 0 or (t_total < budget_s / 2 and reps < 3):
+        t0 = time.perf_counter()
+        G.sample_fwd(w.coords, w.feats, w.shape, pts[:k])
+        G.sample_bwd(w.coords, w.shape, pts[:k], dout[:k])
+        t_total += time.perf_counter() - t0
+        reps += 1
+    sec = t_total / reps
+    return {"value": k / sec, "unit": "points/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {k} of {len(pts)} points against all {w.n} voxels, fwd + bwd, "
+                      f"{reps} repetition(s), float64 numpy"}
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -206,6 +310,9 @@ def main():
         return
     if args.serialize:
         serialize_bench(args)
+        return
+    if args.grid_sample:
+        grid_sample_bench(args)
         return
 
     import numpy as np

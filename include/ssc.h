@@ -232,23 +232,26 @@ int ssc_decode_seq(const void* codes, int64_t n, int32_t B, int32_t X, int32_t Y
  *           the same B, X, Y, Z and key_bits: its voxel hash table is read.
  * C         channels; C * element bytes must be a multiple of 16, C <= 4096.
  * points    [m][4] float32, 16-byte aligned; m <= SSC_MAX_POINTS.
- * Accumulation is fp32 in corner order (fwd) and outputs are rounded to
- * nearest even.  The backward pass adds into an fp32 image of dfeats with
- * float atomics, so its summation order (and last bits) can vary from run
- * to run; for 16-bit types that image lives in the workspace.
+ * Accumulation is fp32 and outputs are rounded to nearest even.  The
+ * forward pass adds the corners in corner order.  The backward pass buckets
+ * the (point, corner) pairs by voxel with integer atomics and sums each
+ * voxel's bucket in the order the atomics placed it, so the last bits of
+ * dfeats can vary from run to run.
  * ------------------------------------------------------------------------ */
-#define SSC_MAX_POINTS (1LL << 30)
+#define SSC_MAX_POINTS (1LL << 28)
 
-/* Workspace bytes for ssc_grid_sample_bwd (at least 256); 0 for invalid
- * arguments. */
-size_t ssc_grid_sample_workspace_bytes(int64_t n, int32_t C, int32_t dtype);
+/* Workspace bytes ssc_grid_sample_bwd needs for n voxels and m points
+ * (about 8 n + 64 m); 0 for sizes out of range. */
+size_t ssc_grid_sample_workspace_bytes(int64_t n, int64_t m);
 
 /* out [m][C] (dtype), overwritten; feats [n][C].  n == 0 writes zeros. */
 int ssc_grid_sample_fwd(const void* plan, int64_t n, int32_t B, int32_t X, int32_t Y, int32_t Z,
                         int32_t key_bits, int32_t C, int32_t dtype, const void* feats, const float* points,
                         int64_t m, void* out, void* stream);
 
-/* dfeats [n][C] (dtype), overwritten; dout [m][C].  m == 0 writes zeros. */
+/* dfeats [n][C] (dtype), overwritten; dout [m][C]; workspace of
+ * ssc_grid_sample_workspace_bytes(n, m) bytes (unused when m == 0, which
+ * writes zeros). */
 int ssc_grid_sample_bwd(const void* plan, int64_t n, int32_t B, int32_t X, int32_t Y, int32_t Z,
                         int32_t key_bits, int32_t C, int32_t dtype, const float* points, int64_t m,
                         const void* dout, void* dfeats, void* workspace, size_t workspace_bytes,

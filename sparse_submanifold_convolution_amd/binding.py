@@ -35,7 +35,7 @@ SIGNATURES = {
     "ssc_seq_code_width": (_I32, [_I32, _I32, _I32, _I32]),
     "ssc_encode_seq": (ctypes.c_int, [_VP, _I64, _I32, _I32, _I32, _I32, _I32, _VP, _I32, _VP]),
     "ssc_decode_seq": (ctypes.c_int, [_VP, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _VP, _VP]),
-    "ssc_grid_sample_workspace_bytes": (_SZ, [_I64, _I32, _I32]),
+    "ssc_grid_sample_workspace_bytes": (_SZ, [_I64, _I64]),
     "ssc_grid_sample_fwd": (ctypes.c_int, [_VP, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _VP, _VP, _I64,
                                            _VP, _VP]),
     "ssc_grid_sample_bwd": (ctypes.c_int, [_VP, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _VP, _I64, _VP,
@@ -298,8 +298,9 @@ def decode_seq(codes: torch.Tensor, shape, mode: str = "z_order") -> torch.Tenso
 # sparse grid sampling
 # ---------------------------------------------------------------------------
 
-def grid_sample_workspace_bytes(n: int, c: int, dtype: torch.dtype) -> int:
-    return int(lib().ssc_grid_sample_workspace_bytes(int(n), int(c), DTYPE_CODE[dtype]))
+def grid_sample_workspace_bytes(n: int, m: int) -> int:
+    """Workspace bytes of grid_sample_bwd for n voxels and m points."""
+    return int(lib().ssc_grid_sample_workspace_bytes(int(n), int(m)))
 
 
 def grid_sample_fwd(plan: Plan, feats: torch.Tensor, points: torch.Tensor,
@@ -334,7 +335,7 @@ def grid_sample_bwd(plan: Plan, points: torch.Tensor, dout: torch.Tensor, dfeats
         dfeats = torch.empty((n, c), dtype=dt, device=dev)
     _need(dfeats, "dfeats", dt, (n, c), dev)
     if ws is None:
-        nbytes = grid_sample_workspace_bytes(n, c, dt)
+        nbytes = grid_sample_workspace_bytes(n, m)
         if nbytes == 0:
             raise SSCError("ssc_grid_sample_workspace_bytes", 2)
         ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)

@@ -19,9 +19,17 @@
 // same time and the group shares rows and weights through lane shuffles;
 // then each lane streams 16-byte vectors of the 8 corner rows (an absent
 // corner reads the plan's zero row, so the loads carry no branch) and
-// accumulates in fp32 in corner order.  The backward pass adds weight * dout
-// into an fp32 image of dfeats with hardware float atomics, then rounds it to
-// the element type; its summation order is therefore not fixed.
+// accumulates in fp32 in corner order.
+//
+// The backward pass is the same sum transposed.  Scattering weight * dout
+// into dfeats with float atomics costs one atomic per (point, corner,
+// channel) and is atomic-bound, so it gathers instead: the (point, corner)
+// pairs are bucketed by voxel with a counting sort (one integer atomic to
+// count and one to place each pair, a device-wide scan between them), then a
+// group of lanes per voxel walks its bucket, recomputes each pair's weight
+// from the point, gathers the dout rows and writes the voxel's gradient row
+// once.  The order of pairs inside a bucket follows the placing atomics, so
+// the fp32 summation order (and the last bits) may vary from run to run.
 
 #include <hip/hip_runtime.h>
 
@@ -94,28 +102,38 @@ struct GsGrid {
   int B, X, Y, Z;
 };
 
-// Corner j of point p: its voxel row (or the sentinel) and its weight (0 when
-// the corner is absent).
+// The weight of corner j of point p (any point whose corner j was found in
+// the table passed the range checks of corner_lookup).
+__device__ __forceinline__ float corner_weight(const float4 p, int j) {
+  const int dx = (j >> 2) & 1, dy = (j >> 1) & 1, dz = j & 1;
+  const float tx = p.y - floorf(p.y), ty = p.z - floorf(p.z), tz = p.w - floorf(p.w);
+  const float wx = dx ? tx : 1.f - tx, wy = dy ? ty : 1.f - ty, wz = dz ? tz : 1.f - tz;
+  return (wx * wy) * wz;
+}
+
+// Corner j of point p: its voxel row, or the sentinel when the point names
+// no sample, the corner is off the grid or no voxel sits there.
+template <typename KeyT>
+__device__ __forceinline__ uint32_t corner_row(const float4 p, int j, const GsGrid g,
+                                               const Slot<KeyT>* __restrict__ table, uint64_t capacity) {
+  // NaN fails every comparison below, so it lands here too
+  if (!(p.x >= 0.f && p.x < float(g.B) && p.x == floorf(p.x))) return kSentinel;
+  if (!(p.y > -1.f && p.y < float(g.X) && p.z > -1.f && p.z < float(g.Y) && p.w > -1.f && p.w < float(g.Z)))
+    return kSentinel;
+  const int cx = int(floorf(p.y)) + ((j >> 2) & 1);
+  const int cy = int(floorf(p.z)) + ((j >> 1) & 1);
+  const int cz = int(floorf(p.w)) + (j & 1);
+  if (cx < 0 || cx >= g.X || cy < 0 || cy >= g.Y || cz < 0 || cz >= g.Z) return kSentinel;
+  return hash_lookup<KeyT>(table, capacity, KeyT(pack_key(int(p.x), cx, cy, cz, g.X, g.Y, g.Z)));
+}
+
+// corner row and weight (0 when absent)
 template <typename KeyT>
 __device__ __forceinline__ void corner_lookup(const float4 p, int j, const GsGrid g,
                                               const Slot<KeyT>* __restrict__ table, uint64_t capacity,
                                               uint32_t* row, float* w) {
-  *row = kSentinel;
-  *w = 0.f;
-  // NaN fails every comparison below, so it lands here too
-  if (!(p.x >= 0.f && p.x < float(g.B) && p.x == floorf(p.x))) return;
-  if (!(p.y > -1.f && p.y < float(g.X) && p.z > -1.f && p.z < float(g.Y) && p.w > -1.f && p.w < float(g.Z)))
-    return;
-  const float fx = floorf(p.y), fy = floorf(p.z), fz = floorf(p.w);
-  const int dx = (j >> 2) & 1, dy = (j >> 1) & 1, dz = j & 1;
-  const int cx = int(fx) + dx, cy = int(fy) + dy, cz = int(fz) + dz;
-  if (cx < 0 || cx >= g.X || cy < 0 || cy >= g.Y || cz < 0 || cz >= g.Z) return;
-  const float tx = p.y - fx, ty = p.z - fy, tz = p.w - fz;
-  const float wx = dx ? tx : 1.f - tx, wy = dy ? ty : 1.f - ty, wz = dz ? tz : 1.f - tz;
-  const uint32_t r = hash_lookup<KeyT>(table, capacity, KeyT(pack_key(int(p.x), cx, cy, cz, g.X, g.Y, g.Z)));
-  if (r == kSentinel) return;
-  *row = r;
-  *w = (wx * wy) * wz;
+  *row = corner_row<KeyT>(p, j, g, table, capacity);
+  *w = *row == kSentinel ? 0.f : corner_weight(p, j);
 }
 
 // The 8 corners of the group's point, shared from the group's first 8 lanes.
@@ -167,29 +185,68 @@ __global__ void __launch_bounds__(256) gs_fwd(const u32x4* __restrict__ feats, c
   }
 }
 
-template <int DT, typename KeyT, int L>
-__global__ void __launch_bounds__(256) gs_bwd(const u32x4* __restrict__ dout, const float4* __restrict__ pts,
-                                              int64_t m, int nvec, const GsGrid g,
-                                              const Slot<KeyT>* __restrict__ table, uint64_t capacity,
-                                              float* __restrict__ acc) {
+// Backward, step 1: one thread per (point, corner) pair t = 8 p + j: the
+// corner's row into idx[t] and one count for that voxel.
+template <typename KeyT>
+__global__ void __launch_bounds__(256) gs_pairs(const float4* __restrict__ pts, int64_t m, const GsGrid g,
+                                                const Slot<KeyT>* __restrict__ table, uint64_t capacity,
+                                                uint32_t* __restrict__ idx, uint32_t* __restrict__ cnt) {
+  const int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (t >= m * 8) return;
+  const uint32_t r = corner_row<KeyT>(pts[t >> 3], int(t & 7), g, table, capacity);
+  idx[t] = r;
+  if (r != kSentinel) atomicAdd(&cnt[r], 1u);
+}
+
+// Backward, step 2 (after the scan turned the counts into bucket starts):
+// place each pair in its voxel's bucket.
+__global__ void __launch_bounds__(256) gs_place(const uint32_t* __restrict__ idx, int64_t pairs,
+                                                const uint32_t* __restrict__ start, uint32_t* __restrict__ fill,
+                                                uint32_t* __restrict__ list) {
+  const int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (t >= pairs) return;
+  const uint32_t r = idx[t];
+  if (r == kSentinel) return;
+  list[start[r] + atomicAdd(&fill[r], 1u)] = uint32_t(t);
+}
+
+// Backward, step 3: a group of L lanes per voxel sums weight * dout over its
+// bucket, four pairs at a time, and writes the voxel's gradient row.
+template <int DT, int L>
+__global__ void __launch_bounds__(256) gs_gather(const uint32_t* __restrict__ list,
+                                                 const uint32_t* __restrict__ start, int64_t n,
+                                                 const float4* __restrict__ pts, const u32x4* __restrict__ dout,
+                                                 int nvec, u32x4* __restrict__ dfeats) {
   using V = GsVec<DT>;
-  constexpr int kG = 256 / L;
-  const int64_t p = int64_t(blockIdx.x) * kG + threadIdx.x / L;
-  if (p >= m) return;
-  uint32_t rows[8];
-  float ws[8];
-  group_corners<KeyT, L>(pts, p, g, table, capacity, rows, ws);
-  const int64_t C = int64_t(nvec) * V::kVec;
+  constexpr int kG = 256 / L, kU = 4;
+  const int64_t i = int64_t(blockIdx.x) * kG + threadIdx.x / L;
+  if (i >= n) return;  // uniform over the group
+  const uint32_t b0 = start[i], b1 = start[i + 1];
   for (int v = int(threadIdx.x % L); v < nvec; v += L) {
-    float d[V::kVec];
-    V::unpack(dout[p * nvec + v], d);
+    float acc[V::kVec];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (rows[j] == kSentinel) continue;
-      float* dst = acc + int64_t(rows[j]) * C + int64_t(v) * V::kVec;
+    for (int e = 0; e < V::kVec; ++e) acc[e] = 0.f;
+    for (uint32_t k = b0; k < b1; k += kU) {
+      uint32_t t[kU];
 #pragma unroll
-      for (int e = 0; e < V::kVec; ++e) unsafeAtomicAdd(dst + e, ws[j] * d[e]);
+      for (int u = 0; u < kU; ++u) t[u] = list[k + u < b1 ? k + u : b1 - 1];
+      float4 p[kU];
+      u32x4 d[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        p[u] = pts[t[u] >> 3];
+        d[u] = dout[int64_t(t[u] >> 3) * nvec + v];
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const float w = k + u < b1 ? corner_weight(p[u], int(t[u] & 7)) : 0.f;
+        float f[V::kVec];
+        V::unpack(d[u], f);
+#pragma unroll
+        for (int e = 0; e < V::kVec; ++e) acc[e] = fmaf(w, f[e], acc[e]);
+      }
     }
+    dfeats[i * nvec + v] = V::pack(acc);
   }
 }
 
@@ -198,19 +255,6 @@ __global__ void __launch_bounds__(256) gs_bwd(const u32x4* __restrict__ dout, co
 __global__ void __launch_bounds__(256) gs_zero(u32x4* __restrict__ p, int64_t count) {
   const u32x4 z = {0u, 0u, 0u, 0u};
   for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < count; i += int64_t(gridDim.x) * 256) p[i] = z;
-}
-
-// dfeats = the fp32 sums rounded to the element type, 16 bytes out per thread
-template <int DT>
-__global__ void __launch_bounds__(256) gs_round(const float4* __restrict__ acc, int64_t nvec_total,
-                                                u32x4* __restrict__ dst) {
-  using V = GsVec<DT>;
-  static_assert(V::kVec == 8, "16-bit element types only");
-  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < nvec_total; i += int64_t(gridDim.x) * 256) {
-    const float4 a = acc[2 * i], b = acc[2 * i + 1];
-    const float f[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-    dst[i] = V::pack(f);
-  }
 }
 
 unsigned stream_grid(int64_t count) {
@@ -235,17 +279,18 @@ void launch_fwd(const void* feats, const float* pts, int64_t m, int nvec, GsGrid
   else gs_fwd<DT, KeyT, 64><<<grid, 256, 0, s>>>(f, p, m, nvec, g, table, capacity, z, o);
 }
 
-template <int DT, typename KeyT>
-void launch_bwd(const void* dout, const float* pts, int64_t m, int nvec, GsGrid g, const Slot<KeyT>* table,
-                uint64_t capacity, float* acc, hipStream_t s) {
+template <int DT>
+void launch_gather(const uint32_t* list, const uint32_t* start, int64_t n, const float* pts, const void* dout,
+                   int nvec, void* dfeats, hipStream_t s) {
   const int L = group_lanes(nvec);
-  const unsigned grid = unsigned((m + (256 / L) - 1) / (256 / L));
-  const u32x4* d = static_cast<const u32x4*>(dout);
+  const unsigned grid = unsigned((n + (256 / L) - 1) / (256 / L));
   const float4* p = reinterpret_cast<const float4*>(pts);
-  if (L == 8) gs_bwd<DT, KeyT, 8><<<grid, 256, 0, s>>>(d, p, m, nvec, g, table, capacity, acc);
-  else if (L == 16) gs_bwd<DT, KeyT, 16><<<grid, 256, 0, s>>>(d, p, m, nvec, g, table, capacity, acc);
-  else if (L == 32) gs_bwd<DT, KeyT, 32><<<grid, 256, 0, s>>>(d, p, m, nvec, g, table, capacity, acc);
-  else gs_bwd<DT, KeyT, 64><<<grid, 256, 0, s>>>(d, p, m, nvec, g, table, capacity, acc);
+  const u32x4* d = static_cast<const u32x4*>(dout);
+  u32x4* o = static_cast<u32x4*>(dfeats);
+  if (L == 8) gs_gather<DT, 8><<<grid, 256, 0, s>>>(list, start, n, p, d, nvec, o);
+  else if (L == 16) gs_gather<DT, 16><<<grid, 256, 0, s>>>(list, start, n, p, d, nvec, o);
+  else if (L == 32) gs_gather<DT, 32><<<grid, 256, 0, s>>>(list, start, n, p, d, nvec, o);
+  else gs_gather<DT, 64><<<grid, 256, 0, s>>>(list, start, n, p, d, nvec, o);
 }
 
 template <int DT>
@@ -260,15 +305,27 @@ void dispatch_fwd(int kb, const char* plan, const PlanLayout& L, const void* fea
                              L.capacity, zrow, out, s);
 }
 
-template <int DT>
-void dispatch_bwd(int kb, const char* plan, const PlanLayout& L, const void* dout, const float* pts, int64_t m,
-                  int nvec, GsGrid g, float* acc, hipStream_t s) {
-  if (kb == 64)
-    launch_bwd<DT, uint64_t>(dout, pts, m, nvec, g, reinterpret_cast<const Slot<uint64_t>*>(plan + L.table),
-                             L.capacity, acc, s);
-  else
-    launch_bwd<DT, uint32_t>(dout, pts, m, nvec, g, reinterpret_cast<const Slot<uint32_t>*>(plan + L.table),
-                             L.capacity, acc, s);
+// workspace of the backward pass: bucket starts (n + 1), fill counters (n),
+// the corner row of every pair (8 m), the buckets (8 m), the scan's scratch
+struct GsWs {
+  size_t start, fill, idx, list, tmp, total;
+};
+
+GsWs gs_ws_layout(int64_t n, int64_t m) {
+  GsWs w{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes, 256);
+    return o;
+  };
+  w.start = take(size_t(n + 1) * 4);
+  w.fill = take(size_t(n) * 4);
+  w.idx = take(size_t(m) * 32);
+  w.list = take(size_t(m) * 32);
+  w.tmp = take(size_t(scan_tmp_words(n + 1)) * 4);
+  w.total = off;
+  return w;
 }
 
 int esize(int32_t dtype) { return dtype == SSC_F32 ? 4 : 2; }
@@ -292,12 +349,9 @@ int gs_check(const void* plan, int64_t n, int32_t B, int32_t X, int32_t Y, int32
 
 using namespace ssc;
 
-extern "C" size_t ssc_grid_sample_workspace_bytes(int64_t n, int32_t C, int32_t dtype) {
-  if (n < 0 || n > SSC_MAX_VOXELS || C <= 0 || C > 4096) return 0;
-  if (dtype != SSC_F32 && dtype != SSC_F16 && dtype != SSC_BF16) return 0;
-  if ((int64_t(C) * esize(dtype)) % 16 != 0) return 0;
-  const size_t need = dtype == SSC_F32 ? 0 : size_t(n) * size_t(C) * 4;
-  return need < 256 ? 256 : align_up(need, 256);
+extern "C" size_t ssc_grid_sample_workspace_bytes(int64_t n, int64_t m) {
+  if (n < 0 || n > SSC_MAX_VOXELS || m < 0 || m > SSC_MAX_POINTS) return 0;
+  return gs_ws_layout(n, m).total;
 }
 
 extern "C" int ssc_grid_sample_fwd(const void* plan, int64_t n, int32_t B, int32_t X, int32_t Y, int32_t Z,
@@ -336,31 +390,41 @@ extern "C" int ssc_grid_sample_bwd(const void* plan, int64_t n, int32_t B, int32
   if (n == 0) return SSC_OK;
   if (!dfeats || !aligned16(dfeats)) return SSC_ERR_INVALID_ARG;
   if (m > 0 && (!points || !dout || !aligned16(points) || !aligned16(dout))) return SSC_ERR_INVALID_ARG;
-  const bool narrow = dtype != SSC_F32;
-  if (narrow && (!workspace || !aligned16(workspace))) return SSC_ERR_INVALID_ARG;
-  if (workspace_bytes < ssc_grid_sample_workspace_bytes(n, C, dtype) && narrow) return SSC_ERR_WORKSPACE;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int nvec = int(int64_t(C) * esize(dtype) / 16);
-  float* acc = narrow ? static_cast<float*>(workspace) : static_cast<float*>(dfeats);
-  const int64_t acc_vecs = n * int64_t(C) / 4;
   (void)hipGetLastError();
-  gs_zero<<<stream_grid(acc_vecs), 256, 0, s>>>(reinterpret_cast<u32x4*>(acc), acc_vecs);
-  if (m > 0) {
-    const PlanLayout L = plan_layout(n, kb);
-    const char* pl = static_cast<const char*>(plan);
-    const GsGrid g{B, X, Y, Z};
-    if (dtype == SSC_F32) dispatch_bwd<SSC_F32>(kb, pl, L, dout, points, m, nvec, g, acc, s);
-    else if (dtype == SSC_F16) dispatch_bwd<SSC_F16>(kb, pl, L, dout, points, m, nvec, g, acc, s);
-    else dispatch_bwd<SSC_BF16>(kb, pl, L, dout, points, m, nvec, g, acc, s);
+  if (m == 0) {
+    // no points: the gradient is zero
+    gs_zero<<<stream_grid(n * nvec), 256, 0, s>>>(static_cast<u32x4*>(dfeats), n * nvec);
+    return hipGetLastError() == hipSuccess ? SSC_OK : SSC_ERR_HIP;
   }
-  if (narrow) {
-    const int64_t out_vecs = n * int64_t(nvec);
-    if (dtype == SSC_F16)
-      gs_round<SSC_F16><<<stream_grid(out_vecs), 256, 0, s>>>(reinterpret_cast<const float4*>(acc), out_vecs,
-                                                              static_cast<u32x4*>(dfeats));
-    else
-      gs_round<SSC_BF16><<<stream_grid(out_vecs), 256, 0, s>>>(reinterpret_cast<const float4*>(acc), out_vecs,
-                                                               static_cast<u32x4*>(dfeats));
-  }
+  if (!workspace || !aligned16(workspace)) return SSC_ERR_INVALID_ARG;
+  const GsWs W = gs_ws_layout(n, m);
+  if (workspace_bytes < W.total) return SSC_ERR_WORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  uint32_t* start = reinterpret_cast<uint32_t*>(ws + W.start);
+  uint32_t* fill = reinterpret_cast<uint32_t*>(ws + W.fill);
+  uint32_t* idx = reinterpret_cast<uint32_t*>(ws + W.idx);
+  uint32_t* list = reinterpret_cast<uint32_t*>(ws + W.list);
+  uint32_t* tmp = reinterpret_cast<uint32_t*>(ws + W.tmp);
+  // start and fill are adjacent regions: one zero launch covers both
+  const int64_t zvecs = int64_t((W.idx - W.start) / 16);
+  gs_zero<<<stream_grid(zvecs), 256, 0, s>>>(reinterpret_cast<u32x4*>(start), zvecs);
+  const PlanLayout L = plan_layout(n, kb);
+  const char* pl = static_cast<const char*>(plan);
+  const GsGrid g{B, X, Y, Z};
+  const float4* p4 = reinterpret_cast<const float4*>(points);
+  const unsigned pgrid = unsigned((m * 8 + 255) / 256);
+  if (kb == 64)
+    gs_pairs<uint64_t><<<pgrid, 256, 0, s>>>(p4, m, g, reinterpret_cast<const Slot<uint64_t>*>(pl + L.table),
+                                            L.capacity, idx, start);
+  else
+    gs_pairs<uint32_t><<<pgrid, 256, 0, s>>>(p4, m, g, reinterpret_cast<const Slot<uint32_t>*>(pl + L.table),
+                                            L.capacity, idx, start);
+  launch_scan(start, n + 1, tmp, s);
+  gs_place<<<pgrid, 256, 0, s>>>(idx, m * 8, start, fill, list);
+  if (dtype == SSC_F32) launch_gather<SSC_F32>(list, start, n, points, dout, nvec, dfeats, s);
+  else if (dtype == SSC_F16) launch_gather<SSC_F16>(list, start, n, points, dout, nvec, dfeats, s);
+  else launch_gather<SSC_BF16>(list, start, n, points, dout, nvec, dfeats, s);
   return hipGetLastError() == hipSuccess ? SSC_OK : SSC_ERR_HIP;
 }

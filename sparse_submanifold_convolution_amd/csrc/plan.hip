@@ -125,7 +125,7 @@ __global__ void __launch_bounds__(kScanThreads) scan_apply(uint32_t* __restrict_
   }
 }
 
-static void launch_scan(uint32_t* data, int64_t len, uint32_t* tmp, hipStream_t s) {
+void launch_scan(uint32_t* data, int64_t len, uint32_t* tmp, hipStream_t s) {
   if (len <= 0) return;
   const int64_t nb = (len + kScanBlock - 1) / kScanBlock;
   scan_reduce<<<dim3(unsigned(nb)), dim3(kScanThreads), 0, s>>>(data, len, tmp);

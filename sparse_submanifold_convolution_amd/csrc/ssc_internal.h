@@ -42,6 +42,11 @@ constexpr int kScanThreads = 256;
 constexpr int kScanItems = 16;
 constexpr int kScanBlock = kScanThreads * kScanItems;
 
+// In-place exclusive scan of len uint32 on stream s (three launches); tmp
+// holds ceil(len / kScanBlock) + 1 words.  Defined with the plan builder.
+void launch_scan(uint32_t* data, int64_t len, uint32_t* tmp, hipStream_t s);
+inline int64_t scan_tmp_words(int64_t len) { return (len + kScanBlock - 1) / kScanBlock + 1; }
+
 struct PlanHeader {
   uint32_t magic;
   uint32_t status_bits;

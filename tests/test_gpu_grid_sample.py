@@ -1,8 +1,9 @@
 """GPU parity of ssc_grid_sample_fwd / ssc_grid_sample_bwd against the grid-sampling oracle.
 
 Tolerance as for the convolution: max|err| / max|ref| <= 1e-5 for fp32 and
-2e-2 for fp16 / bf16 inputs with fp32 accumulation (the backward pass adds
-with float atomics, so its last bits may differ between runs).
+2e-2 for fp16 / bf16 inputs with fp32 accumulation (the backward pass sums
+each voxel's bucket in the order integer atomics placed it, so its last bits
+may differ between runs).
 """
 import numpy as np
 import pytest
