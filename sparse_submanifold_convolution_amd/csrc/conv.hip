@@ -1034,8 +1034,17 @@ __global__ void __launch_bounds__(256) wgrad_reduce(const float* __restrict__ pa
   const int64_t pk = hdr->pair_count[k];
   const int nch = rowmode ? max_chunks : int((pk + chunk_len - 1) / chunk_len);
   const float* src = partial + int64_t(k) * max_chunks * cico + e;
+  // chunks added in increasing order, eight loads in flight
   float s = 0.f;
-  for (int c = 0; c < nch; ++c) s += src[int64_t(c) * cico];
+  int c = 0;
+  for (; c + 8 <= nch; c += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = src[int64_t(c + u) * cico];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s += v[u];
+  }
+  for (; c < nch; ++c) s += src[int64_t(c) * cico];
   dW[int64_t(k) * cico + e] = Elt<T>::store(s);
 }
 
