@@ -78,11 +78,18 @@ __global__ void __launch_bounds__(kScanThreads) scan_reduce(const uint32_t* __re
                                                             int64_t len, uint32_t* __restrict__ tmp) {
   __shared__ uint32_t waves[kScanThreads / 64];
   const int64_t base = int64_t(blockIdx.x) * kScanBlock;
-  uint32_t s = 0;
+  // all loads issued before the first use (clamped in range, masked after):
+  // a load under a branch would wait for each one in turn
+  uint32_t v[kScanItems];
+#pragma unroll
   for (int e = 0; e < kScanItems; ++e) {
-    int64_t idx = base + int64_t(e) * kScanThreads + threadIdx.x;
-    if (idx < len) s += data[idx];
+    const int64_t idx = base + int64_t(e) * kScanThreads + threadIdx.x;
+    v[e] = data[idx < len ? idx : len - 1];
   }
+  uint32_t s = 0;
+#pragma unroll
+  for (int e = 0; e < kScanItems; ++e)
+    s += (base + int64_t(e) * kScanThreads + threadIdx.x < len) ? v[e] : 0u;
   uint32_t excl;
   uint32_t total = block_exclusive_scan(s, waves, &excl);
   if (threadIdx.x == 0) tmp[blockIdx.x] = total;
@@ -110,8 +117,12 @@ __global__ void __launch_bounds__(kScanThreads) scan_apply(uint32_t* __restrict_
   uint32_t s = 0;
 #pragma unroll
   for (int e = 0; e < kScanItems; ++e) {
-    int64_t idx = base + e;
-    v[e] = idx < len ? data[idx] : 0u;
+    const int64_t idx = base + e;
+    v[e] = data[idx < len ? idx : len - 1];
+  }
+#pragma unroll
+  for (int e = 0; e < kScanItems; ++e) {
+    v[e] = base + e < len ? v[e] : 0u;
     s += v[e];
   }
   uint32_t excl;
@@ -323,10 +334,15 @@ __global__ void __launch_bounds__(kSortThreads) radix_hist(const uint64_t* __res
   cnt[threadIdx.x] = 0;
   __syncthreads();
   const int64_t base = int64_t(blockIdx.x) * kSortThreads * ITEMS;
-  for (int q = 0; q < ITEMS; ++q) {
+  uint64_t k[ITEMS];
+#pragma unroll
+  for (int q = 0; q < ITEMS; ++q) {  // every load before the first use, as in the scan
     const int64_t idx = base + int64_t(q) * kSortThreads + threadIdx.x;
-    if (idx < n) atomicAdd(&cnt[(keys[idx] >> shift) & 255u], 1u);
+    k[q] = keys[idx < n ? idx : n - 1];
   }
+#pragma unroll
+  for (int q = 0; q < ITEMS; ++q)
+    if (base + int64_t(q) * kSortThreads + threadIdx.x < n) atomicAdd(&cnt[(k[q] >> shift) & 255u], 1u);
   __syncthreads();
   hist[int64_t(threadIdx.x) * nblk + blockIdx.x] = cnt[threadIdx.x];
   if (blockIdx.x == 0 && threadIdx.x == 0) hist[256 * nblk] = 0;
