@@ -257,6 +257,116 @@ int ssc_grid_sample_bwd(const void* plan, int64_t n, int32_t B, int32_t X, int32
                         const void* dout, void* dfeats, void* workspace, size_t workspace_bytes,
                         void* stream);
 
+/* ------------------------------------------------------------------------
+ * Strided (generalised) sparse convolution: the regular sparse_conv3d of
+ * the report, whose output sites differ from its input sites and whose map
+ * comes from its own sparse_neighbor_map primitive (section two: the
+ * ops.spconv and kernels.cuda.spconv module rows; the sparse_conv3d,
+ * sparse_conv_[masked_]implicit_gemm[_splitk] and subm / sparse
+ * neighbor_map key-function rows).  The same masked implicit GEMM runs it.
+ *
+ * Geometry, the same on every axis: kernel side ks in {1, 2, 3} (V = ks^3
+ * offsets), stride s in [1, 64], padding p in [0, ks).  Offset
+ * k = (a*ks + b)*ks + c for window position (a, b, c) in [0, ks)^3 on
+ * (x, y, z).  The output grid is (B, Xo, Yo, Zo), Xo = (X + 2p - ks)/s + 1
+ * (integer division; every side must be >= 1).  Output site o meets the
+ * input site o*s - p + (a, b, c) of the same sample:
+ *   nmap[o][k] = row of that input voxel, or S (absent, or off the input
+ *                grid); columns k >= V are always S;
+ *   out[o]     = bias + sum_{k: nmap[o][k] != S} X[nmap[o][k]] @ W[k];
+ *   dX[j]      = sum over (o, k) with nmap[o][k] = j of W[k] @ dY[o];
+ *   dW[k]      = sum_o outer(X[nmap[o][k]], dY[o]);  dbias = sum_o dY[o];
+ * with W [V][Ci][Co].  With ks = 3, s = 1, p = 1 and the input sites given
+ * as the output sites this is the submanifold convolution above.
+ * ------------------------------------------------------------------------ */
+
+/* Output-grid sides for this geometry into dims_host[4] (host pointer:
+ * B, Xo, Yo, Zo).  Returns SSC_ERR_INVALID_ARG for a bad grid or geometry.
+ * Needs no GPU. */
+int ssc_sparse_out_shape(int32_t B, int32_t X, int32_t Y, int32_t Z, int32_t ks, int32_t stride, int32_t pad,
+                         int32_t* dims_host);
+
+/* Workspace bytes of ssc_sparse_out_count / ssc_sparse_out_coords: one bit
+ * per output-grid site plus a count per 32 sites (about B*Xo*Yo*Zo / 4
+ * bytes); 0 for invalid arguments or an output grid above 2^38 sites. */
+size_t ssc_sparse_out_workspace_bytes(int32_t B, int32_t X, int32_t Y, int32_t Z, int32_t ks, int32_t stride,
+                                      int32_t pad);
+
+/*
+ * Active output sites, step 1: mark every output site whose window holds
+ * an active input (one bit per site), count them and write the count to
+ * *count (one int64 in device memory).  coords [n_in][4] int32 rows
+ * (b, x, y, z), read-only.  A coordinate outside the input grid makes the
+ * count -1.  The caller reads the count, allocates [count][4], then calls
+ * ssc_sparse_out_coords with the same workspace, grid and geometry.
+ */
+int ssc_sparse_out_count(const int32_t* coords, int64_t n_in, int32_t B, int32_t X, int32_t Y, int32_t Z,
+                         int32_t ks, int32_t stride, int32_t pad, void* workspace, size_t workspace_bytes,
+                         int64_t* count, void* stream);
+
+/* Active output sites, step 2: out_coords [n_out][4] int32, out, in
+ * ascending lexicographic (b, x, y, z) order; n_out must be the count of
+ * step 1. */
+int ssc_sparse_out_coords(const void* workspace, size_t workspace_bytes, int32_t B, int32_t X, int32_t Y,
+                          int32_t Z, int32_t ks, int32_t stride, int32_t pad, int32_t* out_coords, int64_t n_out,
+                          void* stream);
+
+/* Bytes of a strided-conv plan for n_in input and n_out output rows (the
+ * key width rule of ssc_plan_bytes applied to each grid); 0 for invalid
+ * arguments.  Needs no GPU. */
+size_t ssc_sparse_plan_bytes(int64_t n_in, int64_t n_out, int32_t B, int32_t X, int32_t Y, int32_t Z,
+                             int32_t ks, int32_t stride, int32_t pad, int32_t key_bits);
+
+/*
+ * Build the strided-conv map and its neighbour cache (sparse_neighbor_map).
+ *   coords_in  [n_in][4] int32 input sites in grid (B, X, Y, Z), any order.
+ *   coords_out [n_out][4] int32 output sites in the output grid, any order
+ *              (from ssc_sparse_out_coords, or the caller's own set).
+ *   nmap       [n_out][27] uint32, out, as defined above.
+ *   perm_out   [n_out] int32, out: the output rows ascending by (mask,
+ *              z-order key over the output grid), as perm of the
+ *              submanifold build.
+ *   plan       ssc_sparse_plan_bytes(...) bytes, out.  It also holds the
+ *              transposed map (per input row, the outputs it feeds, column
+ *              26 - k for offset k) in its own GEMM order, which the input
+ *              gradient walks.
+ * Both coordinate sets must be unique and inside their grids;
+ * ssc_sparse_plan_status reports device-detected problems.
+ */
+int ssc_build_sparse_map(const int32_t* coords_in, int64_t n_in, int32_t B, int32_t X, int32_t Y, int32_t Z,
+                         const int32_t* coords_out, int64_t n_out, int32_t ks, int32_t stride, int32_t pad,
+                         int32_t key_bits, uint32_t* nmap, int32_t* perm_out, void* plan, size_t plan_bytes,
+                         void* stream);
+
+/* As ssc_plan_status, for a strided-conv plan of n_out output rows: the
+ * first problem of the output sites, else of the input sites. */
+int ssc_sparse_plan_status(const void* plan, int64_t n_out, void* stream, int32_t* status_host);
+
+/* Workspace bytes of ssc_sparse_conv3d_fwd / _bwd; 0 for invalid or
+ * unsupported arguments.  Needs no GPU. */
+size_t ssc_sparse_conv_workspace_bytes(int64_t n_in, int64_t n_out, int32_t Ci, int32_t Co, int32_t dtype);
+
+/*
+ * Forward pass: out [n_out][Co] = the definition above.  plan and perm_out
+ * from ssc_build_sparse_map with these n_in, n_out and ks; feats
+ * [n_in][Ci], weight [V][Ci][Co], bias [Co] or NULL, all `dtype`.  Channel
+ * rules, rounding and kernels as ssc_subm_conv3d_fwd.
+ */
+int ssc_sparse_conv3d_fwd(const void* plan, int64_t n_in, int64_t n_out, int32_t ks, const int32_t* perm_out,
+                          int32_t Ci, int32_t Co, int32_t dtype, const void* feats, const void* weight,
+                          const void* bias, void* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Backward pass; each output may be NULL to skip it: dfeats [n_in][Ci] = dX
+ * (the masked implicit GEMM over the input rows through the transposed
+ * map), dweight [V][Ci][Co] = dW (pair-list Split-K, deterministic), dbias
+ * [Co].  dout [n_out][Co].  All `dtype`, fp32 accumulation.
+ */
+int ssc_sparse_conv3d_bwd(const void* plan, int64_t n_in, int64_t n_out, int32_t ks, const int32_t* perm_out,
+                          int32_t Ci, int32_t Co, int32_t dtype, const void* feats, const void* weight,
+                          const void* dout, void* dfeats, void* dweight, void* dbias, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
 /* Static, human-readable name of a status code (host only). */
 const char* ssc_status_string(int status);
 

@@ -40,6 +40,20 @@ SIGNATURES = {
                                            _VP, _VP]),
     "ssc_grid_sample_bwd": (ctypes.c_int, [_VP, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _VP, _I64, _VP,
                                            _VP, _VP, _SZ, _VP]),
+    "ssc_sparse_out_shape": (ctypes.c_int, [_I32, _I32, _I32, _I32, _I32, _I32, _I32, ctypes.POINTER(_I32)]),
+    "ssc_sparse_out_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32, _I32]),
+    "ssc_sparse_out_count": (ctypes.c_int, [_VP, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _VP, _SZ, _VP,
+                                            _VP]),
+    "ssc_sparse_out_coords": (ctypes.c_int, [_VP, _SZ, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _VP, _I64, _VP]),
+    "ssc_sparse_plan_bytes": (_SZ, [_I64, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32]),
+    "ssc_build_sparse_map": (ctypes.c_int, [_VP, _I64, _I32, _I32, _I32, _I32, _VP, _I64, _I32, _I32, _I32, _I32,
+                                            _VP, _VP, _VP, _SZ, _VP]),
+    "ssc_sparse_plan_status": (ctypes.c_int, [_VP, _I64, _VP, ctypes.POINTER(_I32)]),
+    "ssc_sparse_conv_workspace_bytes": (_SZ, [_I64, _I64, _I32, _I32, _I32]),
+    "ssc_sparse_conv3d_fwd": (ctypes.c_int, [_VP, _I64, _I64, _I32, _VP, _I32, _I32, _I32, _VP, _VP, _VP, _VP, _VP,
+                                             _SZ, _VP]),
+    "ssc_sparse_conv3d_bwd": (ctypes.c_int, [_VP, _I64, _I64, _I32, _VP, _I32, _I32, _I32, _VP, _VP, _VP, _VP, _VP,
+                                             _VP, _VP, _SZ, _VP]),
 }
 
 SEQ_MODES = {"z_order": 0, "hilbert": 1}
@@ -236,6 +250,177 @@ class SubmConv3dFunction(torch.autograd.Function):
 def subm_conv3d(feats: torch.Tensor, plan: Plan, weight: torch.Tensor, bias: torch.Tensor | None = None):
     """Differentiable submanifold convolution over a built plan."""
     return SubmConv3dFunction.apply(feats, weight, bias, plan)
+
+
+# ---------------------------------------------------------------------------
+# strided (generalised) sparse convolution
+# ---------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class SparsePlan:
+    """Output sites, map and neighbour cache of a strided convolution over one input coordinate set."""
+    out_coords: torch.Tensor  # [n_out, 4] int32
+    nmap: torch.Tensor        # [n_out, 27] uint32 bits (int32)
+    perm: torch.Tensor        # [n_out] int32: GEMM order of the output rows
+    buf: torch.Tensor         # plan buffer (uint8)
+    n_in: int
+    n_out: int
+    shape: tuple              # input grid (B, X, Y, Z)
+    out_shape: tuple          # output grid (B, Xo, Yo, Zo)
+    ks: int
+    stride: int
+    pad: int
+
+    @property
+    def device(self) -> torch.device:
+        return self.buf.device
+
+
+def sparse_out_shape(shape, ks: int, stride: int, pad: int) -> tuple:
+    B, X, Y, Z = (int(s) for s in shape)
+    dims = (ctypes.c_int32 * 4)()
+    _check("ssc_sparse_out_shape", lib().ssc_sparse_out_shape(B, X, Y, Z, int(ks), int(stride), int(pad), dims))
+    return tuple(int(d) for d in dims)
+
+
+def sparse_out_coords(coords: torch.Tensor, shape, ks: int, stride: int, pad: int) -> torch.Tensor:
+    """Active output sites (lexicographic order) of a strided convolution; reads the count on the host."""
+    dev = coords.device
+    n = int(coords.shape[0])
+    _need(coords, "coords", torch.int32, (n, 4), dev)
+    B, X, Y, Z = (int(s) for s in shape)
+    geo = (int(ks), int(stride), int(pad))
+    nbytes = int(lib().ssc_sparse_out_workspace_bytes(B, X, Y, Z, *geo))
+    if nbytes == 0:
+        raise SSCError("ssc_sparse_out_workspace_bytes", 1)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    count = torch.empty(1, dtype=torch.int64, device=dev)
+    _check("ssc_sparse_out_count", lib().ssc_sparse_out_count(_ptr(coords), n, B, X, Y, Z, *geo, _ptr(ws), nbytes,
+                                                              _ptr(count), _stream(dev)))
+    n_out = int(count.item())
+    if n_out < 0:
+        raise SSCError("ssc_sparse_out_count (device)", 5)
+    out = torch.empty((n_out, 4), dtype=torch.int32, device=dev)
+    _check("ssc_sparse_out_coords", lib().ssc_sparse_out_coords(_ptr(ws), nbytes, B, X, Y, Z, *geo, _ptr(out),
+                                                                n_out, _stream(dev)))
+    return out
+
+
+def build_sparse_map(coords: torch.Tensor, shape, ks: int, stride: int, pad: int,
+                     out_coords: torch.Tensor | None = None, key_bits: int = 0, check: bool = True) -> SparsePlan:
+    """sparse_neighbor_map: output sites (generated unless given), the map and the plan; raises on any error."""
+    dev = coords.device
+    n_in = int(coords.shape[0])
+    _need(coords, "coords", torch.int32, (n_in, 4), dev)
+    oshape = sparse_out_shape(shape, ks, stride, pad)
+    if out_coords is None:
+        out_coords = sparse_out_coords(coords, shape, ks, stride, pad)
+    n_out = int(out_coords.shape[0])
+    _need(out_coords, "out_coords", torch.int32, (n_out, 4), dev)
+    B, X, Y, Z = (int(s) for s in shape)
+    geo = (int(ks), int(stride), int(pad))
+    nbytes = int(lib().ssc_sparse_plan_bytes(n_in, n_out, B, X, Y, Z, *geo, int(key_bits)))
+    if nbytes == 0:
+        raise SSCError("ssc_sparse_plan_bytes", 1)
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    nmap = torch.empty((n_out, 27), dtype=torch.int32, device=dev)
+    perm = torch.empty((n_out,), dtype=torch.int32, device=dev)
+    _check("ssc_build_sparse_map",
+           lib().ssc_build_sparse_map(_ptr(coords), n_in, B, X, Y, Z, _ptr(out_coords), n_out, *geo, int(key_bits),
+                                      _ptr(nmap), _ptr(perm), _ptr(buf), nbytes, _stream(dev)))
+    plan = SparsePlan(out_coords, nmap, perm, buf, n_in, n_out, (B, X, Y, Z), oshape, *geo)
+    if check:
+        st = sparse_plan_status(plan)
+        if st != SSC_OK:
+            raise SSCError("ssc_build_sparse_map (device)", st)
+    return plan
+
+
+def sparse_plan_status(plan: SparsePlan) -> int:
+    out = ctypes.c_int32(-1)
+    _check("ssc_sparse_plan_status", lib().ssc_sparse_plan_status(_ptr(plan.buf), plan.n_out, _stream(plan.device),
+                                                                  ctypes.byref(out)))
+    return int(out.value)
+
+
+def sparse_workspace(plan: SparsePlan, ci: int, co: int, dtype: torch.dtype) -> torch.Tensor:
+    nbytes = int(lib().ssc_sparse_conv_workspace_bytes(plan.n_in, plan.n_out, int(ci), int(co), DTYPE_CODE[dtype]))
+    if nbytes == 0:
+        raise SSCError("ssc_sparse_conv_workspace_bytes", 2)
+    return torch.empty(nbytes, dtype=torch.uint8, device=plan.device)
+
+
+def sparse_conv3d_fwd(plan: SparsePlan, feats: torch.Tensor, weight: torch.Tensor,
+                      bias: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                      ws: torch.Tensor | None = None) -> torch.Tensor:
+    dev, dt = plan.device, feats.dtype
+    ci, co = int(weight.shape[1]), int(weight.shape[2])
+    if dt not in DTYPE_CODE:
+        raise SSCError("ssc_sparse_conv3d_fwd", 2)
+    _need(feats, "feats", dt, (plan.n_in, ci), dev)
+    _need(weight, "weight", dt, (plan.ks ** 3, ci, co), dev)
+    if bias is not None:
+        _need(bias, "bias", dt, (co,), dev)
+    if out is None:
+        out = torch.empty((plan.n_out, co), dtype=dt, device=dev)
+    _need(out, "out", dt, (plan.n_out, co), dev)
+    if ws is None:
+        ws = sparse_workspace(plan, ci, co, dt)
+    _check("ssc_sparse_conv3d_fwd",
+           lib().ssc_sparse_conv3d_fwd(_ptr(plan.buf), plan.n_in, plan.n_out, plan.ks, _ptr(plan.perm), ci, co,
+                                       DTYPE_CODE[dt], _ptr(feats), _ptr(weight), _ptr(bias), _ptr(out), _ptr(ws),
+                                       ws.numel(), _stream(dev)))
+    return out
+
+
+def sparse_conv3d_bwd(plan: SparsePlan, feats: torch.Tensor, weight: torch.Tensor, dout: torch.Tensor,
+                      need_dfeats: bool = True, need_dweight: bool = True, need_dbias: bool = True,
+                      ws: torch.Tensor | None = None, outs: tuple | None = None):
+    """Returns (dfeats, dweight, dbias); entries not asked for are None."""
+    dev, dt = plan.device, dout.dtype
+    ci, co = int(weight.shape[1]), int(weight.shape[2])
+    V = plan.ks ** 3
+    _need(feats, "feats", dt, (plan.n_in, ci), dev)
+    _need(weight, "weight", dt, (V, ci, co), dev)
+    _need(dout, "dout", dt, (plan.n_out, co), dev)
+    if outs is not None:
+        dX, dW, db = outs
+    else:
+        dX = torch.empty((plan.n_in, ci), dtype=dt, device=dev) if need_dfeats else None
+        dW = torch.empty((V, ci, co), dtype=dt, device=dev) if need_dweight else None
+        db = torch.empty((co,), dtype=dt, device=dev) if need_dbias else None
+    if ws is None:
+        ws = sparse_workspace(plan, ci, co, dt)
+    _check("ssc_sparse_conv3d_bwd",
+           lib().ssc_sparse_conv3d_bwd(_ptr(plan.buf), plan.n_in, plan.n_out, plan.ks, _ptr(plan.perm), ci, co,
+                                       DTYPE_CODE[dt], _ptr(feats), _ptr(weight), _ptr(dout), _ptr(dX), _ptr(dW),
+                                       _ptr(db), _ptr(ws), ws.numel(), _stream(dev)))
+    return dX, dW, db
+
+
+class SparseConv3dFunction(torch.autograd.Function):
+    """autograd wrapper: forward = ssc_sparse_conv3d_fwd, backward = ssc_sparse_conv3d_bwd."""
+
+    @staticmethod
+    def forward(ctx, feats, weight, bias, plan):
+        ctx.plan = plan
+        ctx.has_bias = bias is not None
+        ctx.save_for_backward(feats, weight)
+        return sparse_conv3d_fwd(plan, feats.contiguous(), weight.contiguous(),
+                                 None if bias is None else bias.contiguous())
+
+    @staticmethod
+    def backward(ctx, dout):
+        feats, weight = ctx.saved_tensors
+        dX, dW, db = sparse_conv3d_bwd(ctx.plan, feats, weight, dout.contiguous(),
+                                       need_dfeats=ctx.needs_input_grad[0], need_dweight=ctx.needs_input_grad[1],
+                                       need_dbias=ctx.has_bias and ctx.needs_input_grad[2])
+        return dX, dW, db, None
+
+
+def sparse_conv3d(feats: torch.Tensor, plan: SparsePlan, weight: torch.Tensor, bias: torch.Tensor | None = None):
+    """Differentiable strided sparse convolution over a built plan (outputs at plan.out_coords)."""
+    return SparseConv3dFunction.apply(feats, weight, bias, plan)
 
 
 # ---------------------------------------------------------------------------

@@ -813,7 +813,7 @@ __global__ void __launch_bounds__(64 * NWM * NWN)
              const uint32_t* __restrict__ pair_j, const PlanHeader* __restrict__ hdr, float* __restrict__ partial,
              int Ci, int Co, int64_t chunk_len, int max_chunks, int ntiles_m, int ntiles_n,
              const uint32_t* __restrict__ pseg, int pblk, int rows_bpc, const T* __restrict__ zrow,
-             BiasJob<T> bj) {
+             BiasJob<T> bj, int nk) {
   using C = WgradTrCfg<T, FM, FN, NWM, NWN, BKP>;
   using E = Elt<T>;
   using frag_t = typename E::frag_t;
@@ -838,11 +838,11 @@ __global__ void __launch_bounds__(64 * NWM * NWN)
   if (rows_bpc > 0) {
     // Row-range chunks (narrow layers): chunk c holds the pairs of every offset
     // whose output row lies in blocks [c*bpc, (c+1)*bpc) of kPairRows rows.  The
-    // 27 offsets of one chunk run together on one XCD and share its dY rows and
+    // nk offsets of one chunk run together on one XCD and share its dY rows and
     // their neighbours' X rows in L2.  Empty segments still write zeros.
     const int nmn = ntiles_m * ntiles_n;
     int m;
-    if (!xcd_group_work(max_chunks, kV * nmn, &chunk, &m)) return;
+    if (!xcd_group_work(max_chunks, nk * nmn, &chunk, &m)) return;
     k = m / nmn;
     mn = m % nmn;
     const int b0 = chunk * rows_bpc, b1 = (b0 + rows_bpc < pblk) ? b0 + rows_bpc : pblk;
@@ -853,9 +853,9 @@ __global__ void __launch_bounds__(64 * NWM * NWN)
     // on one XCD, so the pair rows they all gather are shared in its L2; groups
     // cycle through the offsets first so every XCD gets dense and sparse ones.
     int g;
-    if (!xcd_group_work(kV * max_chunks, ntiles_m * ntiles_n, &g, &mn)) return;
-    k = g % kV;
-    chunk = g / kV;
+    if (!xcd_group_work(nk * max_chunks, ntiles_m * ntiles_n, &g, &mn)) return;
+    k = g % nk;
+    chunk = g / nk;
     const int64_t pk = hdr->pair_count[k];
     const int64_t start = int64_t(chunk) * chunk_len;
     if (start >= pk) return;
@@ -1023,9 +1023,9 @@ __global__ void __launch_bounds__(256) wgrad_reduce(const float* __restrict__ pa
                                                     const PlanHeader* __restrict__ hdr, T* __restrict__ dW,
                                                     int64_t cico, int64_t chunk_len, int max_chunks, int rowmode,
                                                     const float* __restrict__ bias_part, int bias_nb, int Co,
-                                                    T* __restrict__ dbias) {
+                                                    T* __restrict__ dbias, int nk) {
   const int k = blockIdx.y;
-  if (k == kV) {  // row kV of the grid: dbias stage 2, when the stage-1 partials ride along
+  if (k == nk) {  // row nk of the grid: dbias stage 2, when the stage-1 partials ride along
     if (int(blockIdx.x) * 16 < Co) colsum_final_block<T>(blockIdx.x, bias_part, bias_nb, Co, dbias);
     return;
   }
@@ -1240,18 +1240,18 @@ static inline int colsum_groups(int Co, int esize) {
 template <typename T>
 static bool launch_wgrad(const T* X, const T* dY, const uint32_t* pi, const uint32_t* pj, const PlanHeader* h,
                          const uint32_t* pseg, const T* zrow, float* partial, int64_t n, int Ci, int Co,
-                         const BwdShape& b, float* bias_part, hipStream_t s) {
-  dim3 grid(unsigned(b.max_chunks), kV, unsigned(b.mt * b.nt));
+                         const BwdShape& b, float* bias_part, int nk, hipStream_t s) {
+  dim3 grid(unsigned(b.max_chunks), unsigned(nk), unsigned(b.mt * b.nt));
   if constexpr (sizeof(T) == 2) {
-    const unsigned nwg = b.rows_bpc > 0 ? xcd_group_grid(b.max_chunks, kV * b.mt * b.nt)
-                                        : xcd_group_grid(kV * b.max_chunks, b.mt * b.nt);
+    const unsigned nwg = b.rows_bpc > 0 ? xcd_group_grid(b.max_chunks, nk * b.mt * b.nt)
+                                        : xcd_group_grid(nk * b.max_chunks, b.mt * b.nt);
     BiasJob<T> bj{dY, n, b.bias_rows, Co, colsum_cvb(Co, 2), b.bias_blocks, nwg, bias_part};
     const unsigned nbias = bias_part ? unsigned(b.bias_blocks) * unsigned(colsum_groups(Co, 2)) : 0u;
     const dim3 grid1(nwg + nbias);
 #define SSC_WTR(FM, FN, NWM, NWN)                                                                        \
   wgrad_tr<T, FM, FN, NWM, NWN, 32, 2><<<grid1, 64 * NWM * NWN, 0, s>>>(X, dY, pi, pj, h, partial, Ci, Co, \
                                                                        b.chunk_len, b.max_chunks, b.mt, b.nt, \
-                                                                       pseg, b.pblk, b.rows_bpc, zrow, bj)
+                                                                       pseg, b.pblk, b.rows_bpc, zrow, bj, nk)
     if (b.bm == 256) SSC_WTR(2, 4, 4, 2);
     else if (b.bm == 128) SSC_WTR(2, 2, 2, 2);
     else if (b.bm == 64) SSC_WTR(1, 1, 2, 2);
@@ -1290,56 +1290,98 @@ static bool launch_wgrad(const T* X, const T* dY, const uint32_t* pi, const uint
   return false;
 }
 
+// What one convolution call reads from its plan.  The forward GEMM runs over
+// the output rows (fwd region: sorted map into the input rows, masks, pair
+// lists); the input-gradient GEMM runs over the input rows (bwd region: the
+// transposed map with its columns flipped, k -> 26 - k).  A submanifold plan
+// is one region serving both, with nk = 27 offsets.
+struct ConvView {
+  const char* fwd = nullptr;
+  const int32_t* perm_f = nullptr;
+  int64_t n_f = 0;  // output rows
+  const char* bwd = nullptr;
+  const int32_t* perm_b = nullptr;
+  int64_t n_b = 0;  // input rows
+  int nk = kV;      // weight offsets
+};
+
+static size_t view_ws_bytes(const ConvView& v, int Ci, int Co, int esize) {
+  const size_t a = ws_layout(v.n_f, Ci, Co, esize).total, b = ws_layout(v.n_b, Ci, Co, esize).total;
+  return a > b ? a : b;
+}
+
 template <typename T>
-static int run_fwd(const char* plan, const uint32_t* nmap, const int32_t* perm, int64_t n, int Ci, int Co,
-                   const void* feats, const void* weight, const void* bias, void* out, char* ws,
-                   hipStream_t s) {
-  const PlanLayout L = conv_layout(n);
-  const WsLayout W = ws_layout(n, Ci, Co, sizeof(T));
+static void zero_out(T* p, int64_t count, hipStream_t s) {
+  if (!p || count <= 0) return;
+  int64_t blocks = (count + 255) / 256;
+  if (blocks > 1024) blocks = 1024;
+  zero_kernel<T><<<unsigned(blocks), 256, 0, s>>>(p, count);
+}
+
+template <typename T>
+static int run_fwd(const ConvView& v, int Ci, int Co, const void* feats, const void* weight, const void* bias,
+                   void* out, char* ws, hipStream_t s) {
+  if (v.n_f == 0) return SSC_OK;
+  const PlanLayout L = conv_layout(v.n_f);
+  const WsLayout W = ws_layout(v.n_f, Ci, Co, sizeof(T));
   T* wt = reinterpret_cast<T*>(ws + W.wt);
-  dim3 tg(unsigned((Co + 31) / 32), unsigned((Ci + 31) / 32), kV);
+  dim3 tg(unsigned((Co + 31) / 32), unsigned((Ci + 31) / 32), unsigned(v.nk));
   transpose_w<T><<<tg, 256, 0, s>>>(static_cast<const T*>(weight), wt, Ci, Co);
   launch_igemm<T>(static_cast<const T*>(feats), wt, static_cast<const T*>(bias), static_cast<T*>(out),
-                  reinterpret_cast<const uint32_t*>(plan + L.snmap), perm,
-                  reinterpret_cast<const uint32_t*>(plan + L.smask), reinterpret_cast<const T*>(plan + L.zrow), n,
-                  Ci, Co, 0, reinterpret_cast<float*>(ws + W.split), s);
+                  reinterpret_cast<const uint32_t*>(v.fwd + L.snmap), v.perm_f,
+                  reinterpret_cast<const uint32_t*>(v.fwd + L.smask), reinterpret_cast<const T*>(v.fwd + L.zrow),
+                  v.n_f, Ci, Co, 0, reinterpret_cast<float*>(ws + W.split), s);
   return SSC_OK;
 }
 
 template <typename T>
-static int run_bwd(const char* plan, const uint32_t* nmap, const int32_t* perm, int64_t n, int Ci, int Co,
-                   const void* feats, const void* weight, const void* dout, void* dfeats, void* dweight,
-                   void* dbias, char* ws, hipStream_t s) {
+static int run_bwd(const ConvView& v, int Ci, int Co, const void* feats, const void* weight, const void* dout,
+                   void* dfeats, void* dweight, void* dbias, char* ws, hipStream_t s) {
+  const T* dY = static_cast<const T*>(dout);
+  if (dfeats && v.n_b > 0) {
+    // dX = masked implicit GEMM over the input rows of dY with B[k] = W[26-k]
+    // read as [Ci][Co] (K = Co, N = Ci); the bwd map's column 26-k holds offset k
+    const PlanLayout Lb = conv_layout(v.n_b);
+    const WsLayout Wb = ws_layout(v.n_b, Ci, Co, sizeof(T));
+    if (v.n_f == 0) {
+      zero_out<T>(static_cast<T*>(dfeats), v.n_b * Ci, s);  // no outputs: nothing reaches the inputs
+    } else {
+      launch_igemm<T>(dY, static_cast<const T*>(weight), nullptr, static_cast<T*>(dfeats),
+                      reinterpret_cast<const uint32_t*>(v.bwd + Lb.snmap), v.perm_b,
+                      reinterpret_cast<const uint32_t*>(v.bwd + Lb.smask),
+                      reinterpret_cast<const T*>(v.bwd + Lb.zrow), v.n_b, Co, Ci, 1,
+                      reinterpret_cast<float*>(ws + Wb.split), s);
+    }
+  }
+  if (v.n_f == 0) {
+    // no outputs: dW and dbias are zero
+    if (dweight) zero_out<T>(static_cast<T*>(dweight), int64_t(v.nk) * Ci * Co, s);
+    if (dbias) zero_out<T>(static_cast<T*>(dbias), Co, s);
+    return SSC_OK;
+  }
+  const int64_t n = v.n_f;
   const PlanLayout L = conv_layout(n);
   const WsLayout W = ws_layout(n, Ci, Co, sizeof(T));
   const BwdShape b = bwd_shape(n, Ci, Co, int(sizeof(T)));
-  const PlanHeader* h = reinterpret_cast<const PlanHeader*>(plan + L.header);
-  const T* dY = static_cast<const T*>(dout);
-  if (dfeats) {
-    // dX = masked implicit GEMM of dY with B[k] = W[26-k] read as [Ci][Co] (K = Co, N = Ci)
-    launch_igemm<T>(dY, static_cast<const T*>(weight), nullptr, static_cast<T*>(dfeats),
-                    reinterpret_cast<const uint32_t*>(plan + L.snmap), perm,
-                    reinterpret_cast<const uint32_t*>(plan + L.smask), reinterpret_cast<const T*>(plan + L.zrow),
-                    n, Co, Ci, 1, reinterpret_cast<float*>(ws + W.split), s);
-  }
+  const PlanHeader* h = reinterpret_cast<const PlanHeader*>(v.fwd + L.header);
   float* bpart = reinterpret_cast<float*>(ws + W.bias);
   bool bias_done = false;
   if (dweight) {
     float* part = reinterpret_cast<float*>(ws + W.partial);
     const bool ride = launch_wgrad<T>(static_cast<const T*>(feats), dY,
-                                      reinterpret_cast<const uint32_t*>(plan + L.pair_i),
-                                      reinterpret_cast<const uint32_t*>(plan + L.pair_j), h,
-                                      reinterpret_cast<const uint32_t*>(plan + L.pseg),
-                                      reinterpret_cast<const T*>(plan + L.zrow), part, n, Ci, Co, b,
-                                      dbias ? bpart : nullptr, s);
+                                      reinterpret_cast<const uint32_t*>(v.fwd + L.pair_i),
+                                      reinterpret_cast<const uint32_t*>(v.fwd + L.pair_j), h,
+                                      reinterpret_cast<const uint32_t*>(v.fwd + L.pseg),
+                                      reinterpret_cast<const T*>(v.fwd + L.zrow), part, n, Ci, Co, b,
+                                      dbias ? bpart : nullptr, v.nk, s);
     // with the stage-1 partials written by that launch, stage 2 is one more grid row here
     const int64_t cico = int64_t(Ci) * Co;
     int64_t rx = (cico + 255) / 256;
     if (ride && (Co + 15) / 16 > rx) rx = (Co + 15) / 16;
-    dim3 rg(unsigned(rx), kV + (ride ? 1 : 0));
+    dim3 rg(unsigned(rx), unsigned(v.nk + (ride ? 1 : 0)));
     wgrad_reduce<T><<<rg, 256, 0, s>>>(part, h, static_cast<T*>(dweight), cico, b.chunk_len, b.max_chunks,
                                        b.rows_bpc > 0 ? 1 : 0, bpart, b.bias_blocks, Co,
-                                       static_cast<T*>(dbias));
+                                       static_cast<T*>(dbias), v.nk);
     bias_done = ride;
   }
   if (dbias && !bias_done) {
@@ -1349,6 +1391,16 @@ static int run_bwd(const char* plan, const uint32_t* nmap, const int32_t* perm, 
     colsum_final<T><<<unsigned((Co + 15) / 16), 256, 0, s>>>(bpart, b.bias_blocks, Co, static_cast<T*>(dbias));
   }
   return SSC_OK;
+}
+
+template <typename F>
+static void by_dtype(int dtype, F&& f) {
+  if (dtype == SSC_F32)
+    f(float{});
+  else if (dtype == SSC_F16)
+    f(_Float16{});
+  else
+    f(bf16s{});
 }
 
 }  // namespace ssc
@@ -1376,14 +1428,10 @@ extern "C" int ssc_subm_conv3d_fwd(const void* plan, const uint32_t* nmap, const
   if (workspace_bytes < ws_layout(n, Ci, Co, esize_of(dtype)).total) return SSC_ERR_WORKSPACE;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const char* pl = static_cast<const char*>(plan);
+  const ConvView v{pl, perm, n, pl, perm, n, kV};
   char* ws = static_cast<char*>(workspace);
   (void)hipGetLastError();
-  if (dtype == SSC_F32)
-    run_fwd<float>(pl, nmap, perm, n, Ci, Co, feats, weight, bias, out, ws, s);
-  else if (dtype == SSC_F16)
-    run_fwd<_Float16>(pl, nmap, perm, n, Ci, Co, feats, weight, bias, out, ws, s);
-  else
-    run_fwd<bf16s>(pl, nmap, perm, n, Ci, Co, feats, weight, bias, out, ws, s);
+  by_dtype(dtype, [&](auto t) { run_fwd<decltype(t)>(v, Ci, Co, feats, weight, bias, out, ws, s); });
   return hipGetLastError() == hipSuccess ? SSC_OK : SSC_ERR_HIP;
 }
 
@@ -1403,29 +1451,85 @@ extern "C" int ssc_subm_conv3d_bwd(const void* plan, const uint32_t* nmap, const
   const int es = esize_of(dtype);
   if ((dfeats || dweight || dbias) && workspace_bytes < ws_layout(n, Ci, Co, es).total) return SSC_ERR_WORKSPACE;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  (void)hipGetLastError();
-  if (n == 0) {
-    // no voxels: dW and dbias are zero, dX is empty
-    const int64_t wcount = int64_t(kV) * Ci * Co;
-    if (dtype == SSC_F32) {
-      if (dweight) zero_kernel<float><<<256, 256, 0, s>>>(static_cast<float*>(dweight), wcount);
-      if (dbias) zero_kernel<float><<<1, 256, 0, s>>>(static_cast<float*>(dbias), Co);
-    } else if (dtype == SSC_F16) {
-      if (dweight) zero_kernel<_Float16><<<256, 256, 0, s>>>(static_cast<_Float16*>(dweight), wcount);
-      if (dbias) zero_kernel<_Float16><<<1, 256, 0, s>>>(static_cast<_Float16*>(dbias), Co);
-    } else {
-      if (dweight) zero_kernel<bf16s><<<256, 256, 0, s>>>(static_cast<bf16s*>(dweight), wcount);
-      if (dbias) zero_kernel<bf16s><<<1, 256, 0, s>>>(static_cast<bf16s*>(dbias), Co);
-    }
-    return hipGetLastError() == hipSuccess ? SSC_OK : SSC_ERR_HIP;
-  }
   const char* pl = static_cast<const char*>(plan);
+  const ConvView v{pl, perm, n, pl, perm, n, kV};
   char* ws = static_cast<char*>(workspace);
-  if (dtype == SSC_F32)
-    run_bwd<float>(pl, nmap, perm, n, Ci, Co, feats, weight, dout, dfeats, dweight, dbias, ws, s);
-  else if (dtype == SSC_F16)
-    run_bwd<_Float16>(pl, nmap, perm, n, Ci, Co, feats, weight, dout, dfeats, dweight, dbias, ws, s);
-  else
-    run_bwd<bf16s>(pl, nmap, perm, n, Ci, Co, feats, weight, dout, dfeats, dweight, dbias, ws, s);
+  (void)hipGetLastError();
+  by_dtype(dtype, [&](auto t) {
+    run_bwd<decltype(t)>(v, Ci, Co, feats, weight, dout, dfeats, dweight, dbias, ws, s);
+  });
+  return hipGetLastError() == hipSuccess ? SSC_OK : SSC_ERR_HIP;
+}
+
+namespace {
+
+// The strided-conv plan's two GEMM regions (their starts depend on n_in and n_out only).
+ConvView sparse_view(const void* plan, int64_t n_in, int64_t n_out, int ks, const int32_t* perm_out) {
+  const SparseOffsets o = sparse_offsets(n_in, n_out);
+  const char* base = static_cast<const char*>(plan);
+  return ConvView{base + o.fwd, perm_out, n_out, base + o.bwd,
+                  reinterpret_cast<const int32_t*>(base + o.perm_in), n_in, ks * ks * ks};
+}
+
+bool sparse_sizes_ok(int64_t n_in, int64_t n_out, int32_t ks) {
+  return n_in >= 0 && n_in <= SSC_MAX_VOXELS && n_out >= 0 && n_out <= SSC_MAX_VOXELS && ks >= 1 && ks <= 3;
+}
+
+}  // namespace
+
+extern "C" size_t ssc_sparse_conv_workspace_bytes(int64_t n_in, int64_t n_out, int32_t Ci, int32_t Co,
+                                                  int32_t dtype) {
+  if (!sparse_sizes_ok(n_in, n_out, 1) || !channels_ok(Ci, Co)) return 0;
+  if (dtype != SSC_F32 && dtype != SSC_F16 && dtype != SSC_BF16) return 0;
+  ConvView v;
+  v.n_f = n_out;
+  v.n_b = n_in;
+  return view_ws_bytes(v, Ci, Co, esize_of(dtype));
+}
+
+extern "C" int ssc_sparse_conv3d_fwd(const void* plan, int64_t n_in, int64_t n_out, int32_t ks,
+                                     const int32_t* perm_out, int32_t Ci, int32_t Co, int32_t dtype,
+                                     const void* feats, const void* weight, const void* bias, void* out,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+  if (!sparse_sizes_ok(n_in, n_out, ks) || !plan || !weight) return SSC_ERR_INVALID_ARG;
+  if (dtype != SSC_F32 && dtype != SSC_F16 && dtype != SSC_BF16) return SSC_ERR_UNSUPPORTED;
+  if (!channels_ok(Ci, Co)) return SSC_ERR_UNSUPPORTED;
+  if (n_out > 0 && (!perm_out || !out || !workspace || (n_in > 0 && !feats))) return SSC_ERR_INVALID_ARG;
+  const void* ptrs[] = {plan, perm_out, feats, weight, bias, out, workspace};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return SSC_ERR_INVALID_ARG;
+  if (n_out == 0) return SSC_OK;
+  const ConvView v = sparse_view(plan, n_in, n_out, ks, perm_out);
+  if (workspace_bytes < view_ws_bytes(v, Ci, Co, esize_of(dtype))) return SSC_ERR_WORKSPACE;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  (void)hipGetLastError();
+  by_dtype(dtype, [&](auto t) { run_fwd<decltype(t)>(v, Ci, Co, feats, weight, bias, out, ws, s); });
+  return hipGetLastError() == hipSuccess ? SSC_OK : SSC_ERR_HIP;
+}
+
+extern "C" int ssc_sparse_conv3d_bwd(const void* plan, int64_t n_in, int64_t n_out, int32_t ks,
+                                     const int32_t* perm_out, int32_t Ci, int32_t Co, int32_t dtype,
+                                     const void* feats, const void* weight, const void* dout, void* dfeats,
+                                     void* dweight, void* dbias, void* workspace, size_t workspace_bytes,
+                                     void* stream) {
+  if (!sparse_sizes_ok(n_in, n_out, ks) || !plan) return SSC_ERR_INVALID_ARG;
+  if (dtype != SSC_F32 && dtype != SSC_F16 && dtype != SSC_BF16) return SSC_ERR_UNSUPPORTED;
+  if (!channels_ok(Ci, Co)) return SSC_ERR_UNSUPPORTED;
+  if (dfeats && !weight) return SSC_ERR_INVALID_ARG;
+  if (n_out > 0 && (!perm_out || !dout || (dweight && n_in > 0 && !feats))) return SSC_ERR_INVALID_ARG;
+  if ((dfeats || dweight || dbias) && !workspace) return SSC_ERR_INVALID_ARG;
+  const void* ptrs[] = {plan, perm_out, feats, weight, dout, dfeats, dweight, dbias, workspace};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return SSC_ERR_INVALID_ARG;
+  const ConvView v = sparse_view(plan, n_in, n_out, ks, perm_out);
+  if ((dfeats || dweight || dbias) && workspace_bytes < view_ws_bytes(v, Ci, Co, esize_of(dtype)))
+    return SSC_ERR_WORKSPACE;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  (void)hipGetLastError();
+  by_dtype(dtype, [&](auto t) {
+    run_bwd<decltype(t)>(v, Ci, Co, feats, weight, dout, dfeats, dweight, dbias, ws, s);
+  });
   return hipGetLastError() == hipSuccess ? SSC_OK : SSC_ERR_HIP;
 }

@@ -626,14 +626,6 @@ __global__ void __launch_bounds__(256) pair_scatter(const uint32_t* __restrict__
 // host side
 // ---------------------------------------------------------------------------
 
-static void sort_key_bits(int32_t B, int32_t X, int32_t Y, int32_t Z, int* axis_bits, int* zbits) {
-  int m = X;
-  if (Y > m) m = Y;
-  if (Z > m) m = Z;
-  *axis_bits = ceil_log2_u64(uint64_t(m));
-  *zbits = 3 * *axis_bits + ceil_log2_u64(uint64_t(B));
-}
-
 static inline unsigned grid1d(int64_t work, int threads) {
   int64_t b = (work + threads - 1) / threads;
   return unsigned(b < 1 ? 1 : b);
@@ -654,35 +646,48 @@ extern "C" size_t ssc_plan_bytes(int64_t n, int32_t B, int32_t X, int32_t Y, int
   return plan_layout(n, kb).total;
 }
 
-extern "C" int ssc_build_neighbor_map(const int32_t* coords, int64_t n, int32_t B, int32_t X, int32_t Y,
-                                      int32_t Z, int32_t key_bits, uint32_t* nmap, int32_t* perm,
-                                      void* plan, size_t plan_bytes, void* stream) {
-  if (n < 0 || n > SSC_MAX_VOXELS || !plan) return SSC_ERR_INVALID_ARG;
-  if (n > 0 && (!coords || !nmap || !perm)) return SSC_ERR_INVALID_ARG;
-  if (!aligned16(plan) || (n > 0 && (!aligned16(coords) || !aligned16(nmap) || !aligned16(perm))))
-    return SSC_ERR_INVALID_ARG;
-  if (!grid_ok(B, X, Y, Z)) return SSC_ERR_INVALID_ARG;
-  if (key_bits != 0 && key_bits != 32 && key_bits != 64) return SSC_ERR_INVALID_ARG;
-  const int kb = effective_key_bits(B, X, Y, Z, key_bits);
-  if (kb < 0) return SSC_ERR_UNSUPPORTED;
-  int axis_bits, zbits;
-  sort_key_bits(B, X, Y, Z, &axis_bits, &zbits);
-  if (kV + zbits > 64) return SSC_ERR_UNSUPPORTED;
-  const PlanLayout L = plan_layout(n, kb);
-  if (plan_bytes < L.total) return SSC_ERR_WORKSPACE;
+namespace ssc {
 
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  char* base = static_cast<char*>(plan);
+void prepare_region(char* base, const PlanLayout& L, int64_t n, int B, int X, int Y, int Z, int kb, int zbits,
+                    uint32_t* map, hipStream_t s) {
   PlanHeader* h = reinterpret_cast<PlanHeader*>(base + L.header);
   uint4* zrow = reinterpret_cast<uint4*>(base + L.zrow);
-  (void)hipGetLastError();
-  if (n == 0) {
-    // header only (the key fill touches the plan's own table region)
-    plan_prepare<uint32_t><<<1, 256, 0, s>>>(h, 0, B, X, Y, Z, kb, zbits, L.capacity, nullptr,
-                                             reinterpret_cast<Slot<uint32_t>*>(base + L.table), zrow, nullptr, 0);
-    return hipGetLastError() == hipSuccess ? SSC_OK : SSC_ERR_HIP;
-  }
+  // few sort blocks: row_scan adds the first pass's digit counts to a histogram that starts at zero
+  const bool direct = L.sort_blocks <= kSortDirectBlocks;
+  uint32_t* h0 = (n > 0 && direct) ? reinterpret_cast<uint32_t*>(base + L.hist) : nullptr;
+  const int64_t h0_len = h0 ? L.sort_blocks * 256 : 0;
+  const unsigned prep_blocks = grid1d((n * kV > int64_t(L.capacity) ? n * kV : int64_t(L.capacity)) / 4, 256);
+  const unsigned prep = prep_blocks < 2048 ? prep_blocks : 2048;
+  if (kb == 64)
+    plan_prepare<uint64_t><<<prep, 256, 0, s>>>(h, n, B, X, Y, Z, kb, zbits, L.capacity, map,
+                                                reinterpret_cast<Slot<uint64_t>*>(base + L.table), zrow, h0,
+                                                h0_len);
+  else
+    plan_prepare<uint32_t><<<prep, 256, 0, s>>>(h, n, B, X, Y, Z, kb, zbits, L.capacity, map,
+                                                reinterpret_cast<Slot<uint32_t>*>(base + L.table), zrow, h0,
+                                                h0_len);
+}
 
+void insert_coords(const int4* c4, int64_t n, int B, int X, int Y, int Z, int kb, char* base,
+                   const PlanLayout& L, hipStream_t s) {
+  if (n == 0) return;
+  PlanHeader* h = reinterpret_cast<PlanHeader*>(base + L.header);
+  if (kb == 64)
+    hash_insert<uint64_t><<<grid1d(n, 256), 256, 0, s>>>(c4, n, B, X, Y, Z,
+                                                         reinterpret_cast<Slot<uint64_t>*>(base + L.table),
+                                                         L.capacity, &h->status_bits);
+  else
+    hash_insert<uint32_t><<<grid1d(n, 256), 256, 0, s>>>(c4, n, B, X, Y, Z,
+                                                         reinterpret_cast<Slot<uint32_t>*>(base + L.table),
+                                                         L.capacity, &h->status_bits);
+}
+
+void order_rows(const int4* c4, const uint32_t* nmap, int64_t n, int B, int X, int Y, int Z, int32_t* perm,
+                char* base, const PlanLayout& L, bool want_pairs, hipStream_t s) {
+  if (n == 0) return;
+  int axis_bits, zbits;
+  sort_key_bits(B, X, Y, Z, &axis_bits, &zbits);
+  PlanHeader* h = reinterpret_cast<PlanHeader*>(base + L.header);
   uint32_t* smask = reinterpret_cast<uint32_t*>(base + L.smask);
   uint32_t* pair_i = reinterpret_cast<uint32_t*>(base + L.pair_i);
   uint32_t* pair_j = reinterpret_cast<uint32_t*>(base + L.pair_j);
@@ -693,33 +698,13 @@ extern "C" int ssc_build_neighbor_map(const int32_t* coords, int64_t n, int32_t 
   uint32_t* hist = reinterpret_cast<uint32_t*>(base + L.hist);
   uint32_t* pcnt = reinterpret_cast<uint32_t*>(base + L.pcnt);
   uint32_t* scan_tmp = reinterpret_cast<uint32_t*>(base + L.scan_tmp);
-  const int4* c4 = reinterpret_cast<const int4*>(coords);
 
   const int64_t pblk = L.pair_blocks;
   const int64_t nblk = L.sort_blocks;
-  // few sort blocks: the scatter passes build each other's histograms (radix_scatter<true>)
+  // few sort blocks: the scatter passes build each other's histograms (radix_scatter<true>);
+  // the first one was cleared by prepare_region
   const int direct = nblk <= kSortDirectBlocks ? 1 : 0;
   uint32_t* h0 = direct ? hist : nullptr;
-  const int64_t h0_len = direct ? nblk * 256 : 0;
-  const unsigned prep_blocks = grid1d((n * kV > int64_t(L.capacity) ? n * kV : int64_t(L.capacity)) / 4, 256);
-  const unsigned prep = prep_blocks < 2048 ? prep_blocks : 2048;
-  if (kb == 64) {
-    Slot<uint64_t>* table = reinterpret_cast<Slot<uint64_t>*>(base + L.table);
-    plan_prepare<uint64_t><<<prep, 256, 0, s>>>(h, n, B, X, Y, Z, kb, zbits, L.capacity, nmap, table, zrow, h0,
-                                                h0_len);
-    hash_insert<uint64_t><<<grid1d(n, 256), 256, 0, s>>>(c4, n, B, X, Y, Z, table, L.capacity,
-                                                         &h->status_bits);
-    probe_half<uint64_t><<<grid1d(n * kCentre, 256), 256, 0, s>>>(c4, n, B, X, Y, Z, table, L.capacity,
-                                                                  nmap);
-  } else {
-    Slot<uint32_t>* table = reinterpret_cast<Slot<uint32_t>*>(base + L.table);
-    plan_prepare<uint32_t><<<prep, 256, 0, s>>>(h, n, B, X, Y, Z, kb, zbits, L.capacity, nmap, table, zrow, h0,
-                                                h0_len);
-    hash_insert<uint32_t><<<grid1d(n, 256), 256, 0, s>>>(c4, n, B, X, Y, Z, table, L.capacity,
-                                                         &h->status_bits);
-    probe_half<uint32_t><<<grid1d(n * kCentre, 256), 256, 0, s>>>(c4, n, B, X, Y, Z, table, L.capacity,
-                                                                  nmap);
-  }
   row_scan<<<unsigned(pblk), 256, 0, s>>>(c4, nmap, n, B, X, Y, Z, axis_bits, zbits, key0, pcnt, pblk, h0,
                                           direct ? hist + nblk * 256 : nullptr, nblk, kSortThreads * L.sort_items);
 
@@ -732,7 +717,7 @@ extern "C" int ssc_build_neighbor_map(const int32_t* coords, int64_t n, int32_t 
   uint32_t* vout = val1;
   const int pdirect = pblk <= kPairDirectBlocks ? 1 : 0;
   // small inputs: the pair lists are built by extra workgroups of the first pass
-  const bool pairs_ride = direct && pdirect;
+  const bool pairs_ride = want_pairs && direct && pdirect;
   const PairJob no_pairs{nullptr, nullptr, 0, nullptr, nullptr, nullptr, nullptr};
   const PairJob pair_job{nmap, pcnt, pblk, pair_i, pair_j, h, reinterpret_cast<uint32_t*>(base + L.pseg)};
   for (int p = 0; p < passes; ++p) {
@@ -772,6 +757,7 @@ extern "C" int ssc_build_neighbor_map(const int32_t* coords, int64_t n, int32_t 
   permute_rows<<<grid1d(n * kV, 256), 256, 0, s>>>(nmap, perm, n, reinterpret_cast<uint32_t*>(base + L.snmap));
 
   // per-offset pair lists (already built by the first pass for small inputs)
+  if (!want_pairs) return;
   if (!pdirect) {
     launch_scan(pcnt, pblk * kV + 1, scan_tmp, s);
     pair_offsets<<<1, 64, 0, s>>>(pcnt, pblk, h);
@@ -779,7 +765,43 @@ extern "C" int ssc_build_neighbor_map(const int32_t* coords, int64_t n, int32_t 
   if (!pairs_ride)
     pair_scatter<<<unsigned(pblk), 256, 0, s>>>(nmap, n, pcnt, pblk, pair_i, pair_j, pdirect, h,
                                               reinterpret_cast<uint32_t*>(base + L.pseg));
+}
 
+}  // namespace ssc
+
+extern "C" int ssc_build_neighbor_map(const int32_t* coords, int64_t n, int32_t B, int32_t X, int32_t Y,
+                                      int32_t Z, int32_t key_bits, uint32_t* nmap, int32_t* perm,
+                                      void* plan, size_t plan_bytes, void* stream) {
+  if (n < 0 || n > SSC_MAX_VOXELS || !plan) return SSC_ERR_INVALID_ARG;
+  if (n > 0 && (!coords || !nmap || !perm)) return SSC_ERR_INVALID_ARG;
+  if (!aligned16(plan) || (n > 0 && (!aligned16(coords) || !aligned16(nmap) || !aligned16(perm))))
+    return SSC_ERR_INVALID_ARG;
+  if (!grid_ok(B, X, Y, Z)) return SSC_ERR_INVALID_ARG;
+  if (key_bits != 0 && key_bits != 32 && key_bits != 64) return SSC_ERR_INVALID_ARG;
+  const int kb = effective_key_bits(B, X, Y, Z, key_bits);
+  if (kb < 0) return SSC_ERR_UNSUPPORTED;
+  int axis_bits, zbits;
+  sort_key_bits(B, X, Y, Z, &axis_bits, &zbits);
+  if (kV + zbits > 64) return SSC_ERR_UNSUPPORTED;
+  const PlanLayout L = plan_layout(n, kb);
+  if (plan_bytes < L.total) return SSC_ERR_WORKSPACE;
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* base = static_cast<char*>(plan);
+  (void)hipGetLastError();
+  // header, zero row, first histogram, sentinel fill of nmap, empty table
+  prepare_region(base, L, n, B, X, Y, Z, kb, zbits, n > 0 ? nmap : nullptr, s);
+  if (n == 0) return hipGetLastError() == hipSuccess ? SSC_OK : SSC_ERR_HIP;
+
+  const int4* c4 = reinterpret_cast<const int4*>(coords);
+  insert_coords(c4, n, B, X, Y, Z, kb, base, L, s);
+  if (kb == 64)
+    probe_half<uint64_t><<<grid1d(n * kCentre, 256), 256, 0, s>>>(
+        c4, n, B, X, Y, Z, reinterpret_cast<const Slot<uint64_t>*>(base + L.table), L.capacity, nmap);
+  else
+    probe_half<uint32_t><<<grid1d(n * kCentre, 256), 256, 0, s>>>(
+        c4, n, B, X, Y, Z, reinterpret_cast<const Slot<uint32_t>*>(base + L.table), L.capacity, nmap);
+  order_rows(c4, nmap, n, B, X, Y, Z, perm, base, L, true, s);
   return hipGetLastError() == hipSuccess ? SSC_OK : SSC_ERR_HIP;
 }
 

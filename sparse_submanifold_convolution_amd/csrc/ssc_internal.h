@@ -142,6 +142,79 @@ inline PlanLayout plan_layout(int64_t n, int key_bits) {
   return L;
 }
 
+// Bits per axis and total bits of the z-order part of the sort key of grid (B, X, Y, Z).
+inline void sort_key_bits(int32_t B, int32_t X, int32_t Y, int32_t Z, int* axis_bits, int* zbits) {
+  int m = X;
+  if (Y > m) m = Y;
+  if (Z > m) m = Z;
+  *axis_bits = ceil_log2_u64(uint64_t(m));
+  *zbits = 3 * *axis_bits + ceil_log2_u64(uint64_t(B));
+}
+
+// Moves a plan layout's build-only scratch by delta bytes (its conv regions stay).
+inline PlanLayout relocate_scratch(PlanLayout L, size_t delta) {
+  L.table += delta;
+  L.key0 += delta;
+  L.key1 += delta;
+  L.val0 += delta;
+  L.val1 += delta;
+  L.hist += delta;
+  L.pcnt += delta;
+  L.scan_tmp += delta;
+  L.total += delta;
+  return L;
+}
+
+// A strided (generalised) convolution plan.  Its conv-time regions depend on
+// the row counts only and come first: the forward region over the n_out
+// output rows (sorted map into the input rows, masks, pair lists), the
+// backward region over the n_in input rows (sorted transposed map), the input
+// rows' GEMM order and the transposed map itself.  The build scratch of both
+// directions (hash tables, sort buffers) follows.
+struct SparseOffsets {
+  size_t fwd = 0, bwd = 0, perm_in = 0, tmap = 0, conv_total = 0;
+};
+inline SparseOffsets sparse_offsets(int64_t n_in, int64_t n_out) {
+  SparseOffsets o;
+  o.fwd = 0;
+  o.bwd = align_up(conv_layout(n_out).total, 256);
+  o.perm_in = align_up(o.bwd + conv_layout(n_in).total, 256);
+  o.tmap = align_up(o.perm_in + size_t(n_in) * 4, 256);
+  o.conv_total = align_up(o.tmap + size_t(n_in) * kV * 4, 256);
+  return o;
+}
+struct SparseLayout {
+  SparseOffsets o;
+  PlanLayout f, b;  // relative to base + o.fwd and base + o.bwd, scratch relocated past conv_total
+  size_t total = 0;
+};
+inline SparseLayout sparse_layout(int64_t n_in, int64_t n_out, int kb_in, int kb_out) {
+  SparseLayout S;
+  S.o = sparse_offsets(n_in, n_out);
+  const PlanLayout f = plan_layout(n_out, kb_out), b = plan_layout(n_in, kb_in);
+  const size_t cf = conv_layout(n_out).total, cb = conv_layout(n_in).total;
+  size_t off = S.o.conv_total;
+  S.f = relocate_scratch(f, off - S.o.fwd - cf);
+  off = align_up(S.o.fwd + S.f.total, 256);
+  S.b = relocate_scratch(b, off - S.o.bwd - cb);
+  S.total = align_up(S.o.bwd + S.b.total, 256);
+  return S;
+}
+
+// Plan-build steps shared by the submanifold and strided builders (plan builder):
+// header, zero row, first sort histogram, sentinel fill of map[n][27], empty
+// hash keys of one region
+void prepare_region(char* base, const PlanLayout& L, int64_t n, int B, int X, int Y, int Z, int kb, int zbits,
+                    uint32_t* map, hipStream_t s);
+// coordinate check and hash insert of n rows into the region's table
+void insert_coords(const int4* c4, int64_t n, int B, int X, int Y, int Z, int kb, char* base,
+                   const PlanLayout& L, hipStream_t s);
+// masks, (mask, z-order) sort -> perm and sorted masks, the sorted-order map,
+// and (want_pairs) the per-offset pair lists, of a [n][27] map whose rows sit
+// at coords in grid (B, X, Y, Z)
+void order_rows(const int4* c4, const uint32_t* nmap, int64_t n, int B, int X, int Y, int Z, int32_t* perm,
+                char* base, const PlanLayout& L, bool want_pairs, hipStream_t s);
+
 // round-to-nearest-even float -> bfloat16 bits
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);

@@ -251,6 +251,19 @@ def values_for(coords: np.ndarray, shape: tuple, seed: int, ci: int, co: int, dt
                     ci, co, dtype, 0, feats, weight, bias, dout)
 
 
+def strided_values(seed: int, n_in: int, n_out: int, ks: int, ci: int, co: int, dtype: str,
+                   random_bias: bool = True) -> tuple:
+    """Seeded (feats [n_in, ci], weight [ks^3, ci, co], bias [co], dout [n_out, co]) for a strided
+    convolution, drawn in that order; weight ~ N(0, 1 / (ks^3 ci)), the rest ~ N(0, 1)."""
+    rng = np.random.default_rng(seed)
+    V = ks ** 3
+    feats = normal(rng, (n_in, ci), dtype)
+    weight = normal(rng, (V, ci, co), dtype, scale=1.0 / math.sqrt(V * ci))
+    bias = normal(rng, (co,), dtype) if random_bias else torch.zeros(co, dtype=DTYPES[dtype])
+    dout = normal(rng, (n_out, co), dtype)
+    return feats, weight, bias, dout
+
+
 # ----------------------------------------------------------------------------
 # query points for sparse grid sampling
 # ----------------------------------------------------------------------------

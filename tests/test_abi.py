@@ -152,3 +152,42 @@ def test_grid_sample_workspace_and_rejections(L):
     assert b(FAKE, 100, 1, 8, 8, 8, 0, 64, 1, pts, 10, FAKE, FAKE, None, 1 << 30, None) == 1
     assert b(FAKE, 100, 1, 8, 8, 8, 0, 64, 1, pts, 10, None, FAKE, FAKE, 1 << 30, None) == 1  # dout NULL
     assert b(FAKE, 100, 1, 8, 8, 8, 0, 64, 1, pts, 10, FAKE, None, FAKE, 1 << 30, None) == 1  # dfeats NULL
+
+
+def test_sparse_conv_sizes_and_rejections(L):
+    dims = (ctypes.c_int32 * 4)()
+    assert L.ssc_sparse_out_shape(2, 64, 63, 1, 3, 2, 1, dims) == 0 and list(dims) == [2, 32, 32, 1]
+    assert L.ssc_sparse_out_shape(1, 8, 8, 8, 4, 1, 0, dims) == 1      # kernel side above 3
+    assert L.ssc_sparse_out_shape(1, 8, 8, 8, 2, 1, 2, dims) == 1      # padding must stay below ks
+    assert L.ssc_sparse_out_shape(1, 1, 8, 8, 3, 1, 0, dims) == 1      # empty output grid
+    assert L.ssc_sparse_out_shape(1, 8, 8, 8, 2, 0, 0, dims) == 1      # stride 0
+    # one bit per output site plus a count per 32 sites
+    small = L.ssc_sparse_out_workspace_bytes(1, 64, 64, 64, 2, 2, 0)
+    big = L.ssc_sparse_out_workspace_bytes(1, 64, 64, 64, 3, 1, 1)
+    assert 0 < small < big and big >= 64 ** 3 // 4
+    assert L.ssc_sparse_out_workspace_bytes(1, 8, 8, 8, 5, 1, 0) == 0
+    assert L.ssc_sparse_plan_bytes(100, 50, 1, 32, 32, 32, 2, 2, 0, 0) > 0
+    assert L.ssc_sparse_plan_bytes(100, 50, 1, 32, 32, 32, 2, 2, 0, 17) == 0
+    assert L.ssc_sparse_plan_bytes(-1, 50, 1, 32, 32, 32, 2, 2, 0, 0) == 0
+    assert L.ssc_sparse_plan_bytes(0, 0, 1, 32, 32, 32, 2, 2, 0, 0) > 0
+    assert L.ssc_sparse_conv_workspace_bytes(1000, 200, 64, 128, 1) > 0
+    assert L.ssc_sparse_conv_workspace_bytes(1000, 200, 64, 24, 1) == 0
+    cnt = ctypes.c_void_p(0x10008)
+    assert L.ssc_sparse_out_count(None, 10, 1, 8, 8, 8, 2, 2, 0, FAKE, 1 << 30, cnt, None) == 1
+    assert L.ssc_sparse_out_count(FAKE, 10, 1, 8, 8, 8, 2, 2, 0, FAKE, 16, cnt, None) == 3
+    assert L.ssc_sparse_out_count(FAKE, 10, 1, 8, 8, 8, 2, 2, 3, FAKE, 1 << 30, cnt, None) == 1
+    assert L.ssc_sparse_out_coords(FAKE, 16, 1, 8, 8, 8, 2, 2, 0, FAKE, 4, None) == 3
+    assert L.ssc_sparse_out_coords(FAKE, 1 << 30, 1, 8, 8, 8, 2, 2, 0, None, 4, None) == 1
+    b = L.ssc_build_sparse_map
+    assert b(None, 10, 1, 8, 8, 8, FAKE, 4, 2, 2, 0, 0, FAKE, FAKE, FAKE, 1 << 30, None) == 1
+    assert b(FAKE, 10, 1, 8, 8, 8, FAKE, 4, 2, 2, 0, 0, FAKE, FAKE, FAKE, 16, None) == 3
+    assert b(FAKE, 10, 1, 8, 8, 8, FAKE, 4, 2, 2, 0, 48, FAKE, FAKE, FAKE, 1 << 30, None) == 1
+    assert b(FAKE, 10, 1, 8, 8, 8, ctypes.c_void_p(0x10004), 4, 2, 2, 0, 0, FAKE, FAKE, FAKE, 1 << 30, None) == 1
+    f = L.ssc_sparse_conv3d_fwd
+    assert f(FAKE, 100, 20, 2, FAKE, 32, 32, 5, FAKE, FAKE, None, FAKE, FAKE, 1 << 30, None) == 2
+    assert f(FAKE, 100, 20, 2, FAKE, 32, 32, 0, FAKE, FAKE, None, FAKE, FAKE, 64, None) == 3
+    assert f(FAKE, 100, 20, 4, FAKE, 32, 32, 0, FAKE, FAKE, None, FAKE, FAKE, 1 << 30, None) == 1
+    assert f(FAKE, 100, 20, 2, None, 32, 32, 0, FAKE, FAKE, None, FAKE, FAKE, 1 << 30, None) == 1
+    g = L.ssc_sparse_conv3d_bwd
+    assert g(FAKE, 100, 20, 2, FAKE, 32, 32, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 64, None) == 3
+    assert g(FAKE, 100, 20, 2, FAKE, 32, 32, 0, FAKE, None, FAKE, FAKE, None, None, FAKE, 1 << 30, None) == 1
