@@ -48,6 +48,12 @@ def parse():
     p.add_argument("--serialize", action="store_true",
                    help="only time encode_seq + decode_seq (z-order and Hilbert) on the workload's "
                         "coordinates; prints its own JSON line")
+    p.add_argument("--sparse-conv", action="store_true",
+                   help="only time the strided sparse convolution (output sites, map build, fwd, dgrad, wgrad) "
+                        "over the workload's voxels; prints its own JSON line")
+    p.add_argument("--ks", type=int, default=2, help="--sparse-conv kernel side")
+    p.add_argument("--stride", type=int, default=2, help="--sparse-conv stride")
+    p.add_argument("--pad", type=int, default=0, help="--sparse-conv padding")
     p.add_argument("--grid-sample", action="store_true",
                    help="only time sparse grid sampling (fwd + feature gradient) at one point per voxel of "
                         "the workload; prints its own JSON line")
@@ -274,6 +280,150 @@ def grid_sample_bench(args) -> None:
     print(json.dumps(res), flush=True)
 
 
+def sparse_conv_bench(args) -> None:
+    """Strided sparse convolution over a workload's voxel set, inputs resident in HBM.
+
+    Phases: output sites (count, host read, emit), map build, forward, input gradient, weight
+    gradient + dbias.  The map build and each pass are captured in a HIP graph of `reps` calls and
+    replayed; the output sites include the count's host read.  Values are seeded (strided_values).
+    """
+    import numpy as np
+    import torch
+    import sparse_submanifold_convolution_amd as ssc
+    from sparse_submanifold_convolution_amd import workloads as WL
+
+    dev = torch.device("cuda:0")
+    L = ssc.lib()
+    P_ = ssc.binding._ptr
+    w = WL.make_workload(args.config, values=False)
+    ks, st, pd = args.ks, args.stride, args.pad
+    coords = torch.from_numpy(w.coords).to(dev)
+    print(f"[bench] strided conv on workload {args.config} ({w.n} voxels), ks={ks} s={st} p={pd}",
+          file=sys.stderr, flush=True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    best_sites = 1e30
+    for _ in range(max(3, args.steps // 4)):
+        torch.cuda.synchronize()
+        e0.record()
+        oc = ssc.sparse_out_coords(coords, w.shape, ks, st, pd)
+        e1.record()
+        torch.cuda.synchronize()
+        best_sites = min(best_sites, e0.elapsed_time(e1))
+    plan = ssc.build_sparse_map(coords, w.shape, ks, st, pd, out_coords=oc, key_bits=w.key_bits)
+    n_in, n_out, V, C = plan.n_in, plan.n_out, ks ** 3, w.ci
+    P = int((plan.nmap != -1).sum())
+    X, W, b, dY = (t.to(dev) for t in WL.strided_values(1000 + args.config, n_in, n_out, ks, C, C, w.dtype))
+    out = torch.empty((n_out, C), dtype=X.dtype, device=dev)
+    dX = torch.empty((n_in, C), dtype=X.dtype, device=dev)
+    dW = torch.empty((V, C, C), dtype=X.dtype, device=dev)
+    db = torch.empty((C,), dtype=X.dtype, device=dev)
+    ws = ssc.sparse_workspace(plan, C, C, X.dtype)
+    B_, Xd, Yd, Zd = w.shape
+
+    def build():
+        r = L.ssc_build_sparse_map(P_(coords), n_in, B_, Xd, Yd, Zd, P_(oc), n_out, ks, st, pd, w.key_bits,
+                                   P_(plan.nmap), P_(plan.perm), P_(plan.buf), plan.buf.numel(),
+                                   ssc.binding._stream(dev))
+        if r:
+            raise ssc.SSCError("ssc_build_sparse_map", r)
+
+    reps = 10
+    side = torch.cuda.Stream(dev)
+
+    def timed(fn):
+        side.wait_stream(torch.cuda.current_stream(dev))
+        with torch.cuda.stream(side):
+            fn()
+        torch.cuda.current_stream(dev).wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(reps):
+                fn()
+        for _ in range(max(1, args.warmup)):
+            g.replay()
+        torch.cuda.synchronize()
+        a, c = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        best = 1e30
+        for _ in range(args.steps):
+            a.record()
+            g.replay()
+            c.record()
+            torch.cuda.synchronize()
+            best = min(best, a.elapsed_time(c) / reps)
+        return best
+
+    per = {
+        "map_build": timed(build),
+        "fwd": timed(lambda: ssc.sparse_conv3d_fwd(plan, X, W, b, out=out, ws=ws)),
+        "dgrad": timed(lambda: ssc.sparse_conv3d_bwd(plan, X, W, dY, ws=ws, outs=(dX, None, None))),
+        "wgrad": timed(lambda: ssc.sparse_conv3d_bwd(plan, X, W, dY, ws=ws, outs=(None, dW, db))),
+    }
+    conv_ms = per["fwd"] + per["dgrad"] + per["wgrad"]
+    flops_pass = 2.0 * P * C * C
+    s = X.element_size()
+    # input-gradient GEMM: one index per valid pair, each dY row read once, each dX row written once, W
+    alg_bytes = 4.0 * P + s * (n_out * C + n_in * C) + s * V * C * C
+    ai = flops_pass / alg_bytes
+    peak_f = PEAK_TFLOPS[w.dtype]
+    ridge = peak_f * 1e12 / (PEAK_HBM_GBS * 1e9)
+    t_k = per["dgrad"] * 1e-3
+    if ai >= ridge:
+        ach = flops_pass / t_k / 1e12
+        roof = {"bound": "mfma", "achieved": ach, "peak": peak_f, "unit": "TFLOP/s", "frac": ach / peak_f}
+    else:
+        ach = alg_bytes / t_k / 1e9
+        roof = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": ach / PEAK_HBM_GBS}
+    roof.update({"traffic": None, "kernel": "igemm (input-gradient launch, transposed map)",
+                 "avg_launch_ms": per["dgrad"], "flops_per_launch": flops_pass, "alg_bytes_per_launch": alg_bytes,
+                 "arith_intensity": ai, "ridge": ridge})
+    res = {
+        "metric": "effective TFLOP/s (valid MACs), strided sparse conv3d fwd+bwd, 1 MI355X",
+        "value": 3 * flops_pass / (conv_ms * 1e-3) / 1e12, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": conv_ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": f"config {args.config} voxels: {w.desc}; strided conv ks={ks} stride={st} pad={pd}",
+                   "in_voxels": n_in, "out_voxels": n_out, "valid_pairs": P, "ci": C, "co": C,
+                   "step": "fwd + dgrad + wgrad + dbias on a built map",
+                   "launch": f"graph of {reps} calls per phase, best replay", "parallelism": "single GPU"},
+        "out_voxels_per_s": n_out / (conv_ms * 1e-3),
+        "plan_ms": {"out_sites_incl_host_read": best_sites, "map_build": per["map_build"]},
+        "per_pass_ms": {k: per[k] for k in ("fwd", "dgrad", "wgrad")},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = sparse_conv_cpu_baseline(w, ks, st, pd, X.cpu(), W.cpu(), b.cpu(), dY.cpu(),
+                                                       args.cpu_budget_s)
+    print(json.dumps(res), flush=True)
+
+
+def sparse_conv_cpu_baseline(w, ks, st, pd, X, W, b, dY, budget_s: float) -> dict:
+    """The strided-conv oracle (float64 numpy + BLAS) on the whole workload, on the host."""
+    from oracle import sparse_conv as SC
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [t for t in threadpool_info() if t.get("user_api") == "blas"]
+        cores = int(blas[0]["num_threads"]) if blas else 1
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    reps, t_total, flops = 0, 0.0, 0.0
+    while reps == 0 or (t_total < budget_s / 2 and reps < 3):
+        t0 = time.perf_counter()
+        oc = SC.out_coords(w.coords, w.shape, ks, st, pd)
+        nm = SC.neighbor_map(w.coords, w.shape, oc, ks, st, pd)
+        SC.fwd(X, W, b, nm)
+        SC.dgrad(dY, W, nm, len(w.coords))
+        SC.wgrad(X, dY, nm, ks ** 3)
+        SC.dbias(dY)
+        t_total += time.perf_counter() - t0
+        reps += 1
+        flops = 3 * 2.0 * int((nm != SC.SENTINEL).sum()) * w.ci * w.ci
+    sec = t_total / reps
+    return {"value": flops / sec / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"whole workload ({len(w.coords)} input voxels: output sites, map and the three passes), "
+                      f"{reps} repetition(s), float64 numpy/BLAS", "seconds_per_step": sec}
+
+
 def plan_key_width(w) -> int:
     """Key width the plan of workload w uses (the build's rule: 32 bits when the grid volume fits)."""
     if w.key_bits:
@@ -313,6 +463,9 @@ def main():
         return
     if args.grid_sample:
         grid_sample_bench(args)
+        return
+    if args.sparse_conv:
+        sparse_conv_bench(args)
         return
 
     import numpy as np
