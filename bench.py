@@ -60,12 +60,16 @@ def parse():
     return p.parse_args()
 
 
+# the sources the masked implicit GEMM is compiled from: its translation unit and the headers it includes
+GEMM_SOURCES = ("sparse_submanifold_convolution_amd/csrc/conv.hip", "sparse_submanifold_convolution_amd/csrc/ssc_internal.h",
+                "include/ssc.h")
+
+
 def source_hash() -> str:
     h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "sparse_submanifold_convolution_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(f.encode())
+    for rel in GEMM_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as fh:
+            h.update(os.path.basename(rel).encode())
             h.update(fh.read())
     return h.hexdigest()[:16]
 

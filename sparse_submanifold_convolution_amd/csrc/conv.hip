@@ -1125,9 +1125,13 @@ struct WsLayout {
   size_t wt = 0, partial = 0, bias = 0, split = 0, total = 0;
 };
 
-static WsLayout ws_layout(int64_t n, int Ci, int Co, int esize) {
+// n_f: rows of the forward GEMM and of the weight gradient's pair lists (the
+// output rows); n_b: rows of the input-gradient GEMM (the input rows).  Every
+// region is disjoint, so the input gradient and the weight gradient may run
+// concurrently on one workspace.
+static WsLayout ws_layout(int64_t n_f, int64_t n_b, int Ci, int Co, int esize) {
   WsLayout w;
-  const BwdShape b = bwd_shape(n, Ci, Co, esize);
+  const BwdShape b = bwd_shape(n_f, Ci, Co, esize);
   size_t off = 0;
   w.wt = off;
   off = align_up(off + size_t(kV) * Ci * Co * esize, 256);
@@ -1136,9 +1140,9 @@ static WsLayout ws_layout(int64_t n, int Ci, int Co, int esize) {
   w.bias = off;
   off = align_up(off + size_t(b.bias_blocks) * Co * 4, 256);
   // Split-K partials of the forward (N = Co) or input-gradient (N = Ci) GEMM
-  const int sf = split_parts(n, Co), sd = split_parts(n, Ci);
-  const size_t sbytes_f = sf > 1 ? size_t(sf) * size_t(n) * Co * 4 : 0;
-  const size_t sbytes_d = sd > 1 ? size_t(sd) * size_t(n) * Ci * 4 : 0;
+  const int sf = split_parts(n_f, Co), sd = split_parts(n_b, Ci);
+  const size_t sbytes_f = sf > 1 ? size_t(sf) * size_t(n_f) * Co * 4 : 0;
+  const size_t sbytes_d = sd > 1 ? size_t(sd) * size_t(n_b) * Ci * 4 : 0;
   w.split = off;
   off = align_up(off + (sbytes_f > sbytes_d ? sbytes_f : sbytes_d), 256);
   w.total = off;
@@ -1306,8 +1310,7 @@ struct ConvView {
 };
 
 static size_t view_ws_bytes(const ConvView& v, int Ci, int Co, int esize) {
-  const size_t a = ws_layout(v.n_f, Ci, Co, esize).total, b = ws_layout(v.n_b, Ci, Co, esize).total;
-  return a > b ? a : b;
+  return ws_layout(v.n_f, v.n_b, Ci, Co, esize).total;
 }
 
 template <typename T>
@@ -1323,7 +1326,7 @@ static int run_fwd(const ConvView& v, int Ci, int Co, const void* feats, const v
                    void* out, char* ws, hipStream_t s) {
   if (v.n_f == 0) return SSC_OK;
   const PlanLayout L = conv_layout(v.n_f);
-  const WsLayout W = ws_layout(v.n_f, Ci, Co, sizeof(T));
+  const WsLayout W = ws_layout(v.n_f, v.n_b, Ci, Co, sizeof(T));
   T* wt = reinterpret_cast<T*>(ws + W.wt);
   dim3 tg(unsigned((Co + 31) / 32), unsigned((Ci + 31) / 32), unsigned(v.nk));
   transpose_w<T><<<tg, 256, 0, s>>>(static_cast<const T*>(weight), wt, Ci, Co);
@@ -1342,7 +1345,7 @@ static int run_bwd(const ConvView& v, int Ci, int Co, const void* feats, const v
     // dX = masked implicit GEMM over the input rows of dY with B[k] = W[26-k]
     // read as [Ci][Co] (K = Co, N = Ci); the bwd map's column 26-k holds offset k
     const PlanLayout Lb = conv_layout(v.n_b);
-    const WsLayout Wb = ws_layout(v.n_b, Ci, Co, sizeof(T));
+    const WsLayout Wb = ws_layout(v.n_f, v.n_b, Ci, Co, sizeof(T));
     if (v.n_f == 0) {
       zero_out<T>(static_cast<T*>(dfeats), v.n_b * Ci, s);  // no outputs: nothing reaches the inputs
     } else {
@@ -1361,7 +1364,7 @@ static int run_bwd(const ConvView& v, int Ci, int Co, const void* feats, const v
   }
   const int64_t n = v.n_f;
   const PlanLayout L = conv_layout(n);
-  const WsLayout W = ws_layout(n, Ci, Co, sizeof(T));
+  const WsLayout W = ws_layout(n, v.n_b, Ci, Co, sizeof(T));
   const BwdShape b = bwd_shape(n, Ci, Co, int(sizeof(T)));
   const PlanHeader* h = reinterpret_cast<const PlanHeader*>(v.fwd + L.header);
   float* bpart = reinterpret_cast<float*>(ws + W.bias);
@@ -1410,7 +1413,7 @@ using namespace ssc;
 extern "C" size_t ssc_conv_workspace_bytes(int64_t n, int32_t Ci, int32_t Co, int32_t dtype) {
   if (n < 0 || n > SSC_MAX_VOXELS || !channels_ok(Ci, Co)) return 0;
   if (dtype != SSC_F32 && dtype != SSC_F16 && dtype != SSC_BF16) return 0;
-  return ws_layout(n, Ci, Co, esize_of(dtype)).total;
+  return ws_layout(n, n, Ci, Co, esize_of(dtype)).total;
 }
 
 extern "C" int ssc_subm_conv3d_fwd(const void* plan, const uint32_t* nmap, const int32_t* perm, int64_t n,
@@ -1425,7 +1428,7 @@ extern "C" int ssc_subm_conv3d_fwd(const void* plan, const uint32_t* nmap, const
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return SSC_ERR_INVALID_ARG;
   if (n == 0) return SSC_OK;
-  if (workspace_bytes < ws_layout(n, Ci, Co, esize_of(dtype)).total) return SSC_ERR_WORKSPACE;
+  if (workspace_bytes < ws_layout(n, n, Ci, Co, esize_of(dtype)).total) return SSC_ERR_WORKSPACE;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const char* pl = static_cast<const char*>(plan);
   const ConvView v{pl, perm, n, pl, perm, n, kV};
@@ -1449,7 +1452,7 @@ extern "C" int ssc_subm_conv3d_bwd(const void* plan, const uint32_t* nmap, const
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return SSC_ERR_INVALID_ARG;
   const int es = esize_of(dtype);
-  if ((dfeats || dweight || dbias) && workspace_bytes < ws_layout(n, Ci, Co, es).total) return SSC_ERR_WORKSPACE;
+  if ((dfeats || dweight || dbias) && workspace_bytes < ws_layout(n, n, Ci, Co, es).total) return SSC_ERR_WORKSPACE;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const char* pl = static_cast<const char*>(plan);
   const ConvView v{pl, perm, n, pl, perm, n, kV};

@@ -179,7 +179,10 @@ __global__ void __launch_bounds__(256) plan_prepare(PlanHeader* h, int64_t n, in
   for (int64_t i = t0; i < int64_t(kZeroRowBytes / 16); i += stride) zrow[i] = make_uint4(0, 0, 0, 0);
   for (int64_t i = t0; i < hzero_len; i += stride) hzero[i] = 0;
   for (int64_t i = t0; i < n * kV; i += stride) nmap[i] = kSentinel;
-  for (int64_t i = t0; i < int64_t(capacity); i += stride) table[i].key = empty_key<KeyT>();
+  // whole slots (one aligned 8- or 16-byte store each), the row index zeroed
+  Slot<KeyT> empty{};
+  empty.key = empty_key<KeyT>();
+  for (int64_t i = t0; i < int64_t(capacity); i += stride) table[i] = empty;
 }
 
 template <typename KeyT>

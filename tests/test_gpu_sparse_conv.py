@@ -174,3 +174,73 @@ def test_autograd_and_determinism(ssc):
     assert torch.equal(X.grad, ref[0]) and torch.equal(W.grad, ref[1]) and torch.equal(b.grad, ref[2])
     again = ssc.sparse_conv3d_bwd(plan, X.detach(), W.detach(), dY)
     assert all(torch.equal(a, c) for a, c in zip(ref, again))
+
+
+def test_row_range_weight_gradient_chunks(ssc):
+    """More than 1024 blocks of 256 output rows at 64 channels: the weight gradient chunks by row ranges."""
+    shape = (2, 128, 128, 128)
+    coords = _grid(31, shape, 0.15)
+    plan, _ = _check(ssc, coords, shape, 2, 2, 0, 64, 64, "f16")
+    assert plan.n_out > 1024 * 256
+
+
+@pytest.mark.parametrize("two_streams", [False, True], ids=["one_stream", "two_streams"])
+def test_graph_replay_matches_eager(ssc, two_streams):
+    """Map build + fwd + bwd captured once and replayed with eager work in between equals eager runs;
+    two_streams runs the input gradient and the weight gradient concurrently on one workspace."""
+    shape = (2, 30, 26, 28)
+    coords = _grid(44, shape, 0.2, shuffle=True)
+    ks, s, p = 3, 2, 1
+    print(f"[case] strided graph replay n_in={len(coords)} two_streams={two_streams}", flush=True)
+    ct = torch.from_numpy(coords).to(DEV)
+    ref_plan = ssc.build_sparse_map(ct, shape, ks, s, p)
+    X, W, b, dY = (t.to(DEV) for t in WL.strided_values(5, ref_plan.n_in, ref_plan.n_out, ks, 64, 32, "bf16"))
+    ref = [ssc.sparse_conv3d_fwd(ref_plan, X, W, b), *ssc.sparse_conv3d_bwd(ref_plan, X, W, dY)]
+    torch.cuda.synchronize()
+    plan = ssc.build_sparse_map(ct, shape, ks, s, p, out_coords=ref_plan.out_coords)
+    plan.nmap.zero_()
+    plan.perm.zero_()
+    plan.buf.zero_()
+    ws = ssc.sparse_workspace(plan, 64, 32, X.dtype)
+    out, dX, dW, db = (torch.empty_like(r) for r in ref)
+    L = ssc.lib()
+    P_ = ssc.binding._ptr
+    B_, Xd, Yd, Zd = shape
+    grad_side = torch.cuda.Stream(DEV)
+
+    def step():
+        r = L.ssc_build_sparse_map(P_(ct), plan.n_in, B_, Xd, Yd, Zd, P_(plan.out_coords), plan.n_out, ks, s, p, 0,
+                                   P_(plan.nmap), P_(plan.perm), P_(plan.buf), plan.buf.numel(),
+                                   ssc.binding._stream(DEV))
+        assert r == 0
+        ssc.sparse_conv3d_fwd(plan, X, W, b, out=out, ws=ws)
+        if two_streams:
+            cur = torch.cuda.current_stream(DEV)
+            grad_side.wait_stream(cur)
+            ssc.sparse_conv3d_bwd(plan, X, W, dY, ws=ws, outs=(dX, None, None))
+            with torch.cuda.stream(grad_side):
+                ssc.sparse_conv3d_bwd(plan, X, W, dY, ws=ws, outs=(None, dW, db))
+            cur.wait_stream(grad_side)
+        else:
+            ssc.sparse_conv3d_bwd(plan, X, W, dY, ws=ws, outs=(dX, dW, db))
+
+    side = torch.cuda.Stream(DEV)
+    side.wait_stream(torch.cuda.current_stream(DEV))
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream(DEV).wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(3):
+        for t in (out, dX, dW, db, plan.nmap, plan.perm):
+            t.zero_()
+        junk = (X.float() * 2).sum()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(plan.nmap, ref_plan.nmap) and torch.equal(plan.perm, ref_plan.perm)
+        for got, r in zip((out, dX, dW, db), ref):
+            assert torch.equal(got, r), f"replay {rep} differs"
+        del junk
