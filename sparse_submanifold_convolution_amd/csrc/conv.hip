@@ -157,7 +157,7 @@ __device__ __forceinline__ typename Elt<T>::frag_t a_frag(const u32x4 (&v)[NV], 
 // Split-K (nsplit > 1): work item (tile, column block, part) takes the part-th
 // contiguous share of the tile's offset set and writes fp32 partial sums, in
 // sorted row order, to partial[part][row][N]; split_reduce finishes them.
-template <typename T, int FM, int FN, int BK, int NWM, int NWN, int DEPTH, int KMAP>
+template <typename T, int FM, int FN, int BK, int NWM, int NWN, int DEPTH, int KMAP, int MW>
 __global__ void __launch_bounds__(64 * NWM * NWN)
     igemm(const T* __restrict__ A, const T* __restrict__ Bt, const T* __restrict__ bias, T* __restrict__ out,
           const uint32_t* __restrict__ snmap, const int32_t* __restrict__ perm,
@@ -188,7 +188,7 @@ __global__ void __launch_bounds__(64 * NWM * NWN)
   // XOR-swizzled so that both the row-major writes and the MFMA-order reads
   // of 8 lanes hit 8 distinct bank groups
   __shared__ __align__(16) T lds_a[KMAP == 2 ? NWM * FM * 32 * BK : 8];
-  __shared__ uint32_t jtab[BM * kV];  // [row][k]: this tile's rows of the sorted-order map
+  __shared__ uint32_t jtab[BM * MW];  // [row][column]: this tile's rows of the sorted-order map
   __shared__ int32_t prow[BM];
   __shared__ uint32_t tile_union;
   __shared__ uint32_t wave_union[NWM];  // offsets present among each wave row's rows
@@ -204,13 +204,13 @@ __global__ void __launch_bounds__(64 * NWM * NWN)
   // The tile's rows of the sorted-order map are one contiguous block; all of
   // its loads are issued before any is stored, so the prologue costs one
   // memory round trip, independent of perm.
-  constexpr int JV = (BM * kV + NT - 1) / NT;
+  constexpr int JV = (BM * MW + NT - 1) / NT;
   uint32_t jv[JV];
-  const int64_t jbase = row0 * kV, jend = n * kV;
+  const int64_t jbase = row0 * MW, jend = n * MW;
 #pragma unroll
   for (int q = 0; q < JV; ++q) {
     const int64_t e = jbase + q * NT + tid;
-    jv[q] = (q * NT + tid < BM * kV && e < jend) ? snmap[e] : kSentinel;
+    jv[q] = (q * NT + tid < BM * MW && e < jend) ? snmap[e] : kSentinel;
   }
   if (tid == 0) tile_union = 0;
   if (tid < NWM) wave_union[tid] = 0;
@@ -225,7 +225,7 @@ __global__ void __launch_bounds__(64 * NWM * NWN)
   }
 #pragma unroll
   for (int q = 0; q < JV; ++q)
-    if (q * NT + tid < BM * kV) jtab[q * NT + tid] = jv[q];
+    if (q * NT + tid < BM * MW) jtab[q * NT + tid] = jv[q];
   __syncthreads();
   if (tid < BM) {
     prow[tid] = pr;
@@ -304,7 +304,7 @@ __global__ void __launch_bounds__(64 * NWM * NWN)
 #pragma unroll
         for (int v = 0; v < NV; ++v) {
           const int rr = i * 32 + v * RPI + lane / LPR;
-          const uint32_t j = jtab[(wm * FM * 32 + rr) * kV + a_k] | ~live;
+          const uint32_t j = jtab[(wm * FM * 32 + rr) * MW + a_k] | ~live;
           const int64_t off = j != kSentinel ? (int64_t(j) * K + c0) * int64_t(sizeof(T)) : zoff;
           dst[i * NV + v] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(A) + off);
         }
@@ -313,7 +313,7 @@ __global__ void __launch_bounds__(64 * NWM * NWN)
       constexpr int vstride = KMAP == 0 ? 1 : 2;
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
-        const uint32_t j = jtab[(wm * FM * 32 + i * 32 + (lane & 31)) * kV + a_k] | ~live;
+        const uint32_t j = jtab[(wm * FM * 32 + i * 32 + (lane & 31)) * MW + a_k] | ~live;
         const int64_t off = j != kSentinel ? (int64_t(j) * K + c0) * int64_t(sizeof(T)) : zoff;
         const u32x4* src = reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(A) + off);
 #pragma unroll
@@ -328,7 +328,7 @@ __global__ void __launch_bounds__(64 * NWM * NWN)
     return q ^ ((q >> 3) & 7);
   };
   auto load_b = [&](u32x4 (&rb)[C::kBV]) {
-    const int kb = flip ? (kV - 1 - b_k) : b_k;
+    const int kb = flip ? (MW - 1 - b_k) : b_k;
     const int64_t base = (int64_t(kb) * N * K + b_ks * BK) * int64_t(sizeof(T));
     const int64_t zoff = reinterpret_cast<const char*>(zrow) - reinterpret_cast<const char*>(Bt);
     const int rlim = b_rem != 0 ? N - n0 : 0;  // rows at or past rlim read the zero row
@@ -1100,10 +1100,14 @@ static BwdShape bwd_shape(int64_t n, int Ci, int Co, int esize) {
   }
   s.mt = (Ci + s.bm - 1) / s.bm;
   s.nt = (Co + s.bn - 1) / s.bn;
-  // aim for about 2048 workgroups at P ~ 14 n valid pairs
+  // aim for about 2048 workgroups at P ~ 14 n valid pairs; small layers stop
+  // at a floor that keeps enough chunks in flight (measured on MI355X: the fp32
+  // kernel on 1.9k voxels 72 -> 29 us at 256 instead of 1024 pairs; the 16-bit
+  // kernel on 24k voxels 22.9 -> 21.3 us at 512, slower at 256)
   int64_t len = (14 * n * int64_t(s.mt) * s.nt + 2047) / 2048;
   len = (len + 255) / 256 * 256;
-  if (len < 1024) len = 1024;
+  const int64_t floor_len = esize == 2 ? 512 : 256;
+  if (len < floor_len) len = floor_len;
   if (len > (int64_t(1) << 20)) len = int64_t(1) << 20;
   s.chunk_len = len;
   s.max_chunks = int(n > 0 ? (n + len - 1) / len : 1);
@@ -1155,7 +1159,7 @@ static bool channels_ok(int Ci, int Co) {
   return Ci > 0 && Co > 0 && Ci % 16 == 0 && Co % 16 == 0 && Ci <= 4096 && Co <= 4096;
 }
 
-template <typename T, int FM, int FN, int BK, int NWM, int NWN, int DEPTH, int KMAP>
+template <typename T, int MW, int FM, int FN, int BK, int NWM, int NWN, int DEPTH, int KMAP>
 static void igemm_go(const T* A, const T* Bt, const T* bias, T* out, const uint32_t* nmap, const int32_t* perm,
                      const uint32_t* smask, const T* zrow, int64_t n, int K, int N, int flip, float* partial,
                      hipStream_t s) {
@@ -1165,7 +1169,7 @@ static void igemm_go(const T* A, const T* Bt, const T* bias, T* out, const uint3
   const int nsplit = split_parts(n, N);
   const int tgroup = nblk * nsplit == 1 ? kTileGroup : 1;
   const unsigned grid = xcd_group_grid((ntiles + tgroup - 1) / tgroup, tgroup * nblk * nsplit);
-  igemm<T, FM, FN, BK, NWM, NWN, DEPTH, KMAP><<<grid, 64 * NWM * NWN, 0, s>>>(
+  igemm<T, FM, FN, BK, NWM, NWN, DEPTH, KMAP, MW><<<grid, 64 * NWM * NWN, 0, s>>>(
       A, Bt, bias, out, nmap, perm, smask, zrow, n, K, N, flip, ntiles, nblk, nsplit, partial, tgroup);
   if (nsplit > 1)
     split_reduce<T><<<unsigned((n * N + 255) / 256), 256, 0, s>>>(partial, nsplit, n, N, bias, perm, out);
@@ -1178,14 +1182,14 @@ static void igemm_go(const T* A, const T* Bt, const T* bias, T* out, const uint3
 // workgroups) otherwise.  With 8 waves and a reduction of at most 128 (at most
 // two stages per offset, so the gathers dominate) the rows are gathered whole
 // (KMAP 2); wider reductions keep the register-only natural order.
-template <typename T, int FN>
+template <typename T, int MW, int FN>
 static void igemm_pick_rows(const T* A, const T* Bt, const T* bias, T* out, const uint32_t* nmap,
                             const int32_t* perm, const uint32_t* smask, const T* zrow, int64_t n, int K, int N,
                             int flip, float* partial, hipStream_t s) {
   const int64_t nblk = (N + FN * 32 - 1) / (FN * 32);
   const int64_t wg256 = (n + 255) / 256 * nblk, wg128 = (n + 127) / 128 * nblk;
 #define SSC_GO(NW, BK, DEPTH, KMAP) \
-  igemm_go<T, 1, FN, BK, NW, 1, DEPTH, KMAP>(A, Bt, bias, out, nmap, perm, smask, zrow, n, K, N, flip, partial, s)
+  igemm_go<T, MW, 1, FN, BK, NW, 1, DEPTH, KMAP>(A, Bt, bias, out, nmap, perm, smask, zrow, n, K, N, flip, partial, s)
 #define SSC_BK(NW, DEPTH)                                                 \
   do {                                                                    \
     if constexpr (sizeof(T) == 4) {                                       \
@@ -1215,14 +1219,26 @@ static void igemm_pick_rows(const T* A, const T* Bt, const T* bias, T* out, cons
 #undef SSC_GO
 }
 
-template <typename T>
+// MW: columns of the sorted-order map rows (27, or 8 for the compact map of a
+// 2x2x2 strided kernel); with flip the weight of column c is W[MW - 1 - c].
+template <typename T, int MW>
 static void launch_igemm(const T* A, const T* Bt, const T* bias, T* out, const uint32_t* nmap,
                          const int32_t* perm, const uint32_t* smask, const T* zrow, int64_t n, int K, int N,
                          int flip, float* partial, hipStream_t s) {
-  if (N > 128) igemm_pick_rows<T, 8>(A, Bt, bias, out, nmap, perm, smask, zrow, n, K, N, flip, partial, s);
-  else if (N > 64) igemm_pick_rows<T, 4>(A, Bt, bias, out, nmap, perm, smask, zrow, n, K, N, flip, partial, s);
-  else if (N > 32) igemm_pick_rows<T, 2>(A, Bt, bias, out, nmap, perm, smask, zrow, n, K, N, flip, partial, s);
-  else igemm_pick_rows<T, 1>(A, Bt, bias, out, nmap, perm, smask, zrow, n, K, N, flip, partial, s);
+  if (N > 128) igemm_pick_rows<T, MW, 8>(A, Bt, bias, out, nmap, perm, smask, zrow, n, K, N, flip, partial, s);
+  else if (N > 64) igemm_pick_rows<T, MW, 4>(A, Bt, bias, out, nmap, perm, smask, zrow, n, K, N, flip, partial, s);
+  else if (N > 32) igemm_pick_rows<T, MW, 2>(A, Bt, bias, out, nmap, perm, smask, zrow, n, K, N, flip, partial, s);
+  else igemm_pick_rows<T, MW, 1>(A, Bt, bias, out, nmap, perm, smask, zrow, n, K, N, flip, partial, s);
+}
+
+template <typename T>
+static void launch_igemm_w(int mw, const T* A, const T* Bt, const T* bias, T* out, const uint32_t* nmap,
+                           const int32_t* perm, const uint32_t* smask, const T* zrow, int64_t n, int K, int N,
+                           int flip, float* partial, hipStream_t s) {
+  if (mw == kCompactCols)
+    launch_igemm<T, kCompactCols>(A, Bt, bias, out, nmap, perm, smask, zrow, n, K, N, flip, partial, s);
+  else
+    launch_igemm<T, kV>(A, Bt, bias, out, nmap, perm, smask, zrow, n, K, N, flip, partial, s);
 }
 
 // dbias stage 1 geometry: column vectors (16 bytes) per work item, all of them
@@ -1307,6 +1323,10 @@ struct ConvView {
   const int32_t* perm_b = nullptr;
   int64_t n_b = 0;  // input rows
   int nk = kV;      // weight offsets
+  // sorted-order maps the GEMMs read and their row widths (NULL: the region's 27-wide snmap)
+  const uint32_t* map_f = nullptr;
+  const uint32_t* map_b = nullptr;
+  int mw = kV;
 };
 
 static size_t view_ws_bytes(const ConvView& v, int Ci, int Co, int esize) {
@@ -1330,8 +1350,8 @@ static int run_fwd(const ConvView& v, int Ci, int Co, const void* feats, const v
   T* wt = reinterpret_cast<T*>(ws + W.wt);
   dim3 tg(unsigned((Co + 31) / 32), unsigned((Ci + 31) / 32), unsigned(v.nk));
   transpose_w<T><<<tg, 256, 0, s>>>(static_cast<const T*>(weight), wt, Ci, Co);
-  launch_igemm<T>(static_cast<const T*>(feats), wt, static_cast<const T*>(bias), static_cast<T*>(out),
-                  reinterpret_cast<const uint32_t*>(v.fwd + L.snmap), v.perm_f,
+  launch_igemm_w<T>(v.mw, static_cast<const T*>(feats), wt, static_cast<const T*>(bias), static_cast<T*>(out),
+                  v.map_f ? v.map_f : reinterpret_cast<const uint32_t*>(v.fwd + L.snmap), v.perm_f,
                   reinterpret_cast<const uint32_t*>(v.fwd + L.smask), reinterpret_cast<const T*>(v.fwd + L.zrow),
                   v.n_f, Ci, Co, 0, reinterpret_cast<float*>(ws + W.split), s);
   return SSC_OK;
@@ -1349,8 +1369,8 @@ static int run_bwd(const ConvView& v, int Ci, int Co, const void* feats, const v
     if (v.n_f == 0) {
       zero_out<T>(static_cast<T*>(dfeats), v.n_b * Ci, s);  // no outputs: nothing reaches the inputs
     } else {
-      launch_igemm<T>(dY, static_cast<const T*>(weight), nullptr, static_cast<T*>(dfeats),
-                      reinterpret_cast<const uint32_t*>(v.bwd + Lb.snmap), v.perm_b,
+      launch_igemm_w<T>(v.mw, dY, static_cast<const T*>(weight), nullptr, static_cast<T*>(dfeats),
+                      v.map_b ? v.map_b : reinterpret_cast<const uint32_t*>(v.bwd + Lb.snmap), v.perm_b,
                       reinterpret_cast<const uint32_t*>(v.bwd + Lb.smask),
                       reinterpret_cast<const T*>(v.bwd + Lb.zrow), v.n_b, Co, Ci, 1,
                       reinterpret_cast<float*>(ws + Wb.split), s);
@@ -1468,10 +1488,16 @@ namespace {
 
 // The strided-conv plan's two GEMM regions (their starts depend on n_in and n_out only).
 ConvView sparse_view(const void* plan, int64_t n_in, int64_t n_out, int ks, const int32_t* perm_out) {
-  const SparseOffsets o = sparse_offsets(n_in, n_out);
+  const SparseOffsets o = sparse_offsets(n_in, n_out, ks);
   const char* base = static_cast<const char*>(plan);
-  return ConvView{base + o.fwd, perm_out, n_out, base + o.bwd,
-                  reinterpret_cast<const int32_t*>(base + o.perm_in), n_in, ks * ks * ks};
+  ConvView v{base + o.fwd, perm_out, n_out, base + o.bwd,
+             reinterpret_cast<const int32_t*>(base + o.perm_in), n_in, ks * ks * ks};
+  if (o.compact) {
+    v.map_f = reinterpret_cast<const uint32_t*>(base + o.cmap_f);
+    v.map_b = reinterpret_cast<const uint32_t*>(base + o.cmap_b);
+    v.mw = kCompactCols;
+  }
+  return v;
 }
 
 bool sparse_sizes_ok(int64_t n_in, int64_t n_out, int32_t ks) {

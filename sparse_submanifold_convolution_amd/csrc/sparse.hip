@@ -176,6 +176,19 @@ __global__ void __launch_bounds__(256) sparse_probe(const int4* __restrict__ coo
   tmap[int64_t(j) * kV + (kV - 1 - k)] = uint32_t(o);
 }
 
+// The compact copy of a sorted map for a 2x2x2 kernel: out[r][c] =
+// snmap[r][col0 + c] for c < 8; with smask given, row r's sorted mask moves
+// down by col0 to the same columns (one thread per row touches it).
+__global__ void __launch_bounds__(256) compact_map(const uint32_t* __restrict__ snmap, int64_t n, int col0,
+                                                   uint32_t* __restrict__ out, uint32_t* __restrict__ smask) {
+  const int64_t e = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (e >= n * kCompactCols) return;
+  const int64_t r = e / kCompactCols;
+  const int c = int(e - r * kCompactCols);
+  out[e] = snmap[r * kV + col0 + c];
+  if (smask && c == 0) smask[r] >>= col0;
+}
+
 }  // namespace ssc
 
 using namespace ssc;
@@ -276,7 +289,7 @@ extern "C" size_t ssc_sparse_plan_bytes(int64_t n_in, int64_t n_out, int32_t B, 
   if (!geometry_ok(B, X, Y, Z, ks, stride, pad, od)) return 0;
   int kb_in, kb_out;
   if (!sparse_keys(B, X, Y, Z, od, key_bits, &kb_in, &kb_out)) return 0;
-  return sparse_layout(n_in, n_out, kb_in, kb_out).total;
+  return sparse_layout(n_in, n_out, kb_in, kb_out, ks).total;
 }
 
 extern "C" int ssc_build_sparse_map(const int32_t* coords_in, int64_t n_in, int32_t B, int32_t X, int32_t Y,
@@ -294,7 +307,7 @@ extern "C" int ssc_build_sparse_map(const int32_t* coords_in, int64_t n_in, int3
   if (!geometry_ok(B, X, Y, Z, ks, stride, pad, od)) return SSC_ERR_INVALID_ARG;
   int kb_in, kb_out;
   if (!sparse_keys(B, X, Y, Z, od, key_bits, &kb_in, &kb_out)) return SSC_ERR_UNSUPPORTED;
-  const SparseLayout S = sparse_layout(n_in, n_out, kb_in, kb_out);
+  const SparseLayout S = sparse_layout(n_in, n_out, kb_in, kb_out, ks);
   if (plan_bytes < S.total) return SSC_ERR_WORKSPACE;
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -329,6 +342,17 @@ extern "C" int ssc_build_sparse_map(const int32_t* coords_in, int64_t n_in, int3
   // GEMM order, sorted maps and (forward direction) the pair lists the weight gradient walks
   order_rows(co, nmap, n_out, od[0], od[1], od[2], od[3], perm_out, fb, S.f, true, s);
   order_rows(ci, tmap, n_in, B, X, Y, Z, perm_in, bb, S.b, false, s);
+  if (S.o.compact) {
+    // 8-column copies for the GEMMs: the forward map's columns 0..7, the transposed map's 19..26
+    if (n_out > 0)
+      compact_map<<<blocks_for(n_out * kCompactCols, 256), 256, 0, s>>>(
+          reinterpret_cast<const uint32_t*>(fb + S.f.snmap), n_out, 0,
+          reinterpret_cast<uint32_t*>(base + S.o.cmap_f), nullptr);
+    if (n_in > 0)
+      compact_map<<<blocks_for(n_in * kCompactCols, 256), 256, 0, s>>>(
+          reinterpret_cast<const uint32_t*>(bb + S.b.snmap), n_in, kV - kCompactCols,
+          reinterpret_cast<uint32_t*>(base + S.o.cmap_b), reinterpret_cast<uint32_t*>(bb + S.b.smask));
+  }
   return hipGetLastError() == hipSuccess ? SSC_OK : SSC_ERR_HIP;
 }
 
@@ -336,7 +360,7 @@ extern "C" int ssc_sparse_plan_status(const void* plan, int64_t n_out, void* str
   if (!plan || !status_host || n_out < 0 || n_out > SSC_MAX_VOXELS) return SSC_ERR_INVALID_ARG;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (hipStreamSynchronize(s) != hipSuccess) return SSC_ERR_HIP;
-  const SparseOffsets o = sparse_offsets(0, n_out);  // the region starts depend on n_out only
+  const SparseOffsets o = sparse_offsets(0, n_out, 1);  // both headers' places depend on n_out only
   PlanHeader hf, hb;
   const char* base = static_cast<const char*>(plan);
   if (hipMemcpy(&hf, base + o.fwd, sizeof(hf), hipMemcpyDeviceToHost) != hipSuccess) return SSC_ERR_HIP;

@@ -171,16 +171,24 @@ inline PlanLayout relocate_scratch(PlanLayout L, size_t delta) {
 // backward region over the n_in input rows (sorted transposed map), the input
 // rows' GEMM order and the transposed map itself.  The build scratch of both
 // directions (hash tables, sort buffers) follows.
+// A 2x2x2 kernel (ks = 2) has 8 offsets: its GEMMs read compact 8-column
+// copies of the two sorted maps (the forward map's columns 0..7, the
+// transposed map's columns 19..26, whose masks are shifted down to match).
+constexpr int kCompactCols = 8;
 struct SparseOffsets {
-  size_t fwd = 0, bwd = 0, perm_in = 0, tmap = 0, conv_total = 0;
+  size_t fwd = 0, bwd = 0, perm_in = 0, tmap = 0, cmap_f = 0, cmap_b = 0, conv_total = 0;
+  bool compact = false;
 };
-inline SparseOffsets sparse_offsets(int64_t n_in, int64_t n_out) {
+inline SparseOffsets sparse_offsets(int64_t n_in, int64_t n_out, int ks) {
   SparseOffsets o;
+  o.compact = ks == 2;
   o.fwd = 0;
   o.bwd = align_up(conv_layout(n_out).total, 256);
   o.perm_in = align_up(o.bwd + conv_layout(n_in).total, 256);
   o.tmap = align_up(o.perm_in + size_t(n_in) * 4, 256);
-  o.conv_total = align_up(o.tmap + size_t(n_in) * kV * 4, 256);
+  o.cmap_f = align_up(o.tmap + size_t(n_in) * kV * 4, 256);
+  o.cmap_b = align_up(o.cmap_f + (o.compact ? size_t(n_out) * kCompactCols * 4 : 0), 256);
+  o.conv_total = align_up(o.cmap_b + (o.compact ? size_t(n_in) * kCompactCols * 4 : 0), 256);
   return o;
 }
 struct SparseLayout {
@@ -188,9 +196,9 @@ struct SparseLayout {
   PlanLayout f, b;  // relative to base + o.fwd and base + o.bwd, scratch relocated past conv_total
   size_t total = 0;
 };
-inline SparseLayout sparse_layout(int64_t n_in, int64_t n_out, int kb_in, int kb_out) {
+inline SparseLayout sparse_layout(int64_t n_in, int64_t n_out, int kb_in, int kb_out, int ks) {
   SparseLayout S;
-  S.o = sparse_offsets(n_in, n_out);
+  S.o = sparse_offsets(n_in, n_out, ks);
   const PlanLayout f = plan_layout(n_out, kb_out), b = plan_layout(n_in, kb_in);
   const size_t cf = conv_layout(n_out).total, cb = conv_layout(n_in).total;
   size_t off = S.o.conv_total;
