@@ -244,3 +244,10 @@ def test_graph_replay_matches_eager(ssc, two_streams):
         for got, r in zip((out, dX, dW, db), ref):
             assert torch.equal(got, r), f"replay {rep} differs"
         del junk
+
+
+def test_benchmarked_size_config3_downsample(ssc):
+    """The strided bench workload in full: config 3's 799,512 voxels, ks=2, stride 2, C=256, bf16."""
+    w = WL.make_workload(3, values=False)
+    plan, _ = _check(ssc, w.coords, w.shape, 2, 2, 0, 256, 256, "bf16", seed=1003)
+    assert plan.n_out == 199175
