@@ -116,7 +116,8 @@ __global__ void __launch_bounds__(256) os_mark(const int4* __restrict__ coords, 
   const uint64_t L = pack_key(c.x, ox, oy, oz, Xo, Yo, Zo);
   const uint32_t m = 1u << (L & 31u);
   uint32_t* w = bits + (L >> 5);
-  if (!(*w & m)) atomicOr(w, m);
+  // a relaxed atomic read first: a bit that is already set costs no atomic update
+  if (!(__hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & m)) atomicOr(w, m);
 }
 
 __global__ void __launch_bounds__(256) os_count(const uint32_t* __restrict__ bits, int64_t words,
