@@ -251,3 +251,11 @@ def test_benchmarked_size_config3_downsample(ssc):
     w = WL.make_workload(3, values=False)
     plan, _ = _check(ssc, w.coords, w.shape, 2, 2, 0, 256, 256, "bf16", seed=1003)
     assert plan.n_out == 199175
+
+
+def test_benchmarked_size_config4_downsample(ssc):
+    """The largest strided bench workload in full: config 4's 6,416,526 voxels (64-bit keys), ks=2, stride 2,
+    C=64, fp16 -- row-range weight-gradient chunks and 8-column maps at full size."""
+    w = WL.make_workload(4, values=False)
+    plan, _ = _check(ssc, w.coords, w.shape, 2, 2, 0, 64, 64, "f16", seed=1004, key_bits=w.key_bits)
+    assert plan.n_out == 1649179
