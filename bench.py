@@ -4,15 +4,20 @@ One step runs the whole path over one resident batch: build_neighbor_map
 (hash insert, probes, mask/z-order sort, pair lists), the forward masked
 implicit GEMM, the input-gradient GEMM and the Split-K weight gradient with
 dbias.  The headline value is effective TFLOP/s counting valid-neighbour MACs
-only (3 passes x 2 P Ci Co flops per step); voxels/s is reported beside it.
+only (3 passes x 2 P Ci Co flops per step); voxels/s is reported beside it,
+and so are the three passes on a built plan alone and the plan build alone
+(medians and minima over at least 20 event-timed repetitions).
 
-The roofline object covers the dominant kernel (the masked implicit GEMM,
-timed on its input-gradient launch, which is that kernel alone on the
-stream) or, when the workload's arithmetic intensity sits below the ridge,
+The default workload is the C = 1024 one (1 x 128^3 grid, every cell active
+with p = 0.3, bf16): the largest by valid work.  The roofline object covers
+the dominant kernel (the masked implicit GEMM, timed on the input-gradient
+call, which enqueues nothing but its launches) against the dense bf16 MFMA
+peak, or, when a workload's arithmetic intensity sits below the ridge,
 against HBM bandwidth with algorithmic bytes.  The oracle (CPU, float64) is
-timed on the host on the same workload as a reported baseline.
+timed on the host on a bounded sample of the same workload as a reported
+baseline.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 5]
 """
 from __future__ import annotations
 
@@ -30,7 +35,7 @@ if ROOT not in sys.path:
 METRIC = "effective TFLOP/s (valid MACs) + voxels/s, subm conv3d fwd+bwd, 1 MI355X"
 PEAK_HBM_GBS = 8000.0
 PEAK_TFLOPS = {"f32": 157.3, "f16": 2500.0, "bf16": 2500.0}
-DEFAULT_CONFIG = 2
+DEFAULT_CONFIG = 5
 
 
 def parse():
@@ -87,6 +92,19 @@ def measured_traffic(kernel: str, workload: str):
     return rec.get("bytes_per_launch")
 
 
+def measured_counters(kernel: str, workload: str):
+    """MFMA counters of the kernel's launches (profiles/counters.json), if taken on the current sources."""
+    path = os.path.join(ROOT, "profiles", "counters.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    rec = data.get(f"{kernel}|{workload}")
+    if not rec or rec.get("source_hash") != source_hash():
+        return None
+    return rec
+
+
 def copy_calibration(mib: int) -> None:
     import torch
     a = torch.empty(mib << 20, dtype=torch.uint8, device="cuda:0")
@@ -99,43 +117,94 @@ def copy_calibration(mib: int) -> None:
                       "bytes_written_per_launch": mib << 20}), flush=True)
 
 
-def cpu_baseline(w, budget_s: float) -> dict:
-    """The oracle as it stands (float64, numpy + BLAS) on the same workload, on the host."""
-    import numpy as np
-    from oracle import subm as O
+def host_cpu() -> dict:
+    """CPU model, the cores this process may run on and the BLAS thread count."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    cores = len(os.sched_getaffinity(0))
+    blas_threads = cores
     try:
         from threadpoolctl import threadpool_info
         blas = [t for t in threadpool_info() if t.get("user_api") == "blas"]
-        cores = int(blas[0]["num_threads"]) if blas else 1
-    except Exception:  # threadpoolctl missing: report the affinity set
-        cores = len(os.sched_getaffinity(0))
-    reps, t_total, flops = 0, 0.0, 0.0
-    t_stage = {"nmap": 0.0, "perm": 0.0, "fwd": 0.0, "dgrad": 0.0, "wgrad": 0.0}
-    while reps == 0 or (t_total < budget_s / 2 and reps < 5):
-        t0 = time.perf_counter()
-        nm = O.neighbor_map(w.coords, w.shape)
-        t1 = time.perf_counter()
-        O.sort_perm(w.coords, nm, w.shape)
-        t2 = time.perf_counter()
-        O.fwd(w.feats, w.weight, w.bias, nm)
-        t3 = time.perf_counter()
-        O.dgrad(w.dout, w.weight, nm)
-        t4 = time.perf_counter()
-        O.wgrad(w.feats, w.dout, nm)
-        O.dbias(w.dout)
-        t5 = time.perf_counter()
-        for k, v in zip(t_stage, (t1 - t0, t2 - t1, t3 - t2, t4 - t3, t5 - t4)):
-            t_stage[k] += v
-        t_total += t5 - t0
-        reps += 1
-        P = int((nm != O.SENTINEL).sum())
-        flops = 3 * 2.0 * P * w.ci * w.co
-    sec = t_total / reps
-    return {"value": flops / sec / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": f"whole workload (same {w.n} voxels, all three passes plus map and sort), "
-                      f"{reps} repetition(s), float64 numpy/BLAS",
-            "seconds_per_step": sec, "voxels_per_s": w.n / sec,
-            "stage_seconds": {k: v / reps for k, v in t_stage.items()}}
+        if blas:
+            blas_threads = int(blas[0]["num_threads"])
+    except Exception:  # threadpoolctl missing: BLAS uses the affinity set
+        pass
+    return {"cpu_model": model, "cores": cores, "blas_threads": blas_threads}
+
+
+def _oracle_step(O, coords, shape, X, W, b, dY) -> dict:
+    """One pass of the oracle over a voxel set: map, permutation, fwd, dgrad, wgrad + dbias (seconds)."""
+    t = {}
+    t0 = time.perf_counter()
+    nm = O.neighbor_map(coords, shape)
+    t["nmap"] = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    O.sort_perm(coords, nm, shape)
+    t["perm"] = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    O.fwd(X, W, b, nm)
+    t["fwd"] = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    O.dgrad(dY, W, nm)
+    t["dgrad"] = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    O.wgrad(X, dY, nm)
+    O.dbias(dY)
+    t["wgrad"] = time.perf_counter() - t0
+    t["pairs"] = int((nm != O.SENTINEL).sum())
+    return t
+
+
+def cpu_baseline(w, budget_s: float) -> dict:
+    """The oracle as it stands (float64, numpy + BLAS), timed on the host on a bounded sample.
+
+    The sample is the workload's own voxels in the slab x < t of every batch entry (a whole
+    sub-problem of the same distribution: map, sort and all three passes over those voxels, with
+    the same rounded values).  A thin slab is timed first; the slab is then widened so that one
+    pass of the oracle takes about `budget_s` (the whole workload when it fits), and that pass is
+    the reported figure, in the metric's unit (valid-MAC TFLOP/s of the sample).
+    """
+    import numpy as np
+    import torch
+    from oracle import subm as O
+    X_dim = int(w.shape[1])
+    x = w.coords[:, 1]
+
+    def slab(t):
+        sel = np.nonzero(x < t)[0]
+        idx = torch.from_numpy(sel)
+        return (np.ascontiguousarray(w.coords[sel]), w.feats.index_select(0, idx), w.dout.index_select(0, idx),
+                int(sel.size))
+
+    t0 = max(1, X_dim // 64)
+    c, Xs, dYs, n0 = slab(t0)
+    first = _oracle_step(O, c, w.shape, Xs, w.weight, w.bias, dYs)
+    sec0 = sum(v for k, v in first.items() if k != "pairs")
+    t1 = X_dim if sec0 <= 0 else int(min(X_dim, max(t0, t0 * budget_s / sec0)))
+    if t1 > t0:
+        c, Xs, dYs, n1 = slab(t1)
+        res = _oracle_step(O, c, w.shape, Xs, w.weight, w.bias, dYs)
+    else:
+        t1, n1, res = t0, n0, first
+    sec = sum(v for k, v in res.items() if k != "pairs")
+    flops = 3 * 2.0 * res["pairs"] * w.ci * w.co
+    whole = t1 >= X_dim
+    host = host_cpu()
+    return {"value": flops / sec / 1e12, "unit": "TFLOP/s", "cores": host["blas_threads"], "kind": "oracle",
+            "sample": ("whole workload" if whole else f"slab x < {t1} of {X_dim} in every batch entry")
+                      + f": {n1} of {w.n} voxels, {res['pairs']} valid pairs; neighbour map, permutation, "
+                        f"fwd, dgrad, wgrad + dbias, one pass, float64 numpy/BLAS",
+            "cpu_model": host["cpu_model"], "affinity_cores": host["cores"],
+            "seconds_per_sample_step": sec, "voxels_per_s": n1 / sec,
+            "stage_seconds": {k: v for k, v in res.items() if k != "pairs"}}
 
 
 def serialize_bench(args) -> None:
@@ -532,10 +601,11 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # per-call times of eagerly launched steps (HIP events on the stream the kernels run on)
+    # per-call times of eagerly launched steps: HIP events on the stream the kernels run on
+    # (torch's current stream, which the binding hands to every call), at least 20 repetitions
+    reps = max(20, args.steps)
     ev = {k: [] for k, _ in parts}
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
+    for _ in range(reps):
         for name, f in parts:
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
@@ -544,15 +614,21 @@ def main():
             e1.record(stream)
             ev[name].append((e0, e1))
     torch.cuda.synchronize()
-    wall_eager = time.perf_counter() - t0
-    ms = {k: float(np.mean([a.elapsed_time(c) for a, c in v])) for k, v in ev.items()}
-    ms_step_eager = wall_eager * 1e3 / args.steps
+    per = {k: [a.elapsed_time(c) for a, c in v] for k, v in ev.items()}
+    med = {k: float(np.median(v)) for k, v in per.items()}
+    mins = {k: float(np.min(v)) for k, v in per.items()}
 
+    # the timed region: exactly K whole steps (plan build + fwd + dgrad + wgrad), synchronised on both sides
     if args.no_graph:
-        ms_step = ms_step_eager
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
         mode = "eager launches"
     else:
-        # the whole step (plan build + fwd + both gradients) captured once and replayed
+        # the whole step captured once and replayed
         side = torch.cuda.Stream(dev)
         side.wait_stream(stream)
         with torch.cuda.stream(side):
@@ -571,17 +647,18 @@ def main():
         torch.cuda.synchronize()
         ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
         mode = "one captured HIP graph per step"
-        stream = torch.cuda.current_stream(dev)
 
     value = 3 * flops_pass / (ms_step * 1e-3) / 1e12
+    conv_ms = med["fwd"] + med["dgrad"] + med["wgrad"]
     esize = X.element_size()
-    # dominant kernel: the masked implicit GEMM, timed on its input-gradient launch (one kernel per call)
+    # dominant kernel: the masked implicit GEMM, timed on the input-gradient call, which enqueues
+    # nothing but its launches; one call = one pass of valid work
     kernel = "igemm"
     alg_bytes = 4.0 * P + esize * n * (ci + co) + esize * 27 * ci * co
     ai = flops_pass / alg_bytes
     peak_f = PEAK_TFLOPS[w.dtype]
     ridge = peak_f * 1e12 / (PEAK_HBM_GBS * 1e9)
-    t_k = ms["dgrad"] * 1e-3
+    t_k = med["dgrad"] * 1e-3
     wl_name = f"cfg{args.config}"
     traffic = measured_traffic(kernel, wl_name)
     if ai >= ridge:
@@ -592,9 +669,11 @@ def main():
         ach = alg_bytes / t_k / 1e9
         roof = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": ach / PEAK_HBM_GBS,
                 "traffic": traffic}
-    roof.update({"kernel": f"{kernel} (masked implicit GEMM, input-gradient launch)",
-                 "avg_launch_ms": ms["dgrad"], "flops_per_launch": flops_pass, "alg_bytes_per_launch": alg_bytes,
+    roof.update({"kernel": f"{kernel} (masked implicit GEMM, the input-gradient call's launches)",
+                 "call_ms_median": med["dgrad"], "call_ms_min": mins["dgrad"],
+                 "flops_per_call": flops_pass, "alg_bytes_per_call": alg_bytes,
                  "arith_intensity": ai, "ridge": ridge})
+    ctr = measured_counters(kernel, wl_name)
 
     line = {
         "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -604,9 +683,15 @@ def main():
                    "key_bits": w.key_bits or 32, "step": "neighbour-cache build + fwd + dgrad + wgrad + dbias",
                    "launch": mode, "parallelism": "single GPU"},
         "voxels_per_s": n / (ms_step * 1e-3),
-        "conv_only_tflops": 3 * flops_pass / ((ms["fwd"] + ms["dgrad"] + ms["wgrad"]) * 1e-3) / 1e12,
-        "breakdown_ms": ms,
-        "ms_per_step_eager": ms_step_eager,
+        # the three convolution passes on a built plan, and the plan build on its own (medians)
+        "conv_only": {"ms": conv_ms, "tflops": 3 * flops_pass / (conv_ms * 1e-3) / 1e12,
+                      "voxels_per_s": n / (conv_ms * 1e-3), "frac_of_peak": 3 * flops_pass / (conv_ms * 1e-3)
+                      / 1e12 / peak_f},
+        "plan_build_ms": {"median": med["plan"], "min": mins["plan"]},
+        "phase_ms": {"median": med, "min": mins, "repetitions": reps,
+                     "timing": "HIP events around each call of eagerly launched steps"},
+        "executed_over_valid": None if ctr is None else ctr.get("executed_over_valid"),
+        "mfma_busy": None if ctr is None else ctr.get("mfma_busy"),
         "roofline": roof,
     }
     if not args.no_cpu_baseline:

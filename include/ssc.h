@@ -136,7 +136,9 @@ size_t ssc_conv_workspace_bytes(int64_t n, int32_t Ci, int32_t Co, int32_t dtype
  *                     nmap itself is only checked (non-NULL, aligned).
  *   feats  [n][Ci], weight [27][Ci][Co], bias [Co] or NULL (zero), all `dtype`.
  *   out    [n][Co] `dtype`, out.
- * Ci and Co must be multiples of 16 and at most 4096.  The kernel walks
+ * Ci and Co must be multiples of 8 (fp16, bf16) or 4 (fp32), so that every
+ * row is whole 16-byte vectors, and at most 4096; otherwise
+ * SSC_ERR_UNSUPPORTED and nothing is enqueued.  The kernel walks
  * tiles of rows in perm order and, per tile, only the offsets some row of
  * the tile has; rows are gathered through the map, products run on MFMA with
  * fp32 accumulation, and out is rounded to `dtype` once.

@@ -172,6 +172,10 @@ __global__ void __launch_bounds__(64 * NWM * NWN)
   static_assert(KMAP != 2 || NWN == 1, "row-coalesced gathers keep each wave's rows private");
   // KMAP 2: lanes per gathered row segment and rows per load instruction
   constexpr int LPR = BK / C::kVec, RPI = 64 / LPR;
+  // The host picks BK = 64 or 32 only when it divides the reduction length K;
+  // the 16-wide slices also serve every other K (a multiple of 8 for 16-bit
+  // types, 4 for fp32), whose last slice is ragged.
+  constexpr bool RAG = BK == 16;
 
   // tgroup consecutive row tiles with all their column blocks (and Split-K
   // parts) run on one XCD: they gather overlapping neighbour rows
@@ -257,7 +261,7 @@ __global__ void __launch_bounds__(64 * NWM * NWN)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  const int kslices = K / BK;
+  const int kslices = (K + BK - 1) / BK;
   const int nstages = __popc(uni) * kslices;
   // A wave skips the MFMAs of a stage whose offset none of its rows has (its
   // loads still run and read the zero row), so only the tile's weight slices
@@ -314,10 +318,21 @@ __global__ void __launch_bounds__(64 * NWM * NWN)
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
         const uint32_t j = jtab[(wm * FM * 32 + i * 32 + (lane & 31)) * MW + a_k] | ~live;
-        const int64_t off = j != kSentinel ? (int64_t(j) * K + c0) * int64_t(sizeof(T)) : zoff;
-        const u32x4* src = reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(A) + off);
+        if constexpr (RAG) {
+          // a reduction length that is not a multiple of BK leaves the last
+          // slice ragged: its columns at or past K read zeros
 #pragma unroll
-        for (int v = 0; v < NV; ++v) dst[i * NV + v] = src[v * vstride];
+          for (int v = 0; v < NV; ++v) {
+            const int col = c0 + v * vstride * C::kVec;
+            const int64_t off = (j != kSentinel && col < K) ? (int64_t(j) * K + col) * int64_t(sizeof(T)) : zoff;
+            dst[i * NV + v] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(A) + off);
+          }
+        } else {
+          const int64_t off = j != kSentinel ? (int64_t(j) * K + c0) * int64_t(sizeof(T)) : zoff;
+          const u32x4* src = reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(A) + off);
+#pragma unroll
+          for (int v = 0; v < NV; ++v) dst[i * NV + v] = src[v * vstride];
+        }
       }
     }
     advance(a_rem, a_k, a_ks);
@@ -338,7 +353,8 @@ __global__ void __launch_bounds__(64 * NWM * NWN)
       const int idx = tid + v * NT;
       const int id = idx < BN * VPR ? idx : 0;  // surplus threads reload element 0 and store nothing
       const int r = id / VPR, cv = id % VPR;
-      const int64_t off = (r < rlim ? base + int64_t(n0 + r) * K * int64_t(sizeof(T)) : zoff) + cv * 16;
+      const bool in = r < rlim && (!RAG || b_ks * BK + cv * C::kVec < K);  // ragged last slice: zeros past K
+      const int64_t off = in ? base + int64_t(n0 + r) * K * int64_t(sizeof(T)) + cv * 16 : zoff;
       rb[v] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(Bt) + off);
     }
     advance(b_rem, b_k, b_ks);
@@ -1155,8 +1171,11 @@ static WsLayout ws_layout(int64_t n_f, int64_t n_b, int Ci, int Co, int esize) {
 
 static int esize_of(int dtype) { return dtype == SSC_F32 ? 4 : 2; }
 
-static bool channels_ok(int Ci, int Co) {
-  return Ci > 0 && Co > 0 && Ci % 16 == 0 && Co % 16 == 0 && Ci <= 4096 && Co <= 4096;
+// Every row of X, dY, W and dW starts 16-byte aligned, so that each gather is
+// whole 16-byte vectors: channel counts are multiples of 8 (16-bit) or 4 (fp32).
+static bool channels_ok(int Ci, int Co, int dtype) {
+  const int vec = dtype == SSC_F32 ? 4 : 8;
+  return Ci > 0 && Co > 0 && Ci % vec == 0 && Co % vec == 0 && Ci <= 4096 && Co <= 4096;
 }
 
 template <typename T, int MW, int FM, int FN, int BK, int NWM, int NWN, int DEPTH, int KMAP>
@@ -1431,8 +1450,8 @@ static void by_dtype(int dtype, F&& f) {
 using namespace ssc;
 
 extern "C" size_t ssc_conv_workspace_bytes(int64_t n, int32_t Ci, int32_t Co, int32_t dtype) {
-  if (n < 0 || n > SSC_MAX_VOXELS || !channels_ok(Ci, Co)) return 0;
   if (dtype != SSC_F32 && dtype != SSC_F16 && dtype != SSC_BF16) return 0;
+  if (n < 0 || n > SSC_MAX_VOXELS || !channels_ok(Ci, Co, dtype)) return 0;
   return ws_layout(n, n, Ci, Co, esize_of(dtype)).total;
 }
 
@@ -1442,7 +1461,7 @@ extern "C" int ssc_subm_conv3d_fwd(const void* plan, const uint32_t* nmap, const
                                    void* stream) {
   if (n < 0 || n > SSC_MAX_VOXELS || !plan || !weight) return SSC_ERR_INVALID_ARG;
   if (dtype != SSC_F32 && dtype != SSC_F16 && dtype != SSC_BF16) return SSC_ERR_UNSUPPORTED;
-  if (!channels_ok(Ci, Co)) return SSC_ERR_UNSUPPORTED;
+  if (!channels_ok(Ci, Co, dtype)) return SSC_ERR_UNSUPPORTED;
   if (n > 0 && (!nmap || !perm || !feats || !out || !workspace)) return SSC_ERR_INVALID_ARG;
   const void* ptrs[] = {plan, nmap, perm, feats, weight, bias, out, workspace};
   for (const void* p : ptrs)
@@ -1464,7 +1483,7 @@ extern "C" int ssc_subm_conv3d_bwd(const void* plan, const uint32_t* nmap, const
                                    size_t workspace_bytes, void* stream) {
   if (n < 0 || n > SSC_MAX_VOXELS || !plan) return SSC_ERR_INVALID_ARG;
   if (dtype != SSC_F32 && dtype != SSC_F16 && dtype != SSC_BF16) return SSC_ERR_UNSUPPORTED;
-  if (!channels_ok(Ci, Co)) return SSC_ERR_UNSUPPORTED;
+  if (!channels_ok(Ci, Co, dtype)) return SSC_ERR_UNSUPPORTED;
   if (dfeats && !weight) return SSC_ERR_INVALID_ARG;
   if (n > 0 && (!nmap || !perm || !dout || (dweight && !feats))) return SSC_ERR_INVALID_ARG;
   if ((dfeats || dweight || dbias) && !workspace) return SSC_ERR_INVALID_ARG;
@@ -1508,8 +1527,8 @@ bool sparse_sizes_ok(int64_t n_in, int64_t n_out, int32_t ks) {
 
 extern "C" size_t ssc_sparse_conv_workspace_bytes(int64_t n_in, int64_t n_out, int32_t Ci, int32_t Co,
                                                   int32_t dtype) {
-  if (!sparse_sizes_ok(n_in, n_out, 1) || !channels_ok(Ci, Co)) return 0;
   if (dtype != SSC_F32 && dtype != SSC_F16 && dtype != SSC_BF16) return 0;
+  if (!sparse_sizes_ok(n_in, n_out, 1) || !channels_ok(Ci, Co, dtype)) return 0;
   ConvView v;
   v.n_f = n_out;
   v.n_b = n_in;
@@ -1522,7 +1541,7 @@ extern "C" int ssc_sparse_conv3d_fwd(const void* plan, int64_t n_in, int64_t n_o
                                      void* workspace, size_t workspace_bytes, void* stream) {
   if (!sparse_sizes_ok(n_in, n_out, ks) || !plan || !weight) return SSC_ERR_INVALID_ARG;
   if (dtype != SSC_F32 && dtype != SSC_F16 && dtype != SSC_BF16) return SSC_ERR_UNSUPPORTED;
-  if (!channels_ok(Ci, Co)) return SSC_ERR_UNSUPPORTED;
+  if (!channels_ok(Ci, Co, dtype)) return SSC_ERR_UNSUPPORTED;
   if (n_out > 0 && (!perm_out || !out || !workspace || (n_in > 0 && !feats))) return SSC_ERR_INVALID_ARG;
   const void* ptrs[] = {plan, perm_out, feats, weight, bias, out, workspace};
   for (const void* p : ptrs)
@@ -1544,7 +1563,7 @@ extern "C" int ssc_sparse_conv3d_bwd(const void* plan, int64_t n_in, int64_t n_o
                                      void* stream) {
   if (!sparse_sizes_ok(n_in, n_out, ks) || !plan) return SSC_ERR_INVALID_ARG;
   if (dtype != SSC_F32 && dtype != SSC_F16 && dtype != SSC_BF16) return SSC_ERR_UNSUPPORTED;
-  if (!channels_ok(Ci, Co)) return SSC_ERR_UNSUPPORTED;
+  if (!channels_ok(Ci, Co, dtype)) return SSC_ERR_UNSUPPORTED;
   if (dfeats && !weight) return SSC_ERR_INVALID_ARG;
   if (n_out > 0 && (!perm_out || !dout || (dweight && n_in > 0 && !feats))) return SSC_ERR_INVALID_ARG;
   if ((dfeats || dweight || dbias) && !workspace) return SSC_ERR_INVALID_ARG;

@@ -59,8 +59,14 @@ def test_plan_bytes_validation(L):
 
 def test_workspace_bytes_validation(L):
     assert L.ssc_conv_workspace_bytes(1000, 64, 64, 1) > 0
-    assert L.ssc_conv_workspace_bytes(1000, 24, 64, 1) == 0     # not a multiple of 16
-    assert L.ssc_conv_workspace_bytes(1000, 64, 8, 0) == 0
+    # rows must be whole 16-byte vectors: multiples of 8 channels (16-bit), 4 (fp32)
+    assert L.ssc_conv_workspace_bytes(1000, 24, 64, 1) > 0
+    assert L.ssc_conv_workspace_bytes(1000, 8, 40, 2) > 0
+    assert L.ssc_conv_workspace_bytes(1000, 32, 8, 0) > 0       # the pages' cached fp32 layer
+    assert L.ssc_conv_workspace_bytes(1000, 4, 12, 0) > 0
+    assert L.ssc_conv_workspace_bytes(1000, 12, 64, 1) == 0     # 24-byte fp16 rows
+    assert L.ssc_conv_workspace_bytes(1000, 64, 4, 2) == 0      # 8-byte bf16 rows
+    assert L.ssc_conv_workspace_bytes(1000, 64, 6, 0) == 0      # 24-byte fp32 rows
     assert L.ssc_conv_workspace_bytes(1000, 64, 64, 3) == 0     # unknown dtype
     assert L.ssc_conv_workspace_bytes(1000, 8192, 64, 2) == 0   # too wide
 
@@ -84,14 +90,16 @@ def test_build_rejects_on_host(L):
 def test_conv_rejects_on_host(L):
     f = L.ssc_subm_conv3d_fwd
     assert f(FAKE, FAKE, FAKE, 100, 32, 32, 5, FAKE, FAKE, None, FAKE, FAKE, 1 << 30, None) == 2   # dtype
-    assert f(FAKE, FAKE, FAKE, 100, 20, 32, 0, FAKE, FAKE, None, FAKE, FAKE, 1 << 30, None) == 2   # Ci % 16
+    assert f(FAKE, FAKE, FAKE, 100, 18, 32, 0, FAKE, FAKE, None, FAKE, FAKE, 1 << 30, None) == 2   # fp32 Ci % 4
+    assert f(FAKE, FAKE, FAKE, 100, 32, 20, 1, FAKE, FAKE, None, FAKE, FAKE, 1 << 30, None) == 2   # fp16 Co % 8
     assert f(FAKE, FAKE, FAKE, 100, 32, 32, 0, FAKE, FAKE, None, FAKE, FAKE, 64, None) == 3        # workspace
     assert f(FAKE, FAKE, FAKE, 100, 32, 32, 0, None, FAKE, None, FAKE, FAKE, 1 << 30, None) == 1   # feats NULL
     assert f(FAKE, FAKE, FAKE, -1, 32, 32, 0, FAKE, FAKE, None, FAKE, FAKE, 1 << 30, None) == 1
     b = L.ssc_subm_conv3d_bwd
     assert b(FAKE, FAKE, FAKE, 100, 32, 32, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 64, None) == 3
     assert b(FAKE, FAKE, FAKE, 100, 32, 32, 0, None, FAKE, FAKE, None, FAKE, None, FAKE, 1 << 30, None) == 1
-    assert b(FAKE, FAKE, FAKE, 100, 32, 40, 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == 2
+    assert b(FAKE, FAKE, FAKE, 100, 32, 44, 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == 2
+    assert b(FAKE, FAKE, FAKE, 100, 36, 32, 2, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == 2
 
 
 def test_binding_raises_without_library(monkeypatch):
@@ -171,7 +179,8 @@ def test_sparse_conv_sizes_and_rejections(L):
     assert L.ssc_sparse_plan_bytes(-1, 50, 1, 32, 32, 32, 2, 2, 0, 0) == 0
     assert L.ssc_sparse_plan_bytes(0, 0, 1, 32, 32, 32, 2, 2, 0, 0) > 0
     assert L.ssc_sparse_conv_workspace_bytes(1000, 200, 64, 128, 1) > 0
-    assert L.ssc_sparse_conv_workspace_bytes(1000, 200, 64, 24, 1) == 0
+    assert L.ssc_sparse_conv_workspace_bytes(1000, 200, 64, 24, 1) > 0
+    assert L.ssc_sparse_conv_workspace_bytes(1000, 200, 64, 20, 1) == 0
     cnt = ctypes.c_void_p(0x10008)
     assert L.ssc_sparse_out_count(None, 10, 1, 8, 8, 8, 2, 2, 0, FAKE, 1 << 30, cnt, None) == 1
     assert L.ssc_sparse_out_count(FAKE, 10, 1, 8, 8, 8, 2, 2, 0, FAKE, 16, cnt, None) == 3

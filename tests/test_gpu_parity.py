@@ -161,6 +161,26 @@ SMALL = [
     (9, 1, (3, 3, 3), 0.04, 64, 16, "f16", False),      # one or two voxels
 ]
 
+# Channel counts that are whole 16-byte rows but not multiples of 16: the
+# reduction's last K-slice is ragged (zeros past K) and the column blocks are
+# partly empty.  (32, 8, fp32) is the layer of the pages' autotune-cache entry.
+NARROW = [
+    (51, 1, (12, 12, 12), 0.3, 32, 8, "f32", False),
+    (52, 2, (10, 11, 9), 0.35, 8, 24, "f16", True),
+    (53, 1, (14, 13, 12), 0.3, 40, 8, "bf16", False),
+    (54, 1, (9, 9, 9), 0.4, 4, 12, "f32", True),
+    (55, 2, (10, 10, 10), 0.3, 24, 40, "bf16", True),
+    (56, 1, (40, 40, 40), 0.3, 72, 8, "f16", False),     # 19k rows: 4-wave tiles, ragged reduction
+    (57, 1, (64, 64, 64), 0.55, 8, 40, "bf16", True),   # over 512 tiles of 256: 8-wave tiles
+]
+
+
+@pytest.mark.parametrize("case", NARROW, ids=[f"c{c[4]}x{c[5]}_{c[6]}" for c in NARROW])
+def test_narrow_channel_parity(ssc, case):
+    seed, B, dims, p, ci, co, dt, shuffle = case
+    w = WL.random_workload(seed, B, dims, p, ci, co, dt, random_bias=True, shuffle=shuffle)
+    _full_parity(ssc, w)
+
 
 @pytest.mark.parametrize("case", SMALL, ids=[f"s{c[0]}" for c in SMALL])
 def test_small_parity(ssc, case):

@@ -98,11 +98,18 @@ def test_geometries(ssc, ks, s, p, dtype):
     _check(ssc, coords, (2, 20, 18, 22), ks, s, p, 32, 48, dtype)
 
 
-@pytest.mark.parametrize("ci,co", [(16, 16), (64, 128), (256, 64)])
+@pytest.mark.parametrize("ci,co", [(16, 16), (64, 128), (256, 64), (8, 24), (40, 8)])
 def test_channels_several_tiles(ssc, ci, co):
     # a few thousand outputs: several GEMM tiles and a ragged tail
     coords = _grid(4, (2, 40, 40, 40), 0.2)
     _check(ssc, coords, (2, 40, 40, 40), 2, 2, 0, ci, co, "bf16")
+
+
+def test_narrow_fp32_channels(ssc):
+    # 16-byte fp32 rows (4 channels) and the pages' cached layer width (32 -> 8)
+    coords = _grid(6, (1, 24, 24, 24), 0.2, shuffle=True)
+    _check(ssc, coords, (1, 24, 24, 24), 3, 2, 1, 4, 12, "f32")
+    _check(ssc, coords, (1, 24, 24, 24), 2, 2, 0, 32, 8, "f32")
 
 
 def test_downsample_of_a_shell_workload(ssc):
