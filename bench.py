@@ -592,6 +592,7 @@ def main():
     counts = ssc.plan_pair_counts(plan)
     P = sum(counts)
     flops_pass = 2.0 * P * ci * co
+    orders, union_rows, mask_bits = ssc.plan_row_orders(plan)
 
     def step():
         for _, f in parts:
@@ -681,7 +682,7 @@ def main():
         "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": f"config {args.config}: {w.desc}", "voxels": n, "valid_pairs": P, "ci": ci, "co": co,
                    "key_bits": w.key_bits or 32, "step": "neighbour-cache build + fwd + dgrad + wgrad + dbias",
-                   "launch": mode, "parallelism": "single GPU"},
+                   "launch": mode, "parallelism": "single GPU", "gemm_row_orders": orders},
         "voxels_per_s": n / (ms_step * 1e-3),
         # the three convolution passes on a built plan, and the plan build on its own (medians)
         "conv_only": {"ms": conv_ms, "tflops": 3 * flops_pass / (conv_ms * 1e-3) / 1e12,
@@ -691,6 +692,9 @@ def main():
         "phase_ms": {"median": med, "min": mins, "repetitions": reps,
                      "timing": "HIP events around each call of eagerly launched steps"},
         "executed_over_valid": None if ctr is None else ctr.get("executed_over_valid"),
+        # rows multiplied by a single (mask, z-order) order's 32-row waves per valid pair, as the build counted
+        # them (only counted where the build considers a second order)
+        "single_order_rows_over_valid": (union_rows / mask_bits) if mask_bits else None,
         "mfma_busy": None if ctr is None else ctr.get("mfma_busy"),
         "roofline": roof,
     }

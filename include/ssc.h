@@ -25,7 +25,8 @@
  * Conventions for every call:
  *  - Pointers are device pointers unless the argument says "host".
  *  - Every call only enqueues work on `stream` (a hipStream_t; NULL is the
- *    null stream) and returns; ssc_plan_status and ssc_plan_pair_counts
+ *    null stream) and returns; ssc_plan_status, ssc_plan_pair_counts and
+ *    ssc_plan_row_orders
  *    also synchronise that stream.
  *  - The caller owns and allocates every buffer (coords, nmap, perm, plan,
  *    workspace, outputs).  The library never allocates device memory, keeps
@@ -120,6 +121,21 @@ int ssc_plan_status(const void* plan, void* stream, int32_t* status_host);
  * 2 * P * Ci * Co useful flops.
  */
 int ssc_plan_pair_counts(const void* plan, void* stream, int64_t* counts_host);
+
+/*
+ * Synchronise `stream` and describe how the built plan orders rows for the
+ * masked GEMMs (the pages' sorted_idx and per-block valid offsets: the Triton
+ * compile-cache post, section six, kernel signature).  orders_host[0] (host)
+ * receives 1 when every offset runs in the one (mask, z-order) row order, or
+ * 2 when the build also sorted the rows by the mask of the offsets 0..12 alone
+ * and the wide-channel fwd / input-gradient GEMMs run those offsets in that
+ * second order (and the offsets 13..26 in the first).  orders_host[1] and
+ * orders_host[2] receive the two sums the build decided it from: 32 times the
+ * offsets present in each 32-row group of the first order, summed over the
+ * groups, and the valid pairs P (both 0 when the build did not consider it).
+ * The results never depend on it.
+ */
+int ssc_plan_row_orders(const void* plan, void* stream, int64_t* orders_host);
 
 /*
  * Bytes of workspace ssc_subm_conv3d_fwd and ssc_subm_conv3d_bwd need for

@@ -26,6 +26,7 @@ SIGNATURES = {
     "ssc_build_neighbor_map": (ctypes.c_int, [_VP, _I64, _I32, _I32, _I32, _I32, _I32, _VP, _VP, _VP, _SZ, _VP]),
     "ssc_plan_status": (ctypes.c_int, [_VP, _VP, ctypes.POINTER(_I32)]),
     "ssc_plan_pair_counts": (ctypes.c_int, [_VP, _VP, ctypes.POINTER(_I64)]),
+    "ssc_plan_row_orders": (ctypes.c_int, [_VP, _VP, ctypes.POINTER(_I64)]),
     "ssc_conv_workspace_bytes": (_SZ, [_I64, _I32, _I32, _I32]),
     "ssc_subm_conv3d_fwd": (ctypes.c_int, [_VP, _VP, _VP, _I64, _I32, _I32, _I32, _VP, _VP, _VP, _VP, _VP, _SZ, _VP]),
     "ssc_subm_conv3d_bwd": (ctypes.c_int, [_VP, _VP, _VP, _I64, _I32, _I32, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
@@ -164,6 +165,13 @@ def plan_pair_counts(plan: Plan) -> list[int]:
     arr = (ctypes.c_int64 * 27)()
     _check("ssc_plan_pair_counts", lib().ssc_plan_pair_counts(_ptr(plan.buf), _stream(plan.device), arr))
     return [int(v) for v in arr]
+
+
+def plan_row_orders(plan: Plan) -> tuple[int, int, int]:
+    """(row orders the GEMMs use: 1 or 2, the first order's 32-row group sum, the valid pairs)."""
+    arr = (ctypes.c_int64 * 3)()
+    _check("ssc_plan_row_orders", lib().ssc_plan_row_orders(_ptr(plan.buf), _stream(plan.device), arr))
+    return int(arr[0]), int(arr[1]), int(arr[2])
 
 
 # ---------------------------------------------------------------------------

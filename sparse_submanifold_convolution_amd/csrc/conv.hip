@@ -157,12 +157,29 @@ __device__ __forceinline__ typename Elt<T>::frag_t a_frag(const u32x4 (&v)[NV], 
 // Split-K (nsplit > 1): work item (tile, column block, part) takes the part-th
 // contiguous share of the tile's offset set and writes fp32 partial sums, in
 // sorted row order, to partial[part][row][N]; split_reduce finishes them.
+// One launch may cover only some offsets and hand its sums to another (the
+// two-part split of the plan header's part_split): `kmask` keeps the offsets
+// of this launch (map columns), `gate` makes the launch a no-op unless the
+// plan took the split (1) or did not (2), and `emode` picks the epilogue:
+// 0 bias + rounding + scatter to perm, 1 fp32 sums to pbuf[perm[r]], 2 those
+// sums + this launch's + bias, rounded, to out.  With flip, map column c
+// meets weight W[kflip - c].
+struct GemmPart {
+  const PlanHeader* hdr;
+  int gate;
+  uint32_t kmask;
+  int kflip;
+  int emode;
+  float* pbuf;
+};
+
 template <typename T, int FM, int FN, int BK, int NWM, int NWN, int DEPTH, int KMAP, int MW>
 __global__ void __launch_bounds__(64 * NWM * NWN)
     igemm(const T* __restrict__ A, const T* __restrict__ Bt, const T* __restrict__ bias, T* __restrict__ out,
           const uint32_t* __restrict__ snmap, const int32_t* __restrict__ perm,
           const uint32_t* __restrict__ smask, const T* __restrict__ zrow, int64_t n, int K, int N, int flip,
-          int ntiles, int nblk_n, int nsplit, float* __restrict__ partial, int tgroup) {
+          int ntiles, int nblk_n, int nsplit, float* __restrict__ partial, int tgroup, GemmPart gp) {
+  if (gp.gate != 0 && (gp.hdr->part_split != 0u) != (gp.gate == 1)) return;
   using C = IgemmCfg<T, FM, FN, BK, NWM, NWN>;
   using E = Elt<T>;
   using frag_t = typename E::frag_t;
@@ -224,7 +241,7 @@ __global__ void __launch_bounds__(64 * NWM * NWN)
     const int64_t g = row0 + tid;
     if (g < n) {
       pr = perm[g];
-      msk = smask[g];
+      msk = smask[g] & gp.kmask;
     }
   }
 #pragma unroll
@@ -343,7 +360,7 @@ __global__ void __launch_bounds__(64 * NWM * NWN)
     return q ^ ((q >> 3) & 7);
   };
   auto load_b = [&](u32x4 (&rb)[C::kBV]) {
-    const int kb = flip ? (MW - 1 - b_k) : b_k;
+    const int kb = flip ? (gp.kflip - b_k) : b_k;
     const int64_t base = (int64_t(kb) * N * K + b_ks * BK) * int64_t(sizeof(T));
     const int64_t zoff = reinterpret_cast<const char*>(zrow) - reinterpret_cast<const char*>(Bt);
     const int rlim = b_rem != 0 ? N - n0 : 0;  // rows at or past rlim read the zero row
@@ -457,7 +474,24 @@ __global__ void __launch_bounds__(64 * NWM * NWN)
     return;
   }
 
-  // ---- epilogue: bias, round once, scatter rows to perm ----
+  if (gp.emode == 1) {
+    // first part of a split: fp32 sums by original row, no bias
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int c = n0 + (wn * FN + j) * 32 + (lane & 31);
+      if (c >= N) continue;
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int32_t p = prow[wm * FM * 32 + i * 32 + acc_row(lane, e)];
+          if (p >= 0) gp.pbuf[int64_t(p) * N + c] = acc[i][j][e];
+        }
+    }
+    return;
+  }
+
+  // ---- epilogue: bias (and the first part's sums), round once, scatter rows to perm ----
 #pragma unroll
   for (int j = 0; j < FN; ++j) {
     const int c = n0 + (wn * FN + j) * 32 + (lane & 31);
@@ -465,11 +499,16 @@ __global__ void __launch_bounds__(64 * NWM * NWN)
     const float bv = bias ? E::load(bias[c]) : 0.f;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
+      float prev[16];
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int r = wm * FM * 32 + i * 32 + acc_row(lane, e);
-        const int32_t p = prow[r];
-        if (p >= 0) out[int64_t(p) * N + c] = E::store(acc[i][j][e] + bv);
+        const int32_t p = prow[wm * FM * 32 + i * 32 + acc_row(lane, e)];
+        prev[e] = (gp.emode == 2 && p >= 0) ? gp.pbuf[int64_t(p) * N + c] : 0.f;
+      }
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int32_t p = prow[wm * FM * 32 + i * 32 + acc_row(lane, e)];
+        if (p >= 0) out[int64_t(p) * N + c] = E::store(acc[i][j][e] + prev[e] + bv);
       }
     }
   }
@@ -1142,14 +1181,21 @@ static BwdShape bwd_shape(int64_t n, int Ci, int Co, int esize) {
 }
 
 struct WsLayout {
-  size_t wt = 0, partial = 0, bias = 0, split = 0, total = 0;
+  size_t wt = 0, partial = 0, bias = 0, split = 0, part = 0, total = 0;
 };
+
+// Whether a submanifold layer of n rows may run its fwd / input-gradient GEMMs
+// in two parts (the plan decides on the device whether it does): 16-bit types,
+// many rows, wide channels on both sides.
+static bool parts_possible(int64_t n, int Ci, int Co, int esize) {
+  return esize == 2 && n >= kPartMinRows && Ci >= kPartMinChannels && Co >= kPartMinChannels;
+}
 
 // n_f: rows of the forward GEMM and of the weight gradient's pair lists (the
 // output rows); n_b: rows of the input-gradient GEMM (the input rows).  Every
 // region is disjoint, so the input gradient and the weight gradient may run
 // concurrently on one workspace.
-static WsLayout ws_layout(int64_t n_f, int64_t n_b, int Ci, int Co, int esize) {
+static WsLayout ws_layout(int64_t n_f, int64_t n_b, int Ci, int Co, int esize, bool parts) {
   WsLayout w;
   const BwdShape b = bwd_shape(n_f, Ci, Co, esize);
   size_t off = 0;
@@ -1165,6 +1211,10 @@ static WsLayout ws_layout(int64_t n_f, int64_t n_b, int Ci, int Co, int esize) {
   const size_t sbytes_d = sd > 1 ? size_t(sd) * size_t(n_b) * Ci * 4 : 0;
   w.split = off;
   off = align_up(off + (sbytes_f > sbytes_d ? sbytes_f : sbytes_d), 256);
+  // fp32 sums handed from the first GEMM part to the second ([n][Co] fwd, [n][Ci] dX)
+  w.part = off;
+  if (parts && parts_possible(n_f, Ci, Co, esize))
+    off = align_up(off + size_t(n_f) * size_t(Ci > Co ? Ci : Co) * 4, 256);
   w.total = off;
   return w;
 }
@@ -1181,7 +1231,7 @@ static bool channels_ok(int Ci, int Co, int dtype) {
 template <typename T, int MW, int FM, int FN, int BK, int NWM, int NWN, int DEPTH, int KMAP>
 static void igemm_go(const T* A, const T* Bt, const T* bias, T* out, const uint32_t* nmap, const int32_t* perm,
                      const uint32_t* smask, const T* zrow, int64_t n, int K, int N, int flip, float* partial,
-                     hipStream_t s) {
+                     hipStream_t s, const GemmPart& gp) {
   constexpr int BM = NWM * FM * 32, BN = NWN * FN * 32;
   const int ntiles = int((n + BM - 1) / BM);
   const int nblk = (N + BN - 1) / BN;
@@ -1189,7 +1239,7 @@ static void igemm_go(const T* A, const T* Bt, const T* bias, T* out, const uint3
   const int tgroup = nblk * nsplit == 1 ? kTileGroup : 1;
   const unsigned grid = xcd_group_grid((ntiles + tgroup - 1) / tgroup, tgroup * nblk * nsplit);
   igemm<T, FM, FN, BK, NWM, NWN, DEPTH, KMAP, MW><<<grid, 64 * NWM * NWN, 0, s>>>(
-      A, Bt, bias, out, nmap, perm, smask, zrow, n, K, N, flip, ntiles, nblk, nsplit, partial, tgroup);
+      A, Bt, bias, out, nmap, perm, smask, zrow, n, K, N, flip, ntiles, nblk, nsplit, partial, tgroup, gp);
   if (nsplit > 1)
     split_reduce<T><<<unsigned((n * N + 255) / 256), 256, 0, s>>>(partial, nsplit, n, N, bias, perm, out);
 }
@@ -1204,11 +1254,12 @@ static void igemm_go(const T* A, const T* Bt, const T* bias, T* out, const uint3
 template <typename T, int MW, int FN>
 static void igemm_pick_rows(const T* A, const T* Bt, const T* bias, T* out, const uint32_t* nmap,
                             const int32_t* perm, const uint32_t* smask, const T* zrow, int64_t n, int K, int N,
-                            int flip, float* partial, hipStream_t s) {
+                            int flip, float* partial, hipStream_t s, const GemmPart& gp) {
   const int64_t nblk = (N + FN * 32 - 1) / (FN * 32);
   const int64_t wg256 = (n + 255) / 256 * nblk, wg128 = (n + 127) / 128 * nblk;
 #define SSC_GO(NW, BK, DEPTH, KMAP) \
-  igemm_go<T, MW, 1, FN, BK, NW, 1, DEPTH, KMAP>(A, Bt, bias, out, nmap, perm, smask, zrow, n, K, N, flip, partial, s)
+  igemm_go<T, MW, 1, FN, BK, NW, 1, DEPTH, KMAP>(A, Bt, bias, out, nmap, perm, smask, zrow, n, K, N, flip, partial, s, \
+                                                 gp)
 #define SSC_BK(NW, DEPTH)                                                 \
   do {                                                                    \
     if constexpr (sizeof(T) == 4) {                                       \
@@ -1244,10 +1295,51 @@ template <typename T, int MW>
 static void launch_igemm(const T* A, const T* Bt, const T* bias, T* out, const uint32_t* nmap,
                          const int32_t* perm, const uint32_t* smask, const T* zrow, int64_t n, int K, int N,
                          int flip, float* partial, hipStream_t s) {
-  if (N > 128) igemm_pick_rows<T, MW, 8>(A, Bt, bias, out, nmap, perm, smask, zrow, n, K, N, flip, partial, s);
-  else if (N > 64) igemm_pick_rows<T, MW, 4>(A, Bt, bias, out, nmap, perm, smask, zrow, n, K, N, flip, partial, s);
-  else if (N > 32) igemm_pick_rows<T, MW, 2>(A, Bt, bias, out, nmap, perm, smask, zrow, n, K, N, flip, partial, s);
-  else igemm_pick_rows<T, MW, 1>(A, Bt, bias, out, nmap, perm, smask, zrow, n, K, N, flip, partial, s);
+  // every offset, one row order; with flip, column c meets W[MW - 1 - c]
+  const GemmPart gp{nullptr, 0, ~0u, MW - 1, 0, nullptr};
+  if (N > 128) igemm_pick_rows<T, MW, 8>(A, Bt, bias, out, nmap, perm, smask, zrow, n, K, N, flip, partial, s, gp);
+  else if (N > 64) igemm_pick_rows<T, MW, 4>(A, Bt, bias, out, nmap, perm, smask, zrow, n, K, N, flip, partial, s, gp);
+  else if (N > 32) igemm_pick_rows<T, MW, 2>(A, Bt, bias, out, nmap, perm, smask, zrow, n, K, N, flip, partial, s, gp);
+  else igemm_pick_rows<T, MW, 1>(A, Bt, bias, out, nmap, perm, smask, zrow, n, K, N, flip, partial, s, gp);
+}
+
+// One gated part of a possibly split GEMM: wide layers only (parts_possible),
+// so always 8 waves of 32 rows and 256 channels.
+template <typename T, int MW>
+static void igemm_part_go(const T* A, const T* Bt, const T* bias, T* out, const uint32_t* nmap, const int32_t* perm,
+                          const uint32_t* smask, const T* zrow, int64_t n, int K, int N, int flip, hipStream_t s,
+                          const GemmPart& gp) {
+  if constexpr (sizeof(T) == 2) {
+    if (K % 64 == 0) igemm_go<T, MW, 1, 8, 64, 8, 1, 2, 1>(A, Bt, bias, out, nmap, perm, smask, zrow, n, K, N, flip,
+                                                          nullptr, s, gp);
+    else if (K % 32 == 0) igemm_go<T, MW, 1, 8, 32, 8, 1, 2, 1>(A, Bt, bias, out, nmap, perm, smask, zrow, n, K, N,
+                                                               flip, nullptr, s, gp);
+    else igemm_go<T, MW, 1, 8, 16, 8, 1, 2, 1>(A, Bt, bias, out, nmap, perm, smask, zrow, n, K, N, flip, nullptr, s,
+                                               gp);
+  }
+}
+
+// The fwd (flip = 0) or input-gradient (flip = 1) GEMM of a submanifold plan
+// region whose build may have taken the two-part split: three gated launches,
+// of which either the first (single order, every offset) or the other two
+// (part 1 in the main order into pbuf, part 0 in its own order adding pbuf,
+// the bias and the rounding) do the work.
+template <typename T>
+static void launch_igemm_split(const T* A, const T* Bt, const T* bias, T* out, const char* region,
+                               const int32_t* perm, int64_t n, int K, int N, int flip, float* pbuf, hipStream_t s) {
+  const PlanLayout L = conv_layout(n);
+  const PlanHeader* h = reinterpret_cast<const PlanHeader*>(region + L.header);
+  const uint32_t* snmap = reinterpret_cast<const uint32_t*>(region + L.snmap);
+  const uint32_t* smask = reinterpret_cast<const uint32_t*>(region + L.smask);
+  const T* zrow = reinterpret_cast<const T*>(region + L.zrow);
+  igemm_part_go<T, kV>(A, Bt, bias, out, snmap, perm, smask, zrow, n, K, N, flip, s,
+                       GemmPart{h, 2, ~0u, kV - 1, 0, nullptr});
+  igemm_part_go<T, kV>(A, Bt, bias, out, snmap, perm, smask, zrow, n, K, N, flip, s,
+                       GemmPart{h, 1, kPart1Mask, kV - 1, 1, pbuf});
+  igemm_part_go<T, kPart0Cols>(A, Bt, bias, out, reinterpret_cast<const uint32_t*>(region + L.snmap0),
+                               reinterpret_cast<const int32_t*>(region + L.perm0),
+                               reinterpret_cast<const uint32_t*>(region + L.smask0), zrow, n, K, N, flip, s,
+                               GemmPart{h, 1, kPart0Mask, kV - 1, 2, pbuf});
 }
 
 template <typename T>
@@ -1346,10 +1438,11 @@ struct ConvView {
   const uint32_t* map_f = nullptr;
   const uint32_t* map_b = nullptr;
   int mw = kV;
+  bool parts = false;  // a submanifold plan: its build may have taken the two-part split
 };
 
 static size_t view_ws_bytes(const ConvView& v, int Ci, int Co, int esize) {
-  return ws_layout(v.n_f, v.n_b, Ci, Co, esize).total;
+  return ws_layout(v.n_f, v.n_b, Ci, Co, esize, v.parts).total;
 }
 
 template <typename T>
@@ -1365,10 +1458,15 @@ static int run_fwd(const ConvView& v, int Ci, int Co, const void* feats, const v
                    void* out, char* ws, hipStream_t s) {
   if (v.n_f == 0) return SSC_OK;
   const PlanLayout L = conv_layout(v.n_f);
-  const WsLayout W = ws_layout(v.n_f, v.n_b, Ci, Co, sizeof(T));
+  const WsLayout W = ws_layout(v.n_f, v.n_b, Ci, Co, sizeof(T), v.parts);
   T* wt = reinterpret_cast<T*>(ws + W.wt);
   dim3 tg(unsigned((Co + 31) / 32), unsigned((Ci + 31) / 32), unsigned(v.nk));
   transpose_w<T><<<tg, 256, 0, s>>>(static_cast<const T*>(weight), wt, Ci, Co);
+  if (v.parts && parts_possible(v.n_f, Ci, Co, sizeof(T))) {
+    launch_igemm_split<T>(static_cast<const T*>(feats), wt, static_cast<const T*>(bias), static_cast<T*>(out), v.fwd,
+                          v.perm_f, v.n_f, Ci, Co, 0, reinterpret_cast<float*>(ws + W.part), s);
+    return SSC_OK;
+  }
   launch_igemm_w<T>(v.mw, static_cast<const T*>(feats), wt, static_cast<const T*>(bias), static_cast<T*>(out),
                   v.map_f ? v.map_f : reinterpret_cast<const uint32_t*>(v.fwd + L.snmap), v.perm_f,
                   reinterpret_cast<const uint32_t*>(v.fwd + L.smask), reinterpret_cast<const T*>(v.fwd + L.zrow),
@@ -1384,9 +1482,12 @@ static int run_bwd(const ConvView& v, int Ci, int Co, const void* feats, const v
     // dX = masked implicit GEMM over the input rows of dY with B[k] = W[26-k]
     // read as [Ci][Co] (K = Co, N = Ci); the bwd map's column 26-k holds offset k
     const PlanLayout Lb = conv_layout(v.n_b);
-    const WsLayout Wb = ws_layout(v.n_f, v.n_b, Ci, Co, sizeof(T));
+    const WsLayout Wb = ws_layout(v.n_f, v.n_b, Ci, Co, sizeof(T), v.parts);
     if (v.n_f == 0) {
       zero_out<T>(static_cast<T*>(dfeats), v.n_b * Ci, s);  // no outputs: nothing reaches the inputs
+    } else if (v.parts && parts_possible(v.n_b, Ci, Co, sizeof(T))) {
+      launch_igemm_split<T>(dY, static_cast<const T*>(weight), nullptr, static_cast<T*>(dfeats), v.bwd, v.perm_b,
+                            v.n_b, Co, Ci, 1, reinterpret_cast<float*>(ws + Wb.part), s);
     } else {
       launch_igemm_w<T>(v.mw, dY, static_cast<const T*>(weight), nullptr, static_cast<T*>(dfeats),
                       v.map_b ? v.map_b : reinterpret_cast<const uint32_t*>(v.bwd + Lb.snmap), v.perm_b,
@@ -1403,7 +1504,7 @@ static int run_bwd(const ConvView& v, int Ci, int Co, const void* feats, const v
   }
   const int64_t n = v.n_f;
   const PlanLayout L = conv_layout(n);
-  const WsLayout W = ws_layout(n, v.n_b, Ci, Co, sizeof(T));
+  const WsLayout W = ws_layout(n, v.n_b, Ci, Co, sizeof(T), v.parts);
   const BwdShape b = bwd_shape(n, Ci, Co, int(sizeof(T)));
   const PlanHeader* h = reinterpret_cast<const PlanHeader*>(v.fwd + L.header);
   float* bpart = reinterpret_cast<float*>(ws + W.bias);
@@ -1452,7 +1553,7 @@ using namespace ssc;
 extern "C" size_t ssc_conv_workspace_bytes(int64_t n, int32_t Ci, int32_t Co, int32_t dtype) {
   if (dtype != SSC_F32 && dtype != SSC_F16 && dtype != SSC_BF16) return 0;
   if (n < 0 || n > SSC_MAX_VOXELS || !channels_ok(Ci, Co, dtype)) return 0;
-  return ws_layout(n, n, Ci, Co, esize_of(dtype)).total;
+  return ws_layout(n, n, Ci, Co, esize_of(dtype), true).total;
 }
 
 extern "C" int ssc_subm_conv3d_fwd(const void* plan, const uint32_t* nmap, const int32_t* perm, int64_t n,
@@ -1467,10 +1568,11 @@ extern "C" int ssc_subm_conv3d_fwd(const void* plan, const uint32_t* nmap, const
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return SSC_ERR_INVALID_ARG;
   if (n == 0) return SSC_OK;
-  if (workspace_bytes < ws_layout(n, n, Ci, Co, esize_of(dtype)).total) return SSC_ERR_WORKSPACE;
+  if (workspace_bytes < ws_layout(n, n, Ci, Co, esize_of(dtype), true).total) return SSC_ERR_WORKSPACE;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const char* pl = static_cast<const char*>(plan);
-  const ConvView v{pl, perm, n, pl, perm, n, kV};
+  ConvView v{pl, perm, n, pl, perm, n, kV};
+  v.parts = true;
   char* ws = static_cast<char*>(workspace);
   (void)hipGetLastError();
   by_dtype(dtype, [&](auto t) { run_fwd<decltype(t)>(v, Ci, Co, feats, weight, bias, out, ws, s); });
@@ -1491,10 +1593,12 @@ extern "C" int ssc_subm_conv3d_bwd(const void* plan, const uint32_t* nmap, const
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return SSC_ERR_INVALID_ARG;
   const int es = esize_of(dtype);
-  if ((dfeats || dweight || dbias) && workspace_bytes < ws_layout(n, n, Ci, Co, es).total) return SSC_ERR_WORKSPACE;
+  if ((dfeats || dweight || dbias) && workspace_bytes < ws_layout(n, n, Ci, Co, es, true).total)
+    return SSC_ERR_WORKSPACE;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const char* pl = static_cast<const char*>(plan);
-  const ConvView v{pl, perm, n, pl, perm, n, kV};
+  ConvView v{pl, perm, n, pl, perm, n, kV};
+  v.parts = true;
   char* ws = static_cast<char*>(workspace);
   (void)hipGetLastError();
   by_dtype(dtype, [&](auto t) {

@@ -74,8 +74,14 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* l
   return total;
 }
 
+// A non-null `gate` word that reads zero turns a launch into a no-op (steps of
+// the build that the device decides to skip).
+__device__ __forceinline__ bool gated_off(const uint32_t* gate) { return gate && *gate == 0u; }
+
 __global__ void __launch_bounds__(kScanThreads) scan_reduce(const uint32_t* __restrict__ data,
-                                                            int64_t len, uint32_t* __restrict__ tmp) {
+                                                            int64_t len, uint32_t* __restrict__ tmp,
+                                                            const uint32_t* __restrict__ gate) {
+  if (gated_off(gate)) return;
   __shared__ uint32_t waves[kScanThreads / 64];
   const int64_t base = int64_t(blockIdx.x) * kScanBlock;
   // all loads issued before the first use (clamped in range, masked after):
@@ -96,7 +102,9 @@ __global__ void __launch_bounds__(kScanThreads) scan_reduce(const uint32_t* __re
 }
 
 // one workgroup: exclusive scan of the block sums, in chunks with a carry
-__global__ void __launch_bounds__(kScanThreads) scan_top(uint32_t* __restrict__ tmp, int64_t nb) {
+__global__ void __launch_bounds__(kScanThreads) scan_top(uint32_t* __restrict__ tmp, int64_t nb,
+                                                         const uint32_t* __restrict__ gate) {
+  if (gated_off(gate)) return;
   __shared__ uint32_t waves[kScanThreads / 64];
   uint32_t carry = 0;
   for (int64_t c0 = 0; c0 < nb; c0 += kScanThreads) {
@@ -110,7 +118,9 @@ __global__ void __launch_bounds__(kScanThreads) scan_top(uint32_t* __restrict__ 
 }
 
 __global__ void __launch_bounds__(kScanThreads) scan_apply(uint32_t* __restrict__ data, int64_t len,
-                                                           const uint32_t* __restrict__ tmp) {
+                                                           const uint32_t* __restrict__ tmp,
+                                                           const uint32_t* __restrict__ gate) {
+  if (gated_off(gate)) return;
   __shared__ uint32_t waves[kScanThreads / 64];
   const int64_t base = int64_t(blockIdx.x) * kScanBlock + int64_t(threadIdx.x) * kScanItems;
   uint32_t v[kScanItems];
@@ -136,12 +146,12 @@ __global__ void __launch_bounds__(kScanThreads) scan_apply(uint32_t* __restrict_
   }
 }
 
-void launch_scan(uint32_t* data, int64_t len, uint32_t* tmp, hipStream_t s) {
+void launch_scan(uint32_t* data, int64_t len, uint32_t* tmp, hipStream_t s, const uint32_t* gate) {
   if (len <= 0) return;
   const int64_t nb = (len + kScanBlock - 1) / kScanBlock;
-  scan_reduce<<<dim3(unsigned(nb)), dim3(kScanThreads), 0, s>>>(data, len, tmp);
-  scan_top<<<dim3(1), dim3(kScanThreads), 0, s>>>(tmp, nb);
-  scan_apply<<<dim3(unsigned(nb)), dim3(kScanThreads), 0, s>>>(data, len, tmp);
+  scan_reduce<<<dim3(unsigned(nb)), dim3(kScanThreads), 0, s>>>(data, len, tmp, gate);
+  scan_top<<<dim3(1), dim3(kScanThreads), 0, s>>>(tmp, nb, gate);
+  scan_apply<<<dim3(unsigned(nb)), dim3(kScanThreads), 0, s>>>(data, len, tmp, gate);
 }
 
 // ---------------------------------------------------------------------------
@@ -168,6 +178,9 @@ __global__ void __launch_bounds__(256) plan_prepare(PlanHeader* h, int64_t n, in
       h->key_bits = key_bits;
       h->zbits = zbits;
       h->capacity = capacity;
+      h->part_split = 0;
+      h->union_rows = 0;
+      h->mask_bits = 0;
     }
     if (threadIdx.x < 32) {
       h->pair_count[threadIdx.x] = 0;
@@ -332,7 +345,8 @@ __global__ void __launch_bounds__(256) row_scan(const int4* __restrict__ coords,
 template <int ITEMS>
 __global__ void __launch_bounds__(kSortThreads) radix_hist(const uint64_t* __restrict__ keys, int64_t n,
                                                            int shift, uint32_t* __restrict__ hist,
-                                                           int64_t nblk) {
+                                                           int64_t nblk, const uint32_t* __restrict__ gate) {
+  if (gated_off(gate)) return;
   __shared__ uint32_t cnt[256];
   cnt[threadIdx.x] = 0;
   __syncthreads();
@@ -385,7 +399,9 @@ __global__ void __launch_bounds__(kSortThreads)
                   uint64_t* __restrict__ keys_out, uint32_t* __restrict__ vals_out, int64_t n, int shift,
                   const uint32_t* __restrict__ offsets, int64_t nblk, int first, int last,
                   int32_t* __restrict__ perm, uint32_t* __restrict__ smask, int zbits, int direct,
-                  uint32_t* __restrict__ hnext, uint32_t* __restrict__ hclear, PairJob pj) {
+                  uint32_t* __restrict__ hnext, uint32_t* __restrict__ hclear, PairJob pj,
+                  const uint32_t* __restrict__ gate) {
+  if (gated_off(gate)) return;
   if constexpr (FUSE) {
     if (int64_t(blockIdx.x) >= nblk) {
       pair_scatter_block(int64_t(blockIdx.x) - nblk, pj.nmap, n, pj.pcnt, pj.pblk, pj.pair_i, pj.pair_j, 1, pj.h,
@@ -626,12 +642,85 @@ __global__ void __launch_bounds__(256) pair_scatter(const uint32_t* __restrict__
 }
 
 // ---------------------------------------------------------------------------
+// the part-0 row order (see kPart0Mask)
+// ---------------------------------------------------------------------------
+
+// Sums over the main order: 32 * popcount(OR of each 32-row group's masks) and
+// the masks' popcounts; one atomic per wave into the header.
+__global__ void __launch_bounds__(256) union_stats(const uint32_t* __restrict__ smask, int64_t n,
+                                                   PlanHeader* __restrict__ h) {
+  const int64_t r = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  const uint32_t m = r < n ? smask[r] : 0u;
+  uint32_t u = m;
+  for (int d = 1; d < 32; d <<= 1) u |= __shfl_xor(u, d, 64);  // OR over each 32-lane half
+  uint32_t bits = __popc(m);
+  uint32_t rows = (__lane_id() & 31) == 0 ? 32u * __popc(u) : 0u;
+  for (int d = 32; d >= 1; d >>= 1) {
+    bits += __shfl_xor(bits, d, 64);
+    rows += __shfl_xor(rows, d, 64);
+  }
+  if (__lane_id() == 0) {
+    atomicAdd(&h->union_rows, (unsigned long long)rows);
+    atomicAdd(&h->mask_bits, (unsigned long long)bits);
+  }
+}
+
+// Takes the split when the main order's groups multiply enough zero rows, and
+// then writes the part-0 sort keys: (part-0 mask << zbits) | z-order code, with
+// the original row as payload, in main sorted order (the keys are unique, so
+// the input order cannot change the result).
+__global__ void __launch_bounds__(256) part_keys(const int4* __restrict__ coords, const int32_t* __restrict__ perm,
+                                                 const uint32_t* __restrict__ smask, int64_t n, int axis_bits,
+                                                 int zbits, PlanHeader* __restrict__ h,
+                                                 uint64_t* __restrict__ key, uint32_t* __restrict__ val) {
+  const unsigned long long rows = h->union_rows, bits = h->mask_bits;
+  if (rows * kPartWasteDen < bits * kPartWasteNum) return;
+  if (blockIdx.x == 0 && threadIdx.x == 0) h->part_split = 1u;
+  const int64_t r = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (r >= n) return;
+  const int32_t i = perm[r];
+  const int4 c = coords[i];
+  const uint64_t z = (uint64_t(uint32_t(c.x)) << (3 * axis_bits)) |
+                     zorder(uint32_t(c.y), uint32_t(c.z), uint32_t(c.w), axis_bits);
+  key[r] = (uint64_t(smask[r] & kPart0Mask) << zbits) | z;
+  val[r] = uint32_t(i);
+}
+
+// dst[r][c] = nmap[perm[r]][c] for the first `cols` columns
+__global__ void __launch_bounds__(256) permute_cols(const uint32_t* __restrict__ nmap, const int32_t* __restrict__ perm,
+                                                    int64_t n, int cols, uint32_t* __restrict__ dst,
+                                                    const uint32_t* __restrict__ gate) {
+  if (gated_off(gate)) return;
+  const int64_t e = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (e >= n * cols) return;
+  const int64_t r = e / cols;
+  const int c = int(e - r * cols);
+  dst[e] = nmap[int64_t(perm[r]) * kV + c];
+}
+
+// ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
 
 static inline unsigned grid1d(int64_t work, int threads) {
   int64_t b = (work + threads - 1) / threads;
   return unsigned(b < 1 ? 1 : b);
+}
+
+// One LSD pass of 8 bits at `shift` over keys of the multi-block path
+// (histogram, device-wide scan, stable scatter).  first: the payload is the
+// key's index; last: write perm and the sorted masks (key >> zbits) instead of
+// keys and payloads.
+static void sort_pass(const uint64_t* kin, const uint32_t* vin, uint64_t* kout, uint32_t* vout, int64_t n,
+                      int shift, bool first, bool last, int32_t* perm, uint32_t* smask, int zbits, uint32_t* hist,
+                      uint32_t* scan_tmp, const uint32_t* gate, hipStream_t s) {
+  const int64_t nblk = (n + kSortThreads * kSortItems - 1) / (kSortThreads * kSortItems);
+  const PairJob no_pairs{nullptr, nullptr, 0, nullptr, nullptr, nullptr, nullptr};
+  radix_hist<kSortItems><<<unsigned(nblk), kSortThreads, 0, s>>>(kin, n, shift, hist, nblk, gate);
+  launch_scan(hist, nblk * 256 + 1, scan_tmp, s, gate);
+  radix_scatter<false, kSortItems><<<unsigned(nblk), kSortThreads, 0, s>>>(
+      kin, vin, kout, vout, n, shift, hist, nblk, first ? 1 : 0, last ? 1 : 0, perm, smask, zbits, 0, nullptr,
+      nullptr, no_pairs, gate);
 }
 
 }  // namespace ssc
@@ -737,17 +826,13 @@ void order_rows(const int4* c4, const uint32_t* nmap, int64_t n, int B, int X, i
       if (L.sort_items == kSortItemsSmall)
         radix_scatter<true, kSortItemsSmall><<<grid, kSortThreads, 0, s>>>(
             kin, vin, kout, vout, n, shift, hcur, nblk, p == 0 ? 1 : 0, last, perm, smask, zbits, 1, hnext,
-            last ? nullptr : hclr, pj);
+            last ? nullptr : hclr, pj, nullptr);
       else
         radix_scatter<true, kSortItems><<<grid, kSortThreads, 0, s>>>(
             kin, vin, kout, vout, n, shift, hcur, nblk, p == 0 ? 1 : 0, last, perm, smask, zbits, 1, hnext,
-            last ? nullptr : hclr, pj);
+            last ? nullptr : hclr, pj, nullptr);
     } else {
-      radix_hist<kSortItems><<<unsigned(nblk), kSortThreads, 0, s>>>(kin, n, shift, hist, nblk);
-      launch_scan(hist, nblk * 256 + 1, scan_tmp, s);
-      radix_scatter<false, kSortItems><<<unsigned(nblk), kSortThreads, 0, s>>>(
-          kin, vin, kout, vout, n, shift, hist, nblk, p == 0 ? 1 : 0, last, perm, smask, zbits, 0, nullptr,
-          nullptr, no_pairs);
+      sort_pass(kin, vin, kout, vout, n, shift, p == 0, last, perm, smask, zbits, hist, scan_tmp, nullptr, s);
     }
     const uint64_t* tk = kout;
     const uint32_t* tv = vout;
@@ -768,6 +853,43 @@ void order_rows(const int4* c4, const uint32_t* nmap, int64_t n, int B, int X, i
   if (!pairs_ride)
     pair_scatter<<<unsigned(pblk), 256, 0, s>>>(nmap, n, pcnt, pblk, pair_i, pair_j, pdirect, h,
                                               reinterpret_cast<uint32_t*>(base + L.pseg));
+}
+
+void order_part0(const int4* c4, const uint32_t* nmap, const int32_t* perm, int64_t n, int B, int X, int Y, int Z,
+                 char* base, const PlanLayout& L, hipStream_t s) {
+  if (n == 0) return;
+  int axis_bits, zbits;
+  sort_key_bits(B, X, Y, Z, &axis_bits, &zbits);
+  PlanHeader* h = reinterpret_cast<PlanHeader*>(base + L.header);
+  const uint32_t* smask = reinterpret_cast<const uint32_t*>(base + L.smask);
+  uint64_t* key0 = reinterpret_cast<uint64_t*>(base + L.key0);
+  uint64_t* key1 = reinterpret_cast<uint64_t*>(base + L.key1);
+  uint32_t* val0 = reinterpret_cast<uint32_t*>(base + L.val0);
+  uint32_t* val1 = reinterpret_cast<uint32_t*>(base + L.val1);
+  uint32_t* hist = reinterpret_cast<uint32_t*>(base + L.hist);
+  uint32_t* scan_tmp = reinterpret_cast<uint32_t*>(base + L.scan_tmp);
+  const uint32_t* gate = &h->part_split;
+  union_stats<<<grid1d(n, 256), 256, 0, s>>>(smask, n, h);
+  part_keys<<<grid1d(n, 256), 256, 0, s>>>(c4, perm, smask, n, axis_bits, zbits, h, key0, val0);
+  // (part-0 mask, z-order) keys, the payload already the original row
+  const int passes = (kPart0Cols + zbits + 7) / 8;
+  const uint64_t* kin = key0;
+  const uint32_t* vin = val0;
+  uint64_t* kout = key1;
+  uint32_t* vout = val1;
+  for (int p = 0; p < passes; ++p) {
+    sort_pass(kin, vin, kout, vout, n, 8 * p, false, p == passes - 1, reinterpret_cast<int32_t*>(base + L.perm0),
+              reinterpret_cast<uint32_t*>(base + L.smask0), zbits, hist, scan_tmp, gate, s);
+    const uint64_t* tk = kout;
+    const uint32_t* tv = vout;
+    kout = const_cast<uint64_t*>(kin);
+    vout = const_cast<uint32_t*>(vin);
+    kin = tk;
+    vin = tv;
+  }
+  permute_cols<<<grid1d(n * kPart0Cols, 256), 256, 0, s>>>(nmap, reinterpret_cast<const int32_t*>(base + L.perm0), n,
+                                                          kPart0Cols, reinterpret_cast<uint32_t*>(base + L.snmap0),
+                                                          gate);
 }
 
 }  // namespace ssc
@@ -805,6 +927,7 @@ extern "C" int ssc_build_neighbor_map(const int32_t* coords, int64_t n, int32_t 
     probe_half<uint32_t><<<grid1d(n * kCentre, 256), 256, 0, s>>>(
         c4, n, B, X, Y, Z, reinterpret_cast<const Slot<uint32_t>*>(base + L.table), L.capacity, nmap);
   order_rows(c4, nmap, n, B, X, Y, Z, perm, base, L, true, s);
+  if (part_build_wanted(n, B, X, Y, Z)) order_part0(c4, nmap, perm, n, B, X, Y, Z, base, L, s);
   return hipGetLastError() == hipSuccess ? SSC_OK : SSC_ERR_HIP;
 }
 
@@ -834,6 +957,19 @@ extern "C" int ssc_plan_pair_counts(const void* plan, void* stream, int64_t* cou
   if (hipMemcpy(&h, plan, sizeof(h), hipMemcpyDeviceToHost) != hipSuccess) return SSC_ERR_HIP;
   if (h.magic != kPlanMagic) return SSC_ERR_INVALID_ARG;
   for (int k = 0; k < kV; ++k) counts_host[k] = h.pair_count[k];
+  return SSC_OK;
+}
+
+extern "C" int ssc_plan_row_orders(const void* plan, void* stream, int64_t* orders_host) {
+  if (!plan || !orders_host) return SSC_ERR_INVALID_ARG;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  PlanHeader h;
+  if (hipStreamSynchronize(s) != hipSuccess) return SSC_ERR_HIP;
+  if (hipMemcpy(&h, plan, sizeof(h), hipMemcpyDeviceToHost) != hipSuccess) return SSC_ERR_HIP;
+  if (h.magic != kPlanMagic) return SSC_ERR_INVALID_ARG;
+  orders_host[0] = h.part_split ? 2 : 1;
+  orders_host[1] = int64_t(h.union_rows);
+  orders_host[2] = int64_t(h.mask_bits);
   return SSC_OK;
 }
 

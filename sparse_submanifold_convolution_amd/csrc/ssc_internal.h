@@ -44,7 +44,8 @@ constexpr int kScanBlock = kScanThreads * kScanItems;
 
 // In-place exclusive scan of len uint32 on stream s (three launches); tmp
 // holds ceil(len / kScanBlock) + 1 words.  Defined with the plan builder.
-void launch_scan(uint32_t* data, int64_t len, uint32_t* tmp, hipStream_t s);
+// A non-null gate word that reads zero on the device makes the launches no-ops.
+void launch_scan(uint32_t* data, int64_t len, uint32_t* tmp, hipStream_t s, const uint32_t* gate = nullptr);
 inline int64_t scan_tmp_words(int64_t len) { return (len + kScanBlock - 1) / kScanBlock + 1; }
 
 struct PlanHeader {
@@ -57,10 +58,45 @@ struct PlanHeader {
   uint64_t capacity;
   uint32_t pair_count[32];  // [27] used: valid pairs per offset
   uint32_t pair_off[32];    // [28] used: start of each offset's pair list
+  // Two-part offset split (see kPart0Mask): non-zero when the build sorted the
+  // rows a second time by their part-0 masks, so the GEMMs run each part in its
+  // own row order.  Decided on the device from the two sums below.
+  uint32_t part_split;
+  uint32_t reserved;
+  unsigned long long union_rows;  // sum over 32-row groups of the main order: 32 * |OR of their masks|
+  unsigned long long mask_bits;   // sum over rows of popcount(mask): the valid pairs
 };
 static_assert(sizeof(PlanHeader) <= 4096, "plan header too large");
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Two-part offset split of the fwd / input-gradient GEMMs.  Part 1 holds the
+// offsets 13..26, the high bits of the 27-bit mask, so the main (mask, z-order)
+// row order already groups rows by their part-1 masks; part 0 holds the
+// offsets 0..12, and a second sort by (part-0 mask, z-order) groups rows by
+// those.  Each part then runs the masked GEMM in its own order, over only its
+// offsets: part 1 into fp32 partial sums, part 0 adding them, the bias and the
+// one rounding.  Random (volumetric) occupancy makes 32-row groups of the main
+// order share few of their low mask bits, so the split removes most of the
+// zero rows a single order multiplies; shells and solids share them already
+// and keep the single order.
+constexpr uint32_t kPart0Mask = 0x1FFFu;     // offsets 0..12
+constexpr uint32_t kPart1Mask = 0x7FFE000u;  // offsets 13..26
+constexpr int kPart0Cols = 13;
+// the build considers the split from this many rows, with the voxels filling at
+// least 1/kPartMaxSparsity of the grid's cells
+constexpr int64_t kPartMinRows = 131072;
+constexpr int64_t kPartMaxSparsity = 32;
+// the split is taken when the main order's 32-row groups multiply at least
+// kPartWasteNum / kPartWasteDen times the valid pairs
+constexpr unsigned long long kPartWasteNum = 5, kPartWasteDen = 4;
+// the GEMMs use it from this many channels on both sides (the MFMA-bound regime)
+constexpr int kPartMinChannels = 256;
+
+inline bool part_build_wanted(int64_t n, int32_t B, int32_t X, int32_t Y, int32_t Z) {
+  const double cells = double(B) * double(X) * double(Y) * double(Z);
+  return n >= kPartMinRows && double(n) * double(kPartMaxSparsity) >= cells;
+}
 
 inline int ceil_log2_u64(uint64_t v) {
   int e = 0;
@@ -78,6 +114,10 @@ struct PlanLayout {
   size_t pair_i = 0;  // [27n] u32: pair lists, output row i
   size_t pair_j = 0;  // [27n] u32: pair lists, input row j = nmap[i][k]
   size_t pseg = 0;    // [27][pblk + 1] u32: where each kPairRows block of rows starts in each list
+  // part-0 row order (valid while the header's part_split is set)
+  size_t perm0 = 0;   // [n] i32: original row at each part-0 sorted position
+  size_t smask0 = 0;  // [n] u32: part-0 mask (offsets 0..12) at each part-0 sorted position
+  size_t snmap0 = 0;  // [n][13] u32: nmap columns 0..12 in part-0 order
   // build-only scratch
   size_t table = 0;  // hash slots: {key, row} pairs, 8 bytes (32-bit keys) or 16 (64-bit)
   size_t key0 = 0, key1 = 0, val0 = 0, val1 = 0, hist = 0, pcnt = 0, scan_tmp = 0;
@@ -104,6 +144,9 @@ inline PlanLayout conv_layout(int64_t n) {
   L.pair_i = take(size_t(n) * kV * 4);
   L.pair_j = take(size_t(n) * kV * 4);
   L.pseg = take(size_t(kV) * size_t((n + kPairRows - 1) / kPairRows + 1) * 4);
+  L.perm0 = take(size_t(n) * 4);
+  L.smask0 = take(size_t(n) * 4);
+  L.snmap0 = take(size_t(n) * kPart0Cols * 4);
   L.total = off;
   return L;
 }

@@ -208,6 +208,32 @@ def test_mid_parity(ssc, case):
     _full_parity(ssc, w)
 
 
+# Random occupancy with many rows and wide channels: the build sorts the rows a
+# second time by the mask of offsets 0..12 and the GEMMs run in two parts (the
+# first into fp32 sums, the second adding them).  A fully active block has
+# near-identical masks and keeps one order; the same layer in fp32 or with
+# narrow channels runs the single-order GEMM on the split plan.
+SPLIT = [
+    # seed, B, dims, p, ci, co, dtype, shuffle, expected row orders
+    (61, 1, (80, 80, 80), 0.3, 256, 256, "bf16", True, 2),
+    (62, 2, (64, 60, 64), 0.35, 256, 320, "f16", False, 2),
+    (63, 1, (52, 52, 52), 1.0, 256, 256, "bf16", False, 1),
+    (64, 1, (80, 80, 80), 0.3, 64, 264, "f16", False, 2),
+]
+
+
+@pytest.mark.parametrize("case", SPLIT, ids=[f"p{c[0]}" for c in SPLIT])
+def test_split_order_parity(ssc, case):
+    seed, B, dims, p, ci, co, dt, shuffle, orders = case
+    w = WL.random_workload(seed, B, dims, p, ci, co, dt, random_bias=True, shuffle=shuffle)
+    assert w.n >= 131072
+    plan, _ = _full_parity(ssc, w)
+    got, union_rows, pairs = ssc.plan_row_orders(plan)
+    print(f"[orders] {got} union_rows={union_rows} pairs={pairs}", flush=True)
+    assert got == orders
+    assert pairs == sum(ssc.plan_pair_counts(plan))
+
+
 def test_single_voxel(ssc):
     w = WL.values_for(np.array([[0, 3, 4, 5]], np.int32), (1, 8, 8, 8), 4, 32, 32, "f32")
     _full_parity(ssc, w)
@@ -277,6 +303,7 @@ def _sampled_parity(ssc, cfg, n_rows=2048, n_entries=96):
     e_db = _rel(db.double().cpu(), O.dbias(w.dout))
     print(f"[errs] out={e_out:.2e} dX={e_dx:.2e} dW={e_dw:.2e} db={e_db:.2e}", flush=True)
     assert e_out <= tol and e_dx <= tol and e_dw <= tol and e_db <= tol
+    return plan
 
 
 def test_config3_sampled(ssc):
@@ -284,11 +311,15 @@ def test_config3_sampled(ssc):
 
 
 def test_config4_sampled(ssc):
-    _sampled_parity(ssc, 4)
+    plan = _sampled_parity(ssc, 4)
+    # shells: one row order
+    assert ssc.plan_row_orders(plan)[0] == 1
 
 
 def test_config5_sampled(ssc):
-    _sampled_parity(ssc, 5)
+    plan = _sampled_parity(ssc, 5)
+    # random occupancy: the GEMMs run in two row orders
+    assert ssc.plan_row_orders(plan)[0] == 2
 
 
 @pytest.mark.parametrize("two_streams", [False, True], ids=["one_stream", "two_streams"])
