@@ -48,6 +48,8 @@ def parse():
     p.add_argument("--no-graph", action="store_true",
                    help="time eagerly launched steps instead of replaying one captured HIP graph per step")
     p.add_argument("--cpu-budget-s", type=float, default=20.0)
+    p.add_argument("--phase-reps", type=int, default=20,
+                   help="event-timed repetitions of each call (median and min); profiling runs cut this down")
     p.add_argument("--copy-calib", type=int, default=0,
                    help="only run a device copy of this many MiB (HBM counter calibration)")
     p.add_argument("--serialize", action="store_true",
@@ -604,7 +606,7 @@ def main():
 
     # per-call times of eagerly launched steps: HIP events on the stream the kernels run on
     # (torch's current stream, which the binding hands to every call), at least 20 repetitions
-    reps = max(20, args.steps)
+    reps = max(1, args.phase_reps)
     ev = {k: [] for k, _ in parts}
     for _ in range(reps):
         for name, f in parts:

@@ -127,13 +127,13 @@ int ssc_plan_pair_counts(const void* plan, void* stream, int64_t* counts_host);
  * masked GEMMs (the pages' sorted_idx and per-block valid offsets: the Triton
  * compile-cache post, section six, kernel signature).  orders_host[0] (host)
  * receives 1 when every offset runs in the one (mask, z-order) row order, or
- * 2 when the build also sorted the rows by the mask of the offsets 0..12 alone
- * and the wide-channel fwd / input-gradient GEMMs run those offsets in that
- * second order (and the offsets 13..26 in the first).  orders_host[1] and
- * orders_host[2] receive the two sums the build decided it from: 32 times the
- * offsets present in each 32-row group of the first order, summed over the
- * groups, and the valid pairs P (both 0 when the build did not consider it).
- * The results never depend on it.
+ * 3 when the build also sorted the rows by the masks of the offsets 0..8 and
+ * of 9..17 alone, and the wide-channel fwd / input-gradient GEMMs run those
+ * offsets in those orders (and the offsets 18..26 in the first).
+ * orders_host[1] and orders_host[2] receive the two sums the build decided it
+ * from: 32 times the offsets present in each 32-row group of the first order,
+ * summed over the groups, and the valid pairs P (both 0 when the build did not
+ * consider it).  The results never depend on it.
  */
 int ssc_plan_row_orders(const void* plan, void* stream, int64_t* orders_host);
 

@@ -168,7 +168,7 @@ def plan_pair_counts(plan: Plan) -> list[int]:
 
 
 def plan_row_orders(plan: Plan) -> tuple[int, int, int]:
-    """(row orders the GEMMs use: 1 or 2, the first order's 32-row group sum, the valid pairs)."""
+    """(row orders the GEMMs use: 1 or 3, the first order's 32-row group sum, the valid pairs)."""
     arr = (ctypes.c_int64 * 3)()
     _check("ssc_plan_row_orders", lib().ssc_plan_row_orders(_ptr(plan.buf), _stream(plan.device), arr))
     return int(arr[0]), int(arr[1]), int(arr[2])

@@ -642,33 +642,46 @@ __global__ void __launch_bounds__(256) pair_scatter(const uint32_t* __restrict__
 }
 
 // ---------------------------------------------------------------------------
-// the part-0 row order (see kPart0Mask)
+// the row orders of offset parts 0 and 1 (see kParts)
 // ---------------------------------------------------------------------------
 
 // Sums over the main order: 32 * popcount(OR of each 32-row group's masks) and
-// the masks' popcounts; one atomic per wave into the header.
+// the masks' popcounts.  Grid-stride over the rows, a workgroup reduction, one
+// pair of atomics per workgroup into the header.
 __global__ void __launch_bounds__(256) union_stats(const uint32_t* __restrict__ smask, int64_t n,
                                                    PlanHeader* __restrict__ h) {
-  const int64_t r = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  const uint32_t m = r < n ? smask[r] : 0u;
-  uint32_t u = m;
-  for (int d = 1; d < 32; d <<= 1) u |= __shfl_xor(u, d, 64);  // OR over each 32-lane half
-  uint32_t bits = __popc(m);
-  uint32_t rows = (__lane_id() & 31) == 0 ? 32u * __popc(u) : 0u;
+  __shared__ unsigned long long red[2][4];
+  unsigned long long rows = 0, bits = 0;
+  for (int64_t r0 = int64_t(blockIdx.x) * 256; r0 < n; r0 += int64_t(gridDim.x) * 256) {
+    const int64_t r = r0 + threadIdx.x;
+    const uint32_t m = r < n ? smask[r] : 0u;
+    uint32_t u = m;
+    for (int d = 1; d < 32; d <<= 1) u |= __shfl_xor(u, d, 64);  // OR over each 32-lane half
+    bits += __popc(m);
+    if ((__lane_id() & 31) == 0) rows += 32u * __popc(u);
+  }
   for (int d = 32; d >= 1; d >>= 1) {
     bits += __shfl_xor(bits, d, 64);
     rows += __shfl_xor(rows, d, 64);
   }
+  const int wave = threadIdx.x / 64;
   if (__lane_id() == 0) {
-    atomicAdd(&h->union_rows, (unsigned long long)rows);
-    atomicAdd(&h->mask_bits, (unsigned long long)bits);
+    red[0][wave] = rows;
+    red[1][wave] = bits;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    atomicAdd(&h->union_rows, red[0][0] + red[0][1] + red[0][2] + red[0][3]);
+    atomicAdd(&h->mask_bits, red[1][0] + red[1][1] + red[1][2] + red[1][3]);
   }
 }
 
 // Takes the split when the main order's groups multiply enough zero rows, and
-// then writes the part-0 sort keys: (part-0 mask << zbits) | z-order code, with
-// the original row as payload, in main sorted order (the keys are unique, so
-// the input order cannot change the result).
+// then writes the sort keys of parts 0 and 1: for part q,
+// (q << (9 + zbits)) | (the part's 9-bit mask << zbits) | z-order code, with
+// the original row as payload, at position q * n + r for main sorted position
+// r.  Keys are unique, so the input order cannot change the result, and one
+// sort of the 2n keys orders both parts, part 0 first.
 __global__ void __launch_bounds__(256) part_keys(const int4* __restrict__ coords, const int32_t* __restrict__ perm,
                                                  const uint32_t* __restrict__ smask, int64_t n, int axis_bits,
                                                  int zbits, PlanHeader* __restrict__ h,
@@ -682,20 +695,26 @@ __global__ void __launch_bounds__(256) part_keys(const int4* __restrict__ coords
   const int4 c = coords[i];
   const uint64_t z = (uint64_t(uint32_t(c.x)) << (3 * axis_bits)) |
                      zorder(uint32_t(c.y), uint32_t(c.z), uint32_t(c.w), axis_bits);
-  key[r] = (uint64_t(smask[r] & kPart0Mask) << zbits) | z;
-  val[r] = uint32_t(i);
+  const uint32_t m = smask[r];
+#pragma unroll
+  for (int q = 0; q < kOwnOrderParts; ++q) {
+    key[q * n + r] = (uint64_t(q) << (kPartCols + zbits)) |
+                     (uint64_t((m >> (q * kPartCols)) & kPartColMask) << zbits) | z;
+    val[q * n + r] = uint32_t(i);
+  }
 }
 
-// dst[r][c] = nmap[perm[r]][c] for the first `cols` columns
-__global__ void __launch_bounds__(256) permute_cols(const uint32_t* __restrict__ nmap, const int32_t* __restrict__ perm,
-                                                    int64_t n, int cols, uint32_t* __restrict__ dst,
-                                                    const uint32_t* __restrict__ gate) {
+// Part q's map rows in its own order: dst[q][r][c] = nmap[pperm[q][r]][9q + c].
+__global__ void __launch_bounds__(256) permute_parts(const uint32_t* __restrict__ nmap,
+                                                     const int32_t* __restrict__ pperm, int64_t n,
+                                                     uint32_t* __restrict__ dst, const uint32_t* __restrict__ gate) {
   if (gated_off(gate)) return;
   const int64_t e = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  if (e >= n * cols) return;
-  const int64_t r = e / cols;
-  const int c = int(e - r * cols);
-  dst[e] = nmap[int64_t(perm[r]) * kV + c];
+  if (e >= kOwnOrderParts * n * kPartCols) return;
+  const int64_t R = e / kPartCols;  // row of the 2n part rows
+  const int c = int(e - R * kPartCols);
+  const int q = int(R / n);
+  dst[e] = nmap[int64_t(pperm[R]) * kV + q * kPartCols + c];
 }
 
 // ---------------------------------------------------------------------------
@@ -735,7 +754,7 @@ extern "C" size_t ssc_plan_bytes(int64_t n, int32_t B, int32_t X, int32_t Y, int
   int axis_bits, zbits;
   sort_key_bits(B, X, Y, Z, &axis_bits, &zbits);
   if (kV + zbits > 64) return 0;
-  return plan_layout(n, kb).total;
+  return plan_layout(n, kb, part_build_wanted(n, B, X, Y, Z)).total;
 }
 
 namespace ssc {
@@ -855,7 +874,7 @@ void order_rows(const int4* c4, const uint32_t* nmap, int64_t n, int B, int X, i
                                               reinterpret_cast<uint32_t*>(base + L.pseg));
 }
 
-void order_part0(const int4* c4, const uint32_t* nmap, const int32_t* perm, int64_t n, int B, int X, int Y, int Z,
+void order_parts(const int4* c4, const uint32_t* nmap, const int32_t* perm, int64_t n, int B, int X, int Y, int Z,
                  char* base, const PlanLayout& L, hipStream_t s) {
   if (n == 0) return;
   int axis_bits, zbits;
@@ -869,17 +888,20 @@ void order_part0(const int4* c4, const uint32_t* nmap, const int32_t* perm, int6
   uint32_t* hist = reinterpret_cast<uint32_t*>(base + L.hist);
   uint32_t* scan_tmp = reinterpret_cast<uint32_t*>(base + L.scan_tmp);
   const uint32_t* gate = &h->part_split;
-  union_stats<<<grid1d(n, 256), 256, 0, s>>>(smask, n, h);
+  const int64_t nblk_stats = (n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024;
+  union_stats<<<unsigned(nblk_stats), 256, 0, s>>>(smask, n, h);
   part_keys<<<grid1d(n, 256), 256, 0, s>>>(c4, perm, smask, n, axis_bits, zbits, h, key0, val0);
-  // (part-0 mask, z-order) keys, the payload already the original row
-  const int passes = (kPart0Cols + zbits + 7) / 8;
+  // (part, part mask, z-order) keys over both parts, the payload already the original row
+  const int64_t nk = kOwnOrderParts * n;
+  const int bits = 1 + kPartCols + zbits;
+  const int passes = (bits + 7) / 8;
   const uint64_t* kin = key0;
   const uint32_t* vin = val0;
   uint64_t* kout = key1;
   uint32_t* vout = val1;
   for (int p = 0; p < passes; ++p) {
-    sort_pass(kin, vin, kout, vout, n, 8 * p, false, p == passes - 1, reinterpret_cast<int32_t*>(base + L.perm0),
-              reinterpret_cast<uint32_t*>(base + L.smask0), zbits, hist, scan_tmp, gate, s);
+    sort_pass(kin, vin, kout, vout, nk, 8 * p, false, p == passes - 1, reinterpret_cast<int32_t*>(base + L.pperm),
+              reinterpret_cast<uint32_t*>(base + L.psmask), zbits, hist, scan_tmp, gate, s);
     const uint64_t* tk = kout;
     const uint32_t* tv = vout;
     kout = const_cast<uint64_t*>(kin);
@@ -887,9 +909,8 @@ void order_part0(const int4* c4, const uint32_t* nmap, const int32_t* perm, int6
     kin = tk;
     vin = tv;
   }
-  permute_cols<<<grid1d(n * kPart0Cols, 256), 256, 0, s>>>(nmap, reinterpret_cast<const int32_t*>(base + L.perm0), n,
-                                                          kPart0Cols, reinterpret_cast<uint32_t*>(base + L.snmap0),
-                                                          gate);
+  permute_parts<<<grid1d(nk * kPartCols, 256), 256, 0, s>>>(nmap, reinterpret_cast<const int32_t*>(base + L.pperm),
+                                                           n, reinterpret_cast<uint32_t*>(base + L.psnmap), gate);
 }
 
 }  // namespace ssc
@@ -908,7 +929,8 @@ extern "C" int ssc_build_neighbor_map(const int32_t* coords, int64_t n, int32_t 
   int axis_bits, zbits;
   sort_key_bits(B, X, Y, Z, &axis_bits, &zbits);
   if (kV + zbits > 64) return SSC_ERR_UNSUPPORTED;
-  const PlanLayout L = plan_layout(n, kb);
+  const bool parts = part_build_wanted(n, B, X, Y, Z);
+  const PlanLayout L = plan_layout(n, kb, parts);
   if (plan_bytes < L.total) return SSC_ERR_WORKSPACE;
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -927,7 +949,7 @@ extern "C" int ssc_build_neighbor_map(const int32_t* coords, int64_t n, int32_t 
     probe_half<uint32_t><<<grid1d(n * kCentre, 256), 256, 0, s>>>(
         c4, n, B, X, Y, Z, reinterpret_cast<const Slot<uint32_t>*>(base + L.table), L.capacity, nmap);
   order_rows(c4, nmap, n, B, X, Y, Z, perm, base, L, true, s);
-  if (part_build_wanted(n, B, X, Y, Z)) order_part0(c4, nmap, perm, n, B, X, Y, Z, base, L, s);
+  if (parts) order_parts(c4, nmap, perm, n, B, X, Y, Z, base, L, s);
   return hipGetLastError() == hipSuccess ? SSC_OK : SSC_ERR_HIP;
 }
 
@@ -967,7 +989,7 @@ extern "C" int ssc_plan_row_orders(const void* plan, void* stream, int64_t* orde
   if (hipStreamSynchronize(s) != hipSuccess) return SSC_ERR_HIP;
   if (hipMemcpy(&h, plan, sizeof(h), hipMemcpyDeviceToHost) != hipSuccess) return SSC_ERR_HIP;
   if (h.magic != kPlanMagic) return SSC_ERR_INVALID_ARG;
-  orders_host[0] = h.part_split ? 2 : 1;
+  orders_host[0] = h.part_split ? 1 + kOwnOrderParts : 1;
   orders_host[1] = int64_t(h.union_rows);
   orders_host[2] = int64_t(h.mask_bits);
   return SSC_OK;

@@ -58,8 +58,8 @@ struct PlanHeader {
   uint64_t capacity;
   uint32_t pair_count[32];  // [27] used: valid pairs per offset
   uint32_t pair_off[32];    // [28] used: start of each offset's pair list
-  // Two-part offset split (see kPart0Mask): non-zero when the build sorted the
-  // rows a second time by their part-0 masks, so the GEMMs run each part in its
+  // Three-part offset split (see kParts): non-zero when the build sorted the
+  // rows again by the masks of parts 0 and 1, so the GEMMs run each part in its
   // own row order.  Decided on the device from the two sums below.
   uint32_t part_split;
   uint32_t reserved;
@@ -70,19 +70,22 @@ static_assert(sizeof(PlanHeader) <= 4096, "plan header too large");
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-// Two-part offset split of the fwd / input-gradient GEMMs.  Part 1 holds the
-// offsets 13..26, the high bits of the 27-bit mask, so the main (mask, z-order)
-// row order already groups rows by their part-1 masks; part 0 holds the
-// offsets 0..12, and a second sort by (part-0 mask, z-order) groups rows by
-// those.  Each part then runs the masked GEMM in its own order, over only its
-// offsets: part 1 into fp32 partial sums, part 0 adding them, the bias and the
-// one rounding.  Random (volumetric) occupancy makes 32-row groups of the main
-// order share few of their low mask bits, so the split removes most of the
-// zero rows a single order multiplies; shells and solids share them already
-// and keep the single order.
-constexpr uint32_t kPart0Mask = 0x1FFFu;     // offsets 0..12
-constexpr uint32_t kPart1Mask = 0x7FFE000u;  // offsets 13..26
-constexpr int kPart0Cols = 13;
+// Three-part offset split of the fwd / input-gradient GEMMs.  The 27 offsets
+// fall into three runs of nine, part q holding offsets 9q..9q+8.  Part 2 (the
+// offsets 18..26) is the top of the 27-bit mask, so the main (mask, z-order)
+// row order already groups the rows by their part-2 masks; parts 0 and 1 get
+// orders of their own, sorted by (that part's 9-bit mask, z-order).  Each part
+// runs the masked GEMM in its order over its offsets only: part 2 into fp32
+// sums, part 1 adding to them, part 0 adding them, the bias and the one
+// rounding.  With random (volumetric) occupancy the rows of a 256-row tile of
+// the main order share few of their low mask bits, and the tile multiplies
+// about twice the valid pairs; inside a part a tile spans one or two 9-bit
+// masks.  Shells and solids share their masks already and keep one order.
+constexpr int kParts = 3;
+constexpr int kPartCols = 9;                  // offsets (map columns) per part
+constexpr int kOwnOrderParts = kParts - 1;    // parts 0 and 1 have their own row orders
+constexpr uint32_t kPartColMask = 0x1FFu;     // a part's mask in its own column space
+constexpr uint32_t kTopPartMask = 0x7FC0000u; // part 2 in the main order's 27-bit mask
 // the build considers the split from this many rows, with the voxels filling at
 // least 1/kPartMaxSparsity of the grid's cells
 constexpr int64_t kPartMinRows = 131072;
@@ -114,10 +117,11 @@ struct PlanLayout {
   size_t pair_i = 0;  // [27n] u32: pair lists, output row i
   size_t pair_j = 0;  // [27n] u32: pair lists, input row j = nmap[i][k]
   size_t pseg = 0;    // [27][pblk + 1] u32: where each kPairRows block of rows starts in each list
-  // part-0 row order (valid while the header's part_split is set)
-  size_t perm0 = 0;   // [n] i32: original row at each part-0 sorted position
-  size_t smask0 = 0;  // [n] u32: part-0 mask (offsets 0..12) at each part-0 sorted position
-  size_t snmap0 = 0;  // [n][13] u32: nmap columns 0..12 in part-0 order
+  // row orders of parts 0 and 1 (valid while the header's part_split is set),
+  // part q at row offset q * n of each region
+  size_t pperm = 0;   // [2][n] i32: original row at each sorted position of the part
+  size_t psmask = 0;  // [2][n] u32: the part's 9-bit mask there (bit 9 holds q)
+  size_t psnmap = 0;  // [2][n][9] u32: nmap columns 9q..9q+8 in the part's order
   // build-only scratch
   size_t table = 0;  // hash slots: {key, row} pairs, 8 bytes (32-bit keys) or 16 (64-bit)
   size_t key0 = 0, key1 = 0, val0 = 0, val1 = 0, hist = 0, pcnt = 0, scan_tmp = 0;
@@ -144,14 +148,15 @@ inline PlanLayout conv_layout(int64_t n) {
   L.pair_i = take(size_t(n) * kV * 4);
   L.pair_j = take(size_t(n) * kV * 4);
   L.pseg = take(size_t(kV) * size_t((n + kPairRows - 1) / kPairRows + 1) * 4);
-  L.perm0 = take(size_t(n) * 4);
-  L.smask0 = take(size_t(n) * 4);
-  L.snmap0 = take(size_t(n) * kPart0Cols * 4);
+  L.pperm = take(size_t(kOwnOrderParts) * size_t(n) * 4);
+  L.psmask = take(size_t(kOwnOrderParts) * size_t(n) * 4);
+  L.psnmap = take(size_t(kOwnOrderParts) * size_t(n) * kPartCols * 4);
   L.total = off;
   return L;
 }
 
-inline PlanLayout plan_layout(int64_t n, int key_bits) {
+// parts: the build also sorts the rows of parts 0 and 1 (2n keys at once)
+inline PlanLayout plan_layout(int64_t n, int key_bits, bool parts = false) {
   PlanLayout L = conv_layout(n);
   size_t off = L.total;
   auto take = [&](size_t bytes) {
@@ -169,19 +174,31 @@ inline PlanLayout plan_layout(int64_t n, int key_bits) {
   L.sort_blocks = (n + kSortThreads * L.sort_items - 1) / (kSortThreads * L.sort_items);
   L.pair_blocks = (n + kPairRows - 1) / kPairRows;
   L.table = take(L.capacity * (L.key_bytes == 8 ? 16 : 8));
-  L.key0 = take(size_t(n) * 8);
-  L.key1 = take(size_t(n) * 8);
-  L.val0 = take(size_t(n) * 4);
-  L.val1 = take(size_t(n) * 4);
+  const size_t nkeys = size_t(n) * (parts ? kOwnOrderParts : 1);
+  L.key0 = take(nkeys * 8);
+  L.key1 = take(nkeys * 8);
+  L.val0 = take(nkeys * 4);
+  L.val1 = take(nkeys * 4);
   {
     // multi-block sort: one [256][blocks] histogram (+1 for the scan total);
     // direct sort (few blocks): three rotating ones, see the plan builder
     const size_t one = size_t(L.sort_blocks) * 256;
-    const size_t need = L.sort_blocks <= kSortDirectBlocks ? 3 * one : one + 1;
-    L.hist = take((need > one + 1 ? need : one + 1) * 4);
+    size_t need = L.sort_blocks <= kSortDirectBlocks ? 3 * one : one + 1;
+    if (need < one + 1) need = one + 1;
+    if (parts) {
+      // the part sort: multi-block over 2n keys
+      const size_t pb = (nkeys + kSortThreads * kSortItems - 1) / (kSortThreads * kSortItems);
+      if (need < pb * 256 + 1) need = pb * 256 + 1;
+    }
+    L.hist = take(need * 4);
   }
   L.pcnt = take((size_t(L.pair_blocks) * kV + 1) * 4);
   size_t scan_len = size_t(L.sort_blocks) * 256 + 1;
+  if (parts) {
+    // the part sort's histogram: one [256][blocks] table over 2n keys
+    const size_t pb = (nkeys + kSortThreads * kSortItems - 1) / (kSortThreads * kSortItems);
+    if (pb * 256 + 1 > scan_len) scan_len = pb * 256 + 1;
+  }
   if (size_t(L.pair_blocks) * kV + 1 > scan_len) scan_len = size_t(L.pair_blocks) * kV + 1;
   L.scan_tmp = take(((scan_len + kScanBlock - 1) / kScanBlock + 1) * 4);
   L.total = off;
