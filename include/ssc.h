@@ -68,7 +68,8 @@ enum ssc_status {
   SSC_ERR_HIP = 4,           /* a HIP runtime call failed */
   SSC_ERR_COORD_RANGE = 5,   /* device: some coordinate outside [0,B) x [0,X) x [0,Y) x [0,Z) */
   SSC_ERR_DUPLICATE = 6,     /* device: two rows share one coordinate */
-  SSC_ERR_HASH_FULL = 7      /* device: the coordinate hash table overflowed */
+  SSC_ERR_HASH_FULL = 7,     /* device: the coordinate hash table overflowed */
+  SSC_ERR_SCRATCH = 8        /* the call needs more than the built-in scratch of the no-allocation entry point */
 };
 
 /* Largest number of active voxels one plan may hold (27 * n stays below 2^31). */
@@ -163,6 +164,24 @@ int ssc_subm_conv3d_fwd(const void* plan, const uint32_t* nmap, const int32_t* p
                         int32_t Ci, int32_t Co, int32_t dtype, const void* feats,
                         const void* weight, const void* bias, void* out, void* workspace,
                         size_t workspace_bytes, void* stream);
+
+/*
+ * ssc_subm_conv3d_fwd for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments and result without the workspace.  Its
+ * workspace is a scratch array of SSC_NOALLOC_SCRATCH_BYTES compiled into the
+ * library, one per GPU, held until the process ends; the first call on a GPU
+ * looks its address up (no allocation).  Layers whose workspace
+ * (ssc_conv_workspace_bytes) exceeds that size return SSC_ERR_SCRATCH and
+ * enqueue nothing.  Every call on one GPU shares that GPU's array, so calls
+ * that overlap in time on one GPU (on different streams) race; calls ordered
+ * on one stream do not.  The array keeps the last call's contents; nothing the
+ * forward pass reads from it starts from a previous call's values.
+ */
+#define SSC_NOALLOC_SCRATCH_BYTES (64LL << 20)
+int ssc_subm_conv3d_fwd_noalloc(const void* plan, const uint32_t* nmap, const int32_t* perm, int64_t n,
+                                int32_t Ci, int32_t Co, int32_t dtype, const void* feats,
+                                const void* weight, const void* bias, void* out, void* stream);
 
 /*
  * Backward pass.  dout [n][Co] is dY.  Each output may be NULL to skip it:

@@ -17,7 +17,8 @@ _lib = None
 
 SSC_OK = 0
 STATUS_NAMES = {0: "SSC_OK", 1: "SSC_ERR_INVALID_ARG", 2: "SSC_ERR_UNSUPPORTED", 3: "SSC_ERR_WORKSPACE",
-                4: "SSC_ERR_HIP", 5: "SSC_ERR_COORD_RANGE", 6: "SSC_ERR_DUPLICATE", 7: "SSC_ERR_HASH_FULL"}
+                4: "SSC_ERR_HIP", 5: "SSC_ERR_COORD_RANGE", 6: "SSC_ERR_DUPLICATE", 7: "SSC_ERR_HASH_FULL",
+                8: "SSC_ERR_SCRATCH"}
 DTYPE_CODE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 
 _VP, _I64, _I32, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
@@ -29,6 +30,7 @@ SIGNATURES = {
     "ssc_plan_row_orders": (ctypes.c_int, [_VP, _VP, ctypes.POINTER(_I64)]),
     "ssc_conv_workspace_bytes": (_SZ, [_I64, _I32, _I32, _I32]),
     "ssc_subm_conv3d_fwd": (ctypes.c_int, [_VP, _VP, _VP, _I64, _I32, _I32, _I32, _VP, _VP, _VP, _VP, _VP, _SZ, _VP]),
+    "ssc_subm_conv3d_fwd_noalloc": (ctypes.c_int, [_VP, _VP, _VP, _I64, _I32, _I32, _I32, _VP, _VP, _VP, _VP, _VP]),
     "ssc_subm_conv3d_bwd": (ctypes.c_int, [_VP, _VP, _VP, _I64, _I32, _I32, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                                            _SZ, _VP]),
     "ssc_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -208,6 +210,27 @@ def subm_conv3d_fwd(plan: Plan, feats: torch.Tensor, weight: torch.Tensor, bias:
            lib().ssc_subm_conv3d_fwd(_ptr(plan.buf), _ptr(plan.nmap), _ptr(plan.perm), n, ci, co, DTYPE_CODE[dt],
                                      _ptr(feats), _ptr(weight), _ptr(bias), _ptr(out), _ptr(ws), ws.numel(),
                                      _stream(dev)))
+    return out
+
+
+def subm_conv3d_fwd_noalloc(plan: Plan, feats: torch.Tensor, weight: torch.Tensor, bias: torch.Tensor | None = None,
+                            out: torch.Tensor | None = None) -> torch.Tensor:
+    """ssc_subm_conv3d_fwd_noalloc: the forward pass on the library's built-in scratch (no workspace)."""
+    dev, dt, n = plan.device, feats.dtype, plan.n
+    ci, co = int(weight.shape[1]), int(weight.shape[2])
+    if dt not in DTYPE_CODE:
+        raise SSCError("ssc_subm_conv3d_fwd_noalloc", 2)
+    _need(feats, "feats", dt, (n, ci), dev)
+    _need(weight, "weight", dt, (27, ci, co), dev)
+    if bias is not None:
+        _need(bias, "bias", dt, (co,), dev)
+    if out is None:
+        out = torch.empty((n, co), dtype=dt, device=dev)
+    _need(out, "out", dt, (n, co), dev)
+    _check("ssc_subm_conv3d_fwd_noalloc",
+           lib().ssc_subm_conv3d_fwd_noalloc(_ptr(plan.buf), _ptr(plan.nmap), _ptr(plan.perm), n, ci, co,
+                                             DTYPE_CODE[dt], _ptr(feats), _ptr(weight), _ptr(bias), _ptr(out),
+                                             _stream(dev)))
     return out
 
 

@@ -31,6 +31,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "ssc_internal.h"
 
 namespace ssc {
@@ -1604,6 +1606,78 @@ extern "C" int ssc_subm_conv3d_fwd(const void* plan, const uint32_t* nmap, const
   char* ws = static_cast<char*>(workspace);
   (void)hipGetLastError();
   by_dtype(dtype, [&](auto t) { run_fwd<decltype(t)>(v, Ci, Co, feats, weight, bias, out, ws, s); });
+  return hipGetLastError() == hipSuccess ? SSC_OK : SSC_ERR_HIP;
+}
+
+// ---------------------------------------------------------------------------
+// forward pass without a caller workspace
+// ---------------------------------------------------------------------------
+
+// The workspace of ssc_subm_conv3d_fwd_noalloc.  Each GPU the library runs on
+// holds its own copy from module load until the process ends.  Host code must
+// not use this name as a device address: the address of each GPU's copy comes
+// from hipGetSymbolAddress, looked up once per GPU with that GPU current.
+static __device__ __align__(256) char scratch[SSC_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex scratch_mutex;
+void* scratch_address[kMaxScratchDevices] = {};
+
+// Device address of the scratch array on the GPU that runs `stream`.
+int scratch_for_stream(hipStream_t stream, void** out) {
+  int dev = -1;
+  if (stream) {
+    if (hipStreamGetDevice(stream, &dev) != hipSuccess) return SSC_ERR_HIP;
+  } else if (hipGetDevice(&dev) != hipSuccess) {
+    return SSC_ERR_HIP;
+  }
+  if (dev < 0 || dev >= kMaxScratchDevices) return SSC_ERR_HIP;
+  std::lock_guard<std::mutex> lock(scratch_mutex);
+  if (!scratch_address[dev]) {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return SSC_ERR_HIP;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return SSC_ERR_HIP;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev && hipSetDevice(cur) != hipSuccess) return SSC_ERR_HIP;
+    if (e != hipSuccess || !p) return SSC_ERR_HIP;
+    scratch_address[dev] = p;
+  }
+  *out = scratch_address[dev];
+  return SSC_OK;
+}
+
+}  // namespace
+
+extern "C" int ssc_subm_conv3d_fwd_noalloc(const void* plan, const uint32_t* nmap, const int32_t* perm, int64_t n,
+                                           int32_t Ci, int32_t Co, int32_t dtype, const void* feats,
+                                           const void* weight, const void* bias, void* out, void* stream) {
+  if (n < 0 || n > SSC_MAX_VOXELS || !plan || !weight) return SSC_ERR_INVALID_ARG;
+  if (dtype != SSC_F32 && dtype != SSC_F16 && dtype != SSC_BF16) return SSC_ERR_UNSUPPORTED;
+  if (!channels_ok(Ci, Co, dtype)) return SSC_ERR_UNSUPPORTED;
+  if (n > 0 && (!nmap || !perm || !feats || !out)) return SSC_ERR_INVALID_ARG;
+  const void* ptrs[] = {plan, nmap, perm, feats, weight, bias, out};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return SSC_ERR_INVALID_ARG;
+  if (n == 0) return SSC_OK;
+  // the same workspace layout as ssc_subm_conv3d_fwd, checked before any HIP call
+  if (ws_layout(n, n, Ci, Co, esize_of(dtype), true).total > size_t(SSC_NOALLOC_SCRATCH_BYTES))
+    return SSC_ERR_SCRATCH;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  void* ws = nullptr;
+  const int st = scratch_for_stream(s, &ws);
+  if (st != SSC_OK) return st;
+  const char* pl = static_cast<const char*>(plan);
+  ConvView v{pl, perm, n, pl, perm, n, kV};
+  v.parts = true;
+  (void)hipGetLastError();
+  // every region of the workspace the forward kernels read is written first in
+  // this call (W transposed, Split-K and part sums), so nothing is cleared
+  by_dtype(dtype, [&](auto t) {
+    run_fwd<decltype(t)>(v, Ci, Co, feats, weight, bias, out, static_cast<char*>(ws), s);
+  });
   return hipGetLastError() == hipSuccess ? SSC_OK : SSC_ERR_HIP;
 }
 

@@ -1005,6 +1005,7 @@ extern "C" const char* ssc_status_string(int status) {
     case SSC_ERR_COORD_RANGE: return "coordinate out of range";
     case SSC_ERR_DUPLICATE: return "duplicate coordinate";
     case SSC_ERR_HASH_FULL: return "hash table full";
+    case SSC_ERR_SCRATCH: return "larger than the built-in scratch of the no-allocation entry point";
     default: return "unknown status";
   }
 }

@@ -39,7 +39,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_status_strings(L):
-    for code in range(8):
+    for code in range(9):
         assert L.ssc_status_string(code)
     assert L.ssc_status_string(99) == b"unknown status"
 
@@ -100,6 +100,20 @@ def test_conv_rejects_on_host(L):
     assert b(FAKE, FAKE, FAKE, 100, 32, 32, 0, None, FAKE, FAKE, None, FAKE, None, FAKE, 1 << 30, None) == 1
     assert b(FAKE, FAKE, FAKE, 100, 32, 44, 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == 2
     assert b(FAKE, FAKE, FAKE, 100, 36, 32, 2, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == 2
+
+
+def test_noalloc_forward_rejects_on_host(L):
+    f = L.ssc_subm_conv3d_fwd_noalloc
+    # arguments as ssc_subm_conv3d_fwd, checked before any HIP call
+    assert f(FAKE, FAKE, FAKE, 100, 32, 32, 5, FAKE, FAKE, None, FAKE, None) == 2       # dtype
+    assert f(FAKE, FAKE, FAKE, 100, 32, 20, 1, FAKE, FAKE, None, FAKE, None) == 2       # fp16 Co % 8
+    assert f(FAKE, FAKE, FAKE, 100, 32, 32, 0, None, FAKE, None, FAKE, None) == 1       # feats NULL
+    assert f(FAKE, FAKE, FAKE, -1, 32, 32, 0, FAKE, FAKE, None, FAKE, None) == 1
+    assert f(FAKE, FAKE, FAKE, 0, 32, 32, 0, None, FAKE, None, None, None) == 0         # nothing to do
+    # a layer whose workspace exceeds the built-in 64 MiB scratch (and every larger one) is refused
+    assert L.ssc_conv_workspace_bytes(1 << 22, 1024, 1024, 2) > 64 << 20
+    assert f(FAKE, FAKE, FAKE, 1 << 22, 1024, 1024, 2, FAKE, FAKE, None, FAKE, None) == 8
+    assert L.ssc_status_string(8).startswith(b"larger than the built-in scratch")
 
 
 def test_binding_raises_without_library(monkeypatch):
