@@ -124,7 +124,7 @@ def test_config2_voxels_full_check(ssc):
 
 
 def test_config4_voxels_sampled(ssc):
-    """Config 4 voxel set (1024^3 shells, 7.4M voxels, 64-bit keys, C = 64, fp16), one point per voxel,
+    """Config 4 voxel set (1024^3 shells, 6,416,526 voxels, 64-bit keys, C = 64, fp16), one point per voxel,
     as the benchmark runs it: sampled forward rows against the oracle, and the adjoint identity
     <fwd(F), G> = <F, bwd(G)> over the whole run."""
     w = WL.make_workload(4)
