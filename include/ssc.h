@@ -147,10 +147,10 @@ size_t ssc_conv_workspace_bytes(int64_t n, int32_t Ci, int32_t Co, int32_t dtype
 
 /*
  * Forward pass: out[n][Co] = the definition of out above.
- *   plan, nmap, perm  as filled by ssc_build_neighbor_map for these n rows.
- *                     The kernels read the plan (its sorted-order copy of
- *                     nmap, the sorted masks, the pair lists) and perm;
- *                     nmap itself is only checked (non-NULL, aligned).
+ *   plan, nmap, perm  as filled by ssc_build_neighbor_map for these n rows
+ *                     (unchanged since).  The kernels read all three: the
+ *                     plan's sorted masks, pair lists and row orders, perm,
+ *                     and the rows of nmap each tile of sorted rows needs.
  *   feats  [n][Ci], weight [27][Ci][Co], bias [Co] or NULL (zero), all `dtype`.
  *   out    [n][Co] `dtype`, out.
  * Ci and Co must be multiples of 8 (fp16, bf16) or 4 (fp32), so that every

@@ -166,7 +166,9 @@ __device__ __forceinline__ typename Elt<T>::frag_t a_frag(const u32x4 (&v)[NV], 
 // 0 bias + rounding + scatter to perm, 1 fp32 sums to pbuf[perm[r]], 3 those
 // sums plus this launch's back to pbuf, 2 those sums + this launch's + bias,
 // rounded, to out.  Map column c meets weight W[kbase + c], or W[kflip - c]
-// with flip.
+// with flip.  With `gmap` set (a 27-column map in original row order), the
+// tile's map rows are gathered from it through perm instead of read from the
+// sorted-order copy.
 struct GemmPart {
   const PlanHeader* hdr;
   int gate;
@@ -175,6 +177,7 @@ struct GemmPart {
   int kflip;
   int emode;
   float* pbuf;
+  const uint32_t* gmap = nullptr;
 };
 
 // Epilogue of a GEMM tile (see GemmPart): each wave holds FM x FN 32x32
@@ -280,19 +283,12 @@ __global__ void __launch_bounds__(64 * NWM * NWN)
   const int64_t row0 = int64_t(tile) * BM;
 
   // ---- prologue: rows, the tile's offset set, gather indices ----
-  // The tile's rows of the sorted-order map are one contiguous block; all of
+  // The tile's rows of a sorted-order map are one contiguous block; all of
   // its loads are issued before any is stored, so the prologue costs one
-  // memory round trip, independent of perm.
+  // memory round trip, independent of perm.  A map in original row order
+  // (gp.gmap) costs a second one: perm first, then the rows it names.
   constexpr int JV = (BM * MW + NT - 1) / NT;
   uint32_t jv[JV];
-  const int64_t jbase = row0 * MW, jend = n * MW;
-#pragma unroll
-  for (int q = 0; q < JV; ++q) {
-    const int64_t e = jbase + q * NT + tid;
-    jv[q] = (q * NT + tid < BM * MW && e < jend) ? snmap[e] : kSentinel;
-  }
-  if (tid == 0) tile_union = 0;
-  if (tid < NWM) wave_union[tid] = 0;
   int32_t pr = -1;
   uint32_t msk = 0;
   if (tid < BM) {
@@ -302,6 +298,27 @@ __global__ void __launch_bounds__(64 * NWM * NWN)
       msk = smask[g] & gp.kmask;
     }
   }
+  if (gp.gmap) {
+    static_assert(MW <= kV, "map rows");
+    if (tid < BM) prow[tid] = pr;
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < JV; ++q) {
+      const int el = q * NT + tid;
+      const int rr = el / MW, cc = el - rr * MW;
+      const int32_t p = el < BM * MW ? prow[rr] : -1;
+      jv[q] = p >= 0 ? gp.gmap[int64_t(p) * kV + cc] : kSentinel;
+    }
+  } else {
+    const int64_t jbase = row0 * MW, jend = n * MW;
+#pragma unroll
+    for (int q = 0; q < JV; ++q) {
+      const int64_t e = jbase + q * NT + tid;
+      jv[q] = (q * NT + tid < BM * MW && e < jend) ? snmap[e] : kSentinel;
+    }
+  }
+  if (tid == 0) tile_union = 0;
+  if (tid < NWM) wave_union[tid] = 0;
 #pragma unroll
   for (int q = 0; q < JV; ++q)
     if (q * NT + tid < BM * MW) jtab[q * NT + tid] = jv[q];
@@ -1315,9 +1332,9 @@ static void igemm_pick_rows(const T* A, const T* Bt, const T* bias, T* out, cons
 template <typename T, int MW>
 static void launch_igemm(const T* A, const T* Bt, const T* bias, T* out, const uint32_t* nmap,
                          const int32_t* perm, const uint32_t* smask, const T* zrow, int64_t n, int K, int N,
-                         int flip, float* partial, hipStream_t s) {
+                         int flip, float* partial, hipStream_t s, const uint32_t* gmap) {
   // every offset, one row order; with flip, column c meets W[MW - 1 - c]
-  const GemmPart gp{nullptr, 0, ~0u, 0, MW - 1, 0, nullptr};
+  const GemmPart gp{nullptr, 0, ~0u, 0, MW - 1, 0, nullptr, gmap};
   if (N > 128) igemm_pick_rows<T, MW, 8>(A, Bt, bias, out, nmap, perm, smask, zrow, n, K, N, flip, partial, s, gp);
   else if (N > 64) igemm_pick_rows<T, MW, 4>(A, Bt, bias, out, nmap, perm, smask, zrow, n, K, N, flip, partial, s, gp);
   else if (N > 32) igemm_pick_rows<T, MW, 2>(A, Bt, bias, out, nmap, perm, smask, zrow, n, K, N, flip, partial, s, gp);
@@ -1352,16 +1369,17 @@ static void igemm_part_go(const T* A, const T* Bt, const T* bias, T* out, const 
 // adding pbuf, the bias and the rounding.
 template <typename T>
 static void launch_igemm_split(const T* A, const T* Bt, const T* bias, T* out, const char* region,
-                               const int32_t* perm, int64_t n, int K, int N, int flip, float* pbuf, hipStream_t s) {
+                               const int32_t* perm, int64_t n, int K, int N, int flip, float* pbuf, hipStream_t s,
+                               const uint32_t* gmap) {
   const PlanLayout L = conv_layout(n);
   const PlanHeader* h = reinterpret_cast<const PlanHeader*>(region + L.header);
   const uint32_t* snmap = reinterpret_cast<const uint32_t*>(region + L.snmap);
   const uint32_t* smask = reinterpret_cast<const uint32_t*>(region + L.smask);
   const T* zrow = reinterpret_cast<const T*>(region + L.zrow);
   igemm_part_go<T, kV>(A, Bt, bias, out, snmap, perm, smask, zrow, n, K, N, flip, s,
-                       GemmPart{h, 2, ~0u, 0, kV - 1, 0, nullptr});
+                       GemmPart{h, 2, ~0u, 0, kV - 1, 0, nullptr, gmap});
   igemm_part_go<T, kV>(A, Bt, bias, out, snmap, perm, smask, zrow, n, K, N, flip, s,
-                       GemmPart{h, 1, kTopPartMask, 0, kV - 1, 1, pbuf});
+                       GemmPart{h, 1, kTopPartMask, 0, kV - 1, 1, pbuf, gmap});
   for (int q = kOwnOrderParts - 1; q >= 0; --q) {
     const int lo = q * kPartCols;
     igemm_part_go<T, kPartCols>(A, Bt, bias, out,
@@ -1375,11 +1393,11 @@ static void launch_igemm_split(const T* A, const T* Bt, const T* bias, T* out, c
 template <typename T>
 static void launch_igemm_w(int mw, const T* A, const T* Bt, const T* bias, T* out, const uint32_t* nmap,
                            const int32_t* perm, const uint32_t* smask, const T* zrow, int64_t n, int K, int N,
-                           int flip, float* partial, hipStream_t s) {
+                           int flip, float* partial, hipStream_t s, const uint32_t* gmap) {
   if (mw == kCompactCols)
-    launch_igemm<T, kCompactCols>(A, Bt, bias, out, nmap, perm, smask, zrow, n, K, N, flip, partial, s);
+    launch_igemm<T, kCompactCols>(A, Bt, bias, out, nmap, perm, smask, zrow, n, K, N, flip, partial, s, nullptr);
   else
-    launch_igemm<T, kV>(A, Bt, bias, out, nmap, perm, smask, zrow, n, K, N, flip, partial, s);
+    launch_igemm<T, kV>(A, Bt, bias, out, nmap, perm, smask, zrow, n, K, N, flip, partial, s, gmap);
 }
 
 // dbias stage 1 geometry: column vectors (16 bytes) per work item, all of them
@@ -1468,7 +1486,11 @@ struct ConvView {
   const uint32_t* map_f = nullptr;
   const uint32_t* map_b = nullptr;
   int mw = kV;
-  bool parts = false;  // a submanifold plan: its build may have taken the two-part split
+  bool parts = false;  // a submanifold plan: its build may have taken the three-part split
+  // a submanifold plan's map in original row order (the caller's nmap): the
+  // GEMMs gather their tiles' rows of it through perm (the plan keeps no
+  // sorted-order copy)
+  const uint32_t* gmap = nullptr;
 };
 
 static size_t view_ws_bytes(const ConvView& v, int Ci, int Co, int esize) {
@@ -1494,13 +1516,13 @@ static int run_fwd(const ConvView& v, int Ci, int Co, const void* feats, const v
   transpose_w<T><<<tg, 256, 0, s>>>(static_cast<const T*>(weight), wt, Ci, Co);
   if (v.parts && parts_possible(v.n_f, Ci, Co, sizeof(T))) {
     launch_igemm_split<T>(static_cast<const T*>(feats), wt, static_cast<const T*>(bias), static_cast<T*>(out), v.fwd,
-                          v.perm_f, v.n_f, Ci, Co, 0, reinterpret_cast<float*>(ws + W.part), s);
+                          v.perm_f, v.n_f, Ci, Co, 0, reinterpret_cast<float*>(ws + W.part), s, v.gmap);
     return SSC_OK;
   }
   launch_igemm_w<T>(v.mw, static_cast<const T*>(feats), wt, static_cast<const T*>(bias), static_cast<T*>(out),
                   v.map_f ? v.map_f : reinterpret_cast<const uint32_t*>(v.fwd + L.snmap), v.perm_f,
                   reinterpret_cast<const uint32_t*>(v.fwd + L.smask), reinterpret_cast<const T*>(v.fwd + L.zrow),
-                  v.n_f, Ci, Co, 0, reinterpret_cast<float*>(ws + W.split), s);
+                  v.n_f, Ci, Co, 0, reinterpret_cast<float*>(ws + W.split), s, v.gmap);
   return SSC_OK;
 }
 
@@ -1517,13 +1539,13 @@ static int run_bwd(const ConvView& v, int Ci, int Co, const void* feats, const v
       zero_out<T>(static_cast<T*>(dfeats), v.n_b * Ci, s);  // no outputs: nothing reaches the inputs
     } else if (v.parts && parts_possible(v.n_b, Ci, Co, sizeof(T))) {
       launch_igemm_split<T>(dY, static_cast<const T*>(weight), nullptr, static_cast<T*>(dfeats), v.bwd, v.perm_b,
-                            v.n_b, Co, Ci, 1, reinterpret_cast<float*>(ws + Wb.part), s);
+                            v.n_b, Co, Ci, 1, reinterpret_cast<float*>(ws + Wb.part), s, v.gmap);
     } else {
       launch_igemm_w<T>(v.mw, dY, static_cast<const T*>(weight), nullptr, static_cast<T*>(dfeats),
                       v.map_b ? v.map_b : reinterpret_cast<const uint32_t*>(v.bwd + Lb.snmap), v.perm_b,
                       reinterpret_cast<const uint32_t*>(v.bwd + Lb.smask),
                       reinterpret_cast<const T*>(v.bwd + Lb.zrow), v.n_b, Co, Ci, 1,
-                      reinterpret_cast<float*>(ws + Wb.split), s);
+                      reinterpret_cast<float*>(ws + Wb.split), s, v.gmap);
     }
   }
   if (v.n_f == 0) {
@@ -1603,6 +1625,7 @@ extern "C" int ssc_subm_conv3d_fwd(const void* plan, const uint32_t* nmap, const
   const char* pl = static_cast<const char*>(plan);
   ConvView v{pl, perm, n, pl, perm, n, kV};
   v.parts = true;
+  v.gmap = nmap;
   char* ws = static_cast<char*>(workspace);
   (void)hipGetLastError();
   by_dtype(dtype, [&](auto t) { run_fwd<decltype(t)>(v, Ci, Co, feats, weight, bias, out, ws, s); });
@@ -1672,6 +1695,7 @@ extern "C" int ssc_subm_conv3d_fwd_noalloc(const void* plan, const uint32_t* nma
   const char* pl = static_cast<const char*>(plan);
   ConvView v{pl, perm, n, pl, perm, n, kV};
   v.parts = true;
+  v.gmap = nmap;
   (void)hipGetLastError();
   // every region of the workspace the forward kernels read is written first in
   // this call (W transposed, Split-K and part sums), so nothing is cleared
@@ -1701,6 +1725,7 @@ extern "C" int ssc_subm_conv3d_bwd(const void* plan, const uint32_t* nmap, const
   const char* pl = static_cast<const char*>(plan);
   ConvView v{pl, perm, n, pl, perm, n, kV};
   v.parts = true;
+  v.gmap = nmap;
   char* ws = static_cast<char*>(workspace);
   (void)hipGetLastError();
   by_dtype(dtype, [&](auto t) {

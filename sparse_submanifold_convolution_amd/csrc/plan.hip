@@ -275,11 +275,21 @@ __device__ __forceinline__ void store_rows(uint32_t* rows, const uint32_t (&v)[k
   for (int t = 0; t < kV; ++t) rows[t * 256 + threadIdx.x] = v[t];
 }
 
+// Without bit 13 of the mask in the key (squeeze): where every row has its
+// centre offset that bit is constant and the order is the same with one key
+// bit, and often one radix pass, fewer.
+__device__ __forceinline__ uint32_t squeeze_centre(uint32_t m) {
+  return (m & ((1u << kCentre) - 1u)) | ((m >> 1) & ~((1u << kCentre) - 1u));
+}
+__device__ __forceinline__ uint32_t expand_centre(uint32_t v) {
+  return (v & ((1u << kCentre) - 1u)) | ((v & ~((1u << kCentre) - 1u)) << 1) | (1u << kCentre);
+}
+
 __global__ void __launch_bounds__(256) row_scan(const int4* __restrict__ coords, const uint32_t* __restrict__ nmap,
                                                 int64_t n, int B, int X, int Y, int Z, int axis_bits, int zbits,
                                                 uint64_t* __restrict__ sort_key, uint32_t* __restrict__ pcnt,
                                                 int64_t pblk, uint32_t* __restrict__ h0, uint32_t* __restrict__ h1,
-                                                int64_t nsb, int sort_block_keys) {
+                                                int64_t nsb, int sort_block_keys, int squeeze) {
   __shared__ uint32_t rows[256 * kV];
   __shared__ uint32_t cnt[32];
   __shared__ uint32_t dcnt[256];
@@ -315,7 +325,7 @@ __global__ void __launch_bounds__(256) row_scan(const int4* __restrict__ coords,
       if (coord_ok(c.x, c.y, c.z, c.w, B, X, Y, Z)) {
         const uint64_t z = (uint64_t(uint32_t(c.x)) << (3 * axis_bits)) |
                            zorder(uint32_t(c.y), uint32_t(c.z), uint32_t(c.w), axis_bits);
-        key = (uint64_t(mask) << zbits) | z;
+        key = (uint64_t(squeeze ? squeeze_centre(mask) : mask) << zbits) | z;
       }
       sort_key[i] = key;
       if (h0) atomicAdd(&dcnt[uint32_t(key) & 255u], 1u);
@@ -400,7 +410,7 @@ __global__ void __launch_bounds__(kSortThreads)
                   const uint32_t* __restrict__ offsets, int64_t nblk, int first, int last,
                   int32_t* __restrict__ perm, uint32_t* __restrict__ smask, int zbits, int direct,
                   uint32_t* __restrict__ hnext, uint32_t* __restrict__ hclear, PairJob pj,
-                  const uint32_t* __restrict__ gate) {
+                  const uint32_t* __restrict__ gate, int squeezed) {
   if (gated_off(gate)) return;
   if constexpr (FUSE) {
     if (int64_t(blockIdx.x) >= nblk) {
@@ -486,7 +496,7 @@ __global__ void __launch_bounds__(kSortThreads)
         atomicAdd(&nxt[((key >> (shift + 8)) & 255u) * nblk + pos / kBlockKeys], 1u);
       if (last) {
         perm[pos] = int32_t(val);
-        smask[pos] = uint32_t(key >> zbits);
+        smask[pos] = squeezed ? expand_centre(uint32_t(key >> zbits)) : uint32_t(key >> zbits);
       } else {
         keys_out[pos] = key;
         vals_out[pos] = val;
@@ -732,14 +742,14 @@ static inline unsigned grid1d(int64_t work, int threads) {
 // keys and payloads.
 static void sort_pass(const uint64_t* kin, const uint32_t* vin, uint64_t* kout, uint32_t* vout, int64_t n,
                       int shift, bool first, bool last, int32_t* perm, uint32_t* smask, int zbits, uint32_t* hist,
-                      uint32_t* scan_tmp, const uint32_t* gate, hipStream_t s) {
+                      uint32_t* scan_tmp, const uint32_t* gate, int squeezed, hipStream_t s) {
   const int64_t nblk = (n + kSortThreads * kSortItems - 1) / (kSortThreads * kSortItems);
   const PairJob no_pairs{nullptr, nullptr, 0, nullptr, nullptr, nullptr, nullptr};
   radix_hist<kSortItems><<<unsigned(nblk), kSortThreads, 0, s>>>(kin, n, shift, hist, nblk, gate);
   launch_scan(hist, nblk * 256 + 1, scan_tmp, s, gate);
   radix_scatter<false, kSortItems><<<unsigned(nblk), kSortThreads, 0, s>>>(
       kin, vin, kout, vout, n, shift, hist, nblk, first ? 1 : 0, last ? 1 : 0, perm, smask, zbits, 0, nullptr,
-      nullptr, no_pairs, gate);
+      nullptr, no_pairs, gate, squeezed);
 }
 
 }  // namespace ssc
@@ -794,7 +804,7 @@ void insert_coords(const int4* c4, int64_t n, int B, int X, int Y, int Z, int kb
 }
 
 void order_rows(const int4* c4, const uint32_t* nmap, int64_t n, int B, int X, int Y, int Z, int32_t* perm,
-                char* base, const PlanLayout& L, bool want_pairs, hipStream_t s) {
+                char* base, const PlanLayout& L, bool want_pairs, bool centre, hipStream_t s) {
   if (n == 0) return;
   int axis_bits, zbits;
   sort_key_bits(B, X, Y, Z, &axis_bits, &zbits);
@@ -816,11 +826,13 @@ void order_rows(const int4* c4, const uint32_t* nmap, int64_t n, int B, int X, i
   // the first one was cleared by prepare_region
   const int direct = nblk <= kSortDirectBlocks ? 1 : 0;
   uint32_t* h0 = direct ? hist : nullptr;
+  // centre: every row has its centre offset (submanifold), so the key leaves that mask bit out
+  const int sq = centre ? 1 : 0;
   row_scan<<<unsigned(pblk), 256, 0, s>>>(c4, nmap, n, B, X, Y, Z, axis_bits, zbits, key0, pcnt, pblk, h0,
-                                          direct ? hist + nblk * 256 : nullptr, nblk, kSortThreads * L.sort_items);
+                                          direct ? hist + nblk * 256 : nullptr, nblk, kSortThreads * L.sort_items, sq);
 
-  // radix sort over the key's kV + zbits low bits
-  const int bits = kV + zbits;
+  // radix sort over the key's kV (- 1) + zbits low bits
+  const int bits = kV - sq + zbits;
   const int passes = (bits + 7) / 8;
   const uint64_t* kin = key0;
   const uint32_t* vin = val0;
@@ -845,13 +857,13 @@ void order_rows(const int4* c4, const uint32_t* nmap, int64_t n, int B, int X, i
       if (L.sort_items == kSortItemsSmall)
         radix_scatter<true, kSortItemsSmall><<<grid, kSortThreads, 0, s>>>(
             kin, vin, kout, vout, n, shift, hcur, nblk, p == 0 ? 1 : 0, last, perm, smask, zbits, 1, hnext,
-            last ? nullptr : hclr, pj, nullptr);
+            last ? nullptr : hclr, pj, nullptr, sq);
       else
         radix_scatter<true, kSortItems><<<grid, kSortThreads, 0, s>>>(
             kin, vin, kout, vout, n, shift, hcur, nblk, p == 0 ? 1 : 0, last, perm, smask, zbits, 1, hnext,
-            last ? nullptr : hclr, pj, nullptr);
+            last ? nullptr : hclr, pj, nullptr, sq);
     } else {
-      sort_pass(kin, vin, kout, vout, n, shift, p == 0, last, perm, smask, zbits, hist, scan_tmp, nullptr, s);
+      sort_pass(kin, vin, kout, vout, n, shift, p == 0, last, perm, smask, zbits, hist, scan_tmp, nullptr, sq, s);
     }
     const uint64_t* tk = kout;
     const uint32_t* tv = vout;
@@ -861,7 +873,10 @@ void order_rows(const int4* c4, const uint32_t* nmap, int64_t n, int B, int X, i
     vin = tv;
   }
 
-  permute_rows<<<grid1d(n * kV, 256), 256, 0, s>>>(nmap, perm, n, reinterpret_cast<uint32_t*>(base + L.snmap));
+  // The strided convolution's GEMMs read the map in sorted order; the
+  // submanifold GEMMs gather the rows of nmap itself through perm.
+  if (!centre)
+    permute_rows<<<grid1d(n * kV, 256), 256, 0, s>>>(nmap, perm, n, reinterpret_cast<uint32_t*>(base + L.snmap));
 
   // per-offset pair lists (already built by the first pass for small inputs)
   if (!want_pairs) return;
@@ -901,7 +916,7 @@ void order_parts(const int4* c4, const uint32_t* nmap, const int32_t* perm, int6
   uint32_t* vout = val1;
   for (int p = 0; p < passes; ++p) {
     sort_pass(kin, vin, kout, vout, nk, 8 * p, false, p == passes - 1, reinterpret_cast<int32_t*>(base + L.pperm),
-              reinterpret_cast<uint32_t*>(base + L.psmask), zbits, hist, scan_tmp, gate, s);
+              reinterpret_cast<uint32_t*>(base + L.psmask), zbits, hist, scan_tmp, gate, 0, s);
     const uint64_t* tk = kout;
     const uint32_t* tv = vout;
     kout = const_cast<uint64_t*>(kin);
@@ -948,7 +963,7 @@ extern "C" int ssc_build_neighbor_map(const int32_t* coords, int64_t n, int32_t 
   else
     probe_half<uint32_t><<<grid1d(n * kCentre, 256), 256, 0, s>>>(
         c4, n, B, X, Y, Z, reinterpret_cast<const Slot<uint32_t>*>(base + L.table), L.capacity, nmap);
-  order_rows(c4, nmap, n, B, X, Y, Z, perm, base, L, true, s);
+  order_rows(c4, nmap, n, B, X, Y, Z, perm, base, L, true, true, s);
   if (parts) order_parts(c4, nmap, perm, n, B, X, Y, Z, base, L, s);
   return hipGetLastError() == hipSuccess ? SSC_OK : SSC_ERR_HIP;
 }

@@ -341,8 +341,8 @@ extern "C" int ssc_build_sparse_map(const int32_t* coords_in, int64_t n_in, int3
           reinterpret_cast<const Slot<uint32_t>*>(bb + S.b.table), S.b.capacity, nmap, tmap);
   }
   // GEMM order, sorted maps and (forward direction) the pair lists the weight gradient walks
-  order_rows(co, nmap, n_out, od[0], od[1], od[2], od[3], perm_out, fb, S.f, true, s);
-  order_rows(ci, tmap, n_in, B, X, Y, Z, perm_in, bb, S.b, false, s);
+  order_rows(co, nmap, n_out, od[0], od[1], od[2], od[3], perm_out, fb, S.f, true, false, s);
+  order_rows(ci, tmap, n_in, B, X, Y, Z, perm_in, bb, S.b, false, false, s);
   if (S.o.compact) {
     // 8-column copies for the GEMMs: the forward map's columns 0..7, the transposed map's 19..26
     if (n_out > 0)

@@ -113,7 +113,7 @@ struct PlanLayout {
   size_t header = 0;
   size_t zrow = 0;    // kZeroRowBytes of zeros (a row of up to 4096 fp32 channels)
   size_t smask = 0;   // [n] u32: neighbour mask of the row at each sorted position
-  size_t snmap = 0;   // [n][27] u32: nmap rows in sorted order, snmap[r] = nmap[perm[r]]
+  size_t snmap = 0;   // [n][27] u32: nmap rows in sorted order, snmap[r] = nmap[perm[r]] (strided plans)
   size_t pair_i = 0;  // [27n] u32: pair lists, output row i
   size_t pair_j = 0;  // [27n] u32: pair lists, input row j = nmap[i][k]
   size_t pseg = 0;    // [27][pblk + 1] u32: where each kPairRows block of rows starts in each list
@@ -280,11 +280,12 @@ void prepare_region(char* base, const PlanLayout& L, int64_t n, int B, int X, in
 // coordinate check and hash insert of n rows into the region's table
 void insert_coords(const int4* c4, int64_t n, int B, int X, int Y, int Z, int kb, char* base,
                    const PlanLayout& L, hipStream_t s);
-// masks, (mask, z-order) sort -> perm and sorted masks, the sorted-order map,
-// and (want_pairs) the per-offset pair lists, of a [n][27] map whose rows sit
-// at coords in grid (B, X, Y, Z)
+// masks, (mask, z-order) sort -> perm and sorted masks, and (want_pairs) the
+// per-offset pair lists, of a [n][27] map whose rows sit at coords in grid
+// (B, X, Y, Z); centre: every row has its centre offset (a submanifold map),
+// otherwise the sorted-order copy of the map is written too
 void order_rows(const int4* c4, const uint32_t* nmap, int64_t n, int B, int X, int Y, int Z, int32_t* perm,
-                char* base, const PlanLayout& L, bool want_pairs, hipStream_t s);
+                char* base, const PlanLayout& L, bool want_pairs, bool centre, hipStream_t s);
 
 // round-to-nearest-even float -> bfloat16 bits
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
