@@ -67,9 +67,10 @@ def parse():
     return p.parse_args()
 
 
-# the sources the masked implicit GEMM is compiled from: its translation unit and the headers it includes
+# the sources the masked implicit GEMM's work depends on: its translation unit, the plan builder that
+# orders its rows, and the headers they include
 GEMM_SOURCES = ("sparse_submanifold_convolution_amd/csrc/conv.hip", "sparse_submanifold_convolution_amd/csrc/ssc_internal.h",
-                "include/ssc.h")
+                "sparse_submanifold_convolution_amd/csrc/plan.hip", "include/ssc.h")
 
 
 def source_hash() -> str:
@@ -82,7 +83,8 @@ def source_hash() -> str:
 
 
 def measured_traffic(kernel: str, workload: str):
-    """HBM bytes per launch from the committed counter summary, if it matches the current sources."""
+    """HBM bytes per call (all launches of one call) from the committed counter summary, if it matches the
+    current sources."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
@@ -91,7 +93,7 @@ def measured_traffic(kernel: str, workload: str):
     rec = data.get(f"{kernel}|{workload}")
     if not rec or rec.get("source_hash") != source_hash():
         return None
-    return rec.get("bytes_per_launch")
+    return rec.get("bytes_per_call")
 
 
 def measured_counters(kernel: str, workload: str):

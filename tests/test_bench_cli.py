@@ -23,6 +23,7 @@ def test_traffic_record_matches_gemm_sources():
     with open(os.path.join(ROOT, "profiles", "traffic.json")) as f:
         data = json.load(f)
     stored = data["igemm|cfg2"]["source_hash"]
+    assert "bytes_per_call" in data["igemm|cfg2"]
     if stored == bench.source_hash():
         assert rec is not None and rec > 0
     else:
