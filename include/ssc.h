@@ -77,11 +77,15 @@ enum ssc_status {
 
 /*
  * Bytes of device memory a plan for n voxels needs.  key_bits selects the
- * width of the packed coordinate key ((b*X + x)*Y + y)*Z + z in the hash
- * table: 0 picks 32 bits when B*X*Y*Z <= 2^32 - 1 and 64 bits otherwise (the
- * report's init_hashmap picks uint32 or uint64 by grid volume, section two
- * module table); 32 or 64 force a width (32 fails when the volume does not
- * fit).  Returns 0 for invalid arguments.  Needs no GPU.
+ * width of the packed coordinate keys of the voxel hash table: 0 picks 32
+ * bits when B*X*Y*Z <= 2^32 - 1 and 64 bits otherwise (the report's
+ * init_hashmap picks uint32 or uint64 by grid volume, section two module
+ * table); 32 or 64 force a width (32 fails when the volume does not fit).
+ * The table is keyed by bricks of 4 x 4 x 4 cells, key
+ * ((b*X4 + x/4)*Y4 + y/4)*Z4 + z/4 with X4 = ceil(X/4) and so on, each slot
+ * holding the brick's 64-bit occupancy mask; the brick grid is never larger
+ * than the voxel grid, so the same width holds.  Returns 0 for invalid
+ * arguments.  Needs no GPU.
  */
 size_t ssc_plan_bytes(int64_t n, int32_t B, int32_t X, int32_t Y, int32_t Z, int32_t key_bits);
 
@@ -98,10 +102,14 @@ size_t ssc_plan_bytes(int64_t n, int32_t B, int32_t X, int32_t Y, int32_t Z, int
  *          sorted_idx).  Coordinates are unique, so perm is unique.
  *   plan   ssc_plan_bytes(...) bytes, out: the neighbour cache that
  *          ssc_subm_conv3d_fwd/bwd read; valid while coords are unchanged.
- * Kernels: coordinate check + hash insert (atomicCAS on 32/64-bit keys),
- * one probe per (voxel, offset) with per-axis bounds checked before any key
- * is packed, mask and sort key, stable LSD radix sort, per-offset pair lists.
- * n == 0 is valid.  Device-side problems are reported by ssc_plan_status.
+ * Kernels: coordinate check + insert of each voxel's brick (atomicCAS on
+ * 32/64-bit keys, the cell's bit ORed into the slot's occupancy mask), the
+ * voxel rows grouped by brick, one lookup per (brick, neighbouring brick)
+ * and then every (voxel, offset) entry from the neighbour cell's bit, with
+ * per-axis bounds checked before any key is packed; mask and sort key,
+ * stable LSD radix sort, per-offset pair lists.  n == 0 is valid.
+ * Device-side problems are reported by ssc_plan_status; after such a
+ * problem every map entry is still a row index or the sentinel.
  */
 int ssc_build_neighbor_map(const int32_t* coords, int64_t n, int32_t B, int32_t X, int32_t Y,
                            int32_t Z, int32_t key_bits, uint32_t* nmap, int32_t* perm,

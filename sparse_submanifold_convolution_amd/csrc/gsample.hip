@@ -115,7 +115,7 @@ __device__ __forceinline__ float corner_weight(const float4 p, int j) {
 // no sample, the corner is off the grid or no voxel sits there.
 template <typename KeyT>
 __device__ __forceinline__ uint32_t corner_row(const float4 p, int j, const GsGrid g,
-                                               const Slot<KeyT>* __restrict__ table, uint64_t capacity) {
+                                               const VoxelTable<KeyT>& table) {
   // NaN fails every comparison below, so it lands here too
   if (!(p.x >= 0.f && p.x < float(g.B) && p.x == floorf(p.x))) return kSentinel;
   if (!(p.y > -1.f && p.y < float(g.X) && p.z > -1.f && p.z < float(g.Y) && p.w > -1.f && p.w < float(g.Z)))
@@ -124,28 +124,28 @@ __device__ __forceinline__ uint32_t corner_row(const float4 p, int j, const GsGr
   const int cy = int(floorf(p.z)) + ((j >> 1) & 1);
   const int cz = int(floorf(p.w)) + (j & 1);
   if (cx < 0 || cx >= g.X || cy < 0 || cy >= g.Y || cz < 0 || cz >= g.Z) return kSentinel;
-  return hash_lookup<KeyT>(table, capacity, KeyT(pack_key(int(p.x), cx, cy, cz, g.X, g.Y, g.Z)));
+  return voxel_lookup<KeyT>(table, int(p.x), cx, cy, cz);
 }
 
 // corner row and weight (0 when absent)
 template <typename KeyT>
 __device__ __forceinline__ void corner_lookup(const float4 p, int j, const GsGrid g,
-                                              const Slot<KeyT>* __restrict__ table, uint64_t capacity,
+                                              const VoxelTable<KeyT>& table,
                                               uint32_t* row, float* w) {
-  *row = corner_row<KeyT>(p, j, g, table, capacity);
+  *row = corner_row<KeyT>(p, j, g, table);
   *w = *row == kSentinel ? 0.f : corner_weight(p, j);
 }
 
 // The 8 corners of the group's point, shared from the group's first 8 lanes.
 template <typename KeyT, int L>
 __device__ __forceinline__ void group_corners(const float4* __restrict__ pts, int64_t p, const GsGrid g,
-                                              const Slot<KeyT>* __restrict__ table, uint64_t capacity,
+                                              const VoxelTable<KeyT>& table,
                                               uint32_t (&rows)[8], float (&ws)[8]) {
   static_assert(L >= 8 && L <= 64 && (L & (L - 1)) == 0, "a group is 8..64 lanes, a power of two");
   const int q = threadIdx.x % L;
   uint32_t row = kSentinel;
   float w = 0.f;
-  if (q < 8) corner_lookup<KeyT>(pts[p], q, g, table, capacity, &row, &w);
+  if (q < 8) corner_lookup<KeyT>(pts[p], q, g, table, &row, &w);
   const int first = int(threadIdx.x % 64) - q;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
@@ -157,7 +157,7 @@ __device__ __forceinline__ void group_corners(const float4* __restrict__ pts, in
 template <int DT, typename KeyT, int L>
 __global__ void __launch_bounds__(256) gs_fwd(const u32x4* __restrict__ feats, const float4* __restrict__ pts,
                                               int64_t m, int nvec, const GsGrid g,
-                                              const Slot<KeyT>* __restrict__ table, uint64_t capacity,
+                                              const VoxelTable<KeyT> table,
                                               const u32x4* __restrict__ zrow, u32x4* __restrict__ out) {
   using V = GsVec<DT>;
   constexpr int kG = 256 / L;
@@ -165,7 +165,7 @@ __global__ void __launch_bounds__(256) gs_fwd(const u32x4* __restrict__ feats, c
   if (p >= m) return;  // uniform over the group
   uint32_t rows[8];
   float ws[8];
-  group_corners<KeyT, L>(pts, p, g, table, capacity, rows, ws);
+  group_corners<KeyT, L>(pts, p, g, table, rows, ws);
   for (int v = int(threadIdx.x % L); v < nvec; v += L) {
     u32x4 x[8];
 #pragma unroll
@@ -189,11 +189,11 @@ __global__ void __launch_bounds__(256) gs_fwd(const u32x4* __restrict__ feats, c
 // corner's row into idx[t] and one count for that voxel.
 template <typename KeyT>
 __global__ void __launch_bounds__(256) gs_pairs(const float4* __restrict__ pts, int64_t m, const GsGrid g,
-                                                const Slot<KeyT>* __restrict__ table, uint64_t capacity,
+                                                const VoxelTable<KeyT> table,
                                                 uint32_t* __restrict__ idx, uint32_t* __restrict__ cnt) {
   const int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x;
   if (t >= m * 8) return;
-  const uint32_t r = corner_row<KeyT>(pts[t >> 3], int(t & 7), g, table, capacity);
+  const uint32_t r = corner_row<KeyT>(pts[t >> 3], int(t & 7), g, table);
   idx[t] = r;
   if (r != kSentinel) atomicAdd(&cnt[r], 1u);
 }
@@ -265,18 +265,18 @@ unsigned stream_grid(int64_t count) {
 int group_lanes(int nvec) { return nvec <= 8 ? 8 : nvec <= 16 ? 16 : nvec <= 32 ? 32 : 64; }
 
 template <int DT, typename KeyT>
-void launch_fwd(const void* feats, const float* pts, int64_t m, int nvec, GsGrid g, const Slot<KeyT>* table,
-                uint64_t capacity, const void* zrow, void* out, hipStream_t s) {
+void launch_fwd(const void* feats, const float* pts, int64_t m, int nvec, GsGrid g, const VoxelTable<KeyT> table,
+                const void* zrow, void* out, hipStream_t s) {
   const int L = group_lanes(nvec);
   const unsigned grid = unsigned((m + (256 / L) - 1) / (256 / L));
   const u32x4* f = static_cast<const u32x4*>(feats);
   const float4* p = reinterpret_cast<const float4*>(pts);
   const u32x4* z = static_cast<const u32x4*>(zrow);
   u32x4* o = static_cast<u32x4*>(out);
-  if (L == 8) gs_fwd<DT, KeyT, 8><<<grid, 256, 0, s>>>(f, p, m, nvec, g, table, capacity, z, o);
-  else if (L == 16) gs_fwd<DT, KeyT, 16><<<grid, 256, 0, s>>>(f, p, m, nvec, g, table, capacity, z, o);
-  else if (L == 32) gs_fwd<DT, KeyT, 32><<<grid, 256, 0, s>>>(f, p, m, nvec, g, table, capacity, z, o);
-  else gs_fwd<DT, KeyT, 64><<<grid, 256, 0, s>>>(f, p, m, nvec, g, table, capacity, z, o);
+  if (L == 8) gs_fwd<DT, KeyT, 8><<<grid, 256, 0, s>>>(f, p, m, nvec, g, table, z, o);
+  else if (L == 16) gs_fwd<DT, KeyT, 16><<<grid, 256, 0, s>>>(f, p, m, nvec, g, table, z, o);
+  else if (L == 32) gs_fwd<DT, KeyT, 32><<<grid, 256, 0, s>>>(f, p, m, nvec, g, table, z, o);
+  else gs_fwd<DT, KeyT, 64><<<grid, 256, 0, s>>>(f, p, m, nvec, g, table, z, o);
 }
 
 template <int DT>
@@ -298,11 +298,9 @@ void dispatch_fwd(int kb, const char* plan, const PlanLayout& L, const void* fea
                   int nvec, GsGrid g, void* out, hipStream_t s) {
   const void* zrow = plan + L.zrow;
   if (kb == 64)
-    launch_fwd<DT, uint64_t>(feats, pts, m, nvec, g, reinterpret_cast<const Slot<uint64_t>*>(plan + L.table),
-                             L.capacity, zrow, out, s);
+    launch_fwd<DT, uint64_t>(feats, pts, m, nvec, g, voxel_table<uint64_t>(plan, L, g.X, g.Y, g.Z), zrow, out, s);
   else
-    launch_fwd<DT, uint32_t>(feats, pts, m, nvec, g, reinterpret_cast<const Slot<uint32_t>*>(plan + L.table),
-                             L.capacity, zrow, out, s);
+    launch_fwd<DT, uint32_t>(feats, pts, m, nvec, g, voxel_table<uint32_t>(plan, L, g.X, g.Y, g.Z), zrow, out, s);
 }
 
 // workspace of the backward pass: bucket starts (n + 1), fill counters (n),
@@ -416,11 +414,9 @@ extern "C" int ssc_grid_sample_bwd(const void* plan, int64_t n, int32_t B, int32
   const float4* p4 = reinterpret_cast<const float4*>(points);
   const unsigned pgrid = unsigned((m * 8 + 255) / 256);
   if (kb == 64)
-    gs_pairs<uint64_t><<<pgrid, 256, 0, s>>>(p4, m, g, reinterpret_cast<const Slot<uint64_t>*>(pl + L.table),
-                                            L.capacity, idx, start);
+    gs_pairs<uint64_t><<<pgrid, 256, 0, s>>>(p4, m, g, voxel_table<uint64_t>(pl, L, g.X, g.Y, g.Z), idx, start);
   else
-    gs_pairs<uint32_t><<<pgrid, 256, 0, s>>>(p4, m, g, reinterpret_cast<const Slot<uint32_t>*>(pl + L.table),
-                                            L.capacity, idx, start);
+    gs_pairs<uint32_t><<<pgrid, 256, 0, s>>>(p4, m, g, voxel_table<uint32_t>(pl, L, g.X, g.Y, g.Z), idx, start);
   launch_scan(start, n + 1, tmp, s);
   gs_place<<<pgrid, 256, 0, s>>>(idx, m * 8, start, fill, list);
   if (dtype == SSC_F32) launch_gather<SSC_F32>(list, start, n, points, dout, nvec, dfeats, s);

@@ -1,5 +1,5 @@
-// Voxel hash table shared by the plan builder and the grid sampler: keys,
-// slots, the mixing function and the lookup.
+// Voxel hash table shared by the plan builder, the strided-map builder and the
+// grid sampler: keys, slots, the mixing function and the lookup.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -27,19 +27,31 @@ __device__ __forceinline__ uint32_t mix_hash(uint64_t k) {
   return uint32_t(k);
 }
 
-// One hash-table slot: the key and its row index side by side, so a lookup
-// that hits reads one aligned 8- or 16-byte entry.
+// The voxel table is an open-addressing hash keyed by bricks of 4 x 4 x 4
+// cells: the key packs the brick's coordinates (batch, x/4, y/4, z/4) in 32 or
+// 64 bits, and the slot holds the brick's 64-bit occupancy mask beside it.  A
+// brick's voxel rows sit side by side in `rows` from `base[slot]` on, in the
+// order of their cells' mask bits, so a voxel's row is found by one slot read,
+// a mask test (which answers a miss at once) and a popcount.  The neighbours of
+// a voxel mostly share its brick or an adjacent one, so the lookups of
+// neighbouring voxels hit the same few slots in cache instead of one random
+// line each.
+constexpr int kBrickShift = 2;                 // 4 cells per brick side
+constexpr uint32_t kCreator = 0x80000000u;     // vslot flag: this voxel inserted its brick's key
+
 template <typename KeyT>
-struct Slot;
+struct BrickSlot;
 template <>
-struct __align__(8) Slot<uint32_t> {
-  uint32_t key, val;
+struct __align__(16) BrickSlot<uint32_t> {
+  uint32_t key, pad;
+  unsigned long long mask;
 };
 template <>
-struct __align__(16) Slot<uint64_t> {
-  uint64_t key;
-  uint32_t val, pad;
+struct __align__(16) BrickSlot<uint64_t> {
+  unsigned long long key;
+  unsigned long long mask;
 };
+static_assert(sizeof(BrickSlot<uint32_t>) == 16 && sizeof(BrickSlot<uint64_t>) == 16, "one 16-byte slot");
 
 template <typename KeyT>
 __device__ __forceinline__ KeyT empty_key() {
@@ -55,18 +67,69 @@ __device__ __forceinline__ uint64_t pack_key(int b, int x, int y, int z, int X, 
          uint64_t(z);
 }
 
+// The key of the brick holding cell (b, x, y, z) of grid (X, Y, Z).  The
+// brick grid has no more cells than the voxel grid, so the key fits the
+// same width and never equals the empty key.
+__device__ __forceinline__ uint64_t brick_key(int b, int x, int y, int z, int X, int Y, int Z) {
+  return pack_key(b, x >> kBrickShift, y >> kBrickShift, z >> kBrickShift, (X + 3) >> kBrickShift,
+                  (Y + 3) >> kBrickShift, (Z + 3) >> kBrickShift);
+}
+// the cell's bit in its brick's occupancy mask
+__device__ __forceinline__ int brick_bit(int x, int y, int z) { return ((x & 3) << 4) | ((y & 3) << 2) | (z & 3); }
+__device__ __forceinline__ bool same_brick(int x0, int y0, int z0, int x1, int y1, int z1) {
+  return ((x0 ^ x1) | (y0 ^ y1) | (z0 ^ z1)) >> kBrickShift == 0;
+}
+
+// The slot of a brick key (and its mask), or the sentinel when absent.
 template <typename KeyT>
-__device__ __forceinline__ uint32_t hash_lookup(const Slot<KeyT>* __restrict__ table, uint64_t capacity,
-                                                KeyT key) {
-  const uint64_t mask = capacity - 1;
-  uint64_t slot = mix_hash(key) & mask;
+__device__ __forceinline__ uint32_t find_brick(const BrickSlot<KeyT>* __restrict__ slots, uint64_t capacity,
+                                               KeyT key, unsigned long long* mask) {
+  const uint64_t cm = capacity - 1;
+  uint64_t slot = mix_hash(key) & cm;
   for (uint64_t probe = 0; probe < capacity; ++probe) {
-    const Slot<KeyT> e = table[slot];
-    if (e.key == key) return e.val;
+    const BrickSlot<KeyT> e = slots[slot];
+    if (e.key == key) {
+      *mask = e.mask;
+      return uint32_t(slot);
+    }
     if (e.key == empty_key<KeyT>()) return kSentinel;
-    slot = (slot + 1) & mask;
+    slot = (slot + 1) & cm;
   }
   return kSentinel;
+}
+
+// The row of cell `bit` of the brick in `slot` with mask m, or the sentinel.
+__device__ __forceinline__ uint32_t brick_row(const uint32_t* __restrict__ base, const uint32_t* __restrict__ rows,
+                                              uint32_t slot, unsigned long long m, int bit) {
+  if (!((m >> bit) & 1ull)) return kSentinel;
+  return rows[base[slot] + uint32_t(__popcll(m & ((1ull << bit) - 1ull)))];
+}
+
+// A built voxel table, as the lookups see it.
+template <typename KeyT>
+struct VoxelTable {
+  const BrickSlot<KeyT>* slots;
+  const uint32_t* base;  // [capacity]: first entry of each occupied brick's rows
+  const uint32_t* rows;  // [n]: voxel rows grouped by brick
+  uint64_t capacity;
+  int X, Y, Z;           // the voxel grid (the brick grid follows from it)
+};
+
+// The table of a plan region whose voxels sit in grid (X, Y, Z).
+template <typename KeyT>
+inline VoxelTable<KeyT> voxel_table(const char* base, const PlanLayout& L, int X, int Y, int Z) {
+  return VoxelTable<KeyT>{reinterpret_cast<const BrickSlot<KeyT>*>(base + L.table),
+                          reinterpret_cast<const uint32_t*>(base + L.bbase),
+                          reinterpret_cast<const uint32_t*>(base + L.brows), L.capacity, X, Y, Z};
+}
+
+// The row of voxel (b, x, y, z) (inside the grid), or the sentinel.
+template <typename KeyT>
+__device__ __forceinline__ uint32_t voxel_lookup(const VoxelTable<KeyT>& t, int b, int x, int y, int z) {
+  unsigned long long m;
+  const uint32_t slot = find_brick<KeyT>(t.slots, t.capacity, KeyT(brick_key(b, x, y, z, t.X, t.Y, t.Z)), &m);
+  if (slot == kSentinel) return kSentinel;
+  return brick_row(t.base, t.rows, slot, m, brick_bit(x, y, z));
 }
 
 // host side: grid limits and the key width a plan uses

@@ -9,21 +9,28 @@
 //
 // Kernels, in launch order:
 //   plan_prepare    header fields, status word, pair counters; the zero row;
-//                   sentinel fill of nmap; empty (all ones) fill of the hash keys
-//   hash_insert     coordinate check, key packing, open-addressing insert with
-//                   atomicCAS on 32- or 64-bit keys; the row index is stored
-//                   in the same slot, so a lookup is one load
-//   probe_half      one lookup per (voxel, offset k < 13), bounds checked per
-//                   axis before a key is packed (no off-grid neighbour can alias
-//                   a real one); a hit j fills nmap[i][k] and its mirror
-//                   nmap[j][26-k]; the centre entry is the row itself
+//                   empty slots (all-ones key, zero mask); the sentinel fill of
+//                   a strided map (the submanifold probe writes every entry)
+//   brick_insert    coordinate check, key packing of the voxel's 4x4x4 brick;
+//                   the workgroup merges its bricks in LDS, then inserts each
+//                   once (open addressing, atomicCAS on 32- or 64-bit keys) and
+//                   ORs the cells' bits into the slot's occupancy mask (a bit
+//                   already set is a duplicate voxel)
+//   brick_count /   the bricks' row ranges and list: one scan over the voxels
+//   brick_base /    that inserted a brick (each allocating popcount(mask)
+//   brick_rows      entries), in voxel order, so deterministic; every voxel
+//                   then writes its row at its brick's base + its cell's rank
+//   probe_bricks    brick by brick: the 3x3x3 bricks around it looked up once,
+//                   then every (voxel, offset k) entry from the neighbour cell's
+//                   place in those bricks; whole map rows are written at once
+//   fill_orphans    rows no brick wrote become all sentinel (only after an error)
 //   row_scan        per row: neighbour mask and 64-bit sort key
 //                   (mask << zbits) | zorder; per block: pair-list histogram
 //   radix_hist /    stable LSD radix sort, 8 bits a pass, wave64 ballots rank
 //   radix_scatter   equal digits; the last pass writes perm and sorted masks;
 //                   with few blocks the scatter sums the block histograms itself
 //                   instead of a device-wide scan
-//   permute_rows    the map in sorted row order (tiles read it contiguously)
+//   permute_rows    the map in sorted row order (strided plans)
 //   pair_scatter    per-offset lists of (i, nmap[i][k]) in increasing i, from the
 //                   row_scan histogram, a device-wide scan and a stable scatter
 //   scan_*          device-wide exclusive scan of uint32 (three kernels)
@@ -163,7 +170,7 @@ void launch_scan(uint32_t* data, int64_t len, uint32_t* tmp, hipStream_t s, cons
 template <typename KeyT>
 __global__ void __launch_bounds__(256) plan_prepare(PlanHeader* h, int64_t n, int B, int X, int Y, int Z,
                                                    int key_bits, int zbits, uint64_t capacity,
-                                                   uint32_t* __restrict__ nmap, Slot<KeyT>* __restrict__ table,
+                                                   uint32_t* __restrict__ nmap, BrickSlot<KeyT>* __restrict__ table,
                                                    uint4* __restrict__ zrow, uint32_t* __restrict__ hzero,
                                                    int64_t hzero_len) {
   if (blockIdx.x == 0) {
@@ -191,67 +198,304 @@ __global__ void __launch_bounds__(256) plan_prepare(PlanHeader* h, int64_t n, in
   const int64_t t0 = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   for (int64_t i = t0; i < int64_t(kZeroRowBytes / 16); i += stride) zrow[i] = make_uint4(0, 0, 0, 0);
   for (int64_t i = t0; i < hzero_len; i += stride) hzero[i] = 0;
-  for (int64_t i = t0; i < n * kV; i += stride) nmap[i] = kSentinel;
-  // whole slots (one aligned 8- or 16-byte store each), the row index zeroed
-  Slot<KeyT> empty{};
+  if (nmap)
+    for (int64_t i = t0; i < n * kV; i += stride) nmap[i] = kSentinel;
+  // whole slots (one aligned 16-byte store each): empty key, empty mask
+  BrickSlot<KeyT> empty{};
   empty.key = empty_key<KeyT>();
   for (int64_t i = t0; i < int64_t(capacity); i += stride) table[i] = empty;
 }
 
-template <typename KeyT>
-__global__ void __launch_bounds__(256) hash_insert(const int4* __restrict__ coords, int64_t n,
-                                                   int B, int X, int Y, int Z,
-                                                   Slot<KeyT>* __restrict__ table, uint64_t capacity,
-                                                   uint32_t* __restrict__ status) {
-  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i >= n) return;
-  const int4 c = coords[i];
-  if (!coord_ok(c.x, c.y, c.z, c.w, B, X, Y, Z)) {
-    atomicOr(status, kBitCoordRange);
-    return;
-  }
-  const KeyT key = KeyT(pack_key(c.x, c.y, c.z, c.w, X, Y, Z));
-  const uint64_t mask = capacity - 1;
-  uint64_t slot = mix_hash(key) & mask;
-  for (uint64_t probe = 0; probe < capacity; ++probe) {
-    KeyT prev = atomicCAS(&table[slot].key, empty_key<KeyT>(), key);
-    if (prev == empty_key<KeyT>()) {
-      table[slot].val = uint32_t(i);
-      return;
-    }
-    if (prev == key) {
-      atomicOr(status, kBitDuplicate);
-      return;
-    }
-    slot = (slot + 1) & mask;
-  }
-  atomicOr(status, kBitHashFull);
+__device__ __forceinline__ unsigned long long cas_key(uint32_t* p, unsigned long long expect,
+                                                     unsigned long long want) {
+  return atomicCAS(p, uint32_t(expect), uint32_t(want));
+}
+__device__ __forceinline__ unsigned long long cas_key(unsigned long long* p, unsigned long long expect,
+                                                     unsigned long long want) {
+  return atomicCAS(p, expect, want);
 }
 
-// One thread per (voxel i, offset k < 13).  nmap[i][k] = j exactly when
-// nmap[j][26-k] = i, so each unordered neighbour pair is looked up once, from
-// the voxel for which its offset lies in the lower half, and both entries are
-// written; every entry no thread writes keeps the sentinel it was filled
-// with.  The centre entry is the row itself.
+// One thread per voxel.  The workgroup first merges its voxels' bricks in a
+// small LDS table (keys, OR of the cell bits), then inserts each distinct
+// brick of the group once into the global table: one CAS and one atomicOr per
+// (group, brick) instead of per voxel.  A cell bit met twice, in the group or
+// already in the global mask, is a duplicate voxel.  The voxel that put a key
+// into the LDS table of the group that created the brick is its creator.
+constexpr int kInsertSlots = 512;  // LDS slots: at most 256 keys, load factor at most 1/2
 template <typename KeyT>
-__global__ void __launch_bounds__(256) probe_half(const int4* __restrict__ coords, int64_t n, int B, int X,
-                                                  int Y, int Z, const Slot<KeyT>* __restrict__ table,
-                                                  uint64_t capacity, uint32_t* __restrict__ nmap) {
-  const int64_t g = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (g >= n * kCentre) return;
-  const int64_t i = g / kCentre;
-  const int k = int(g - i * kCentre);
+__global__ void __launch_bounds__(256) brick_insert(const int4* __restrict__ coords, int64_t n,
+                                                    int B, int X, int Y, int Z,
+                                                    BrickSlot<KeyT>* __restrict__ table, uint64_t capacity,
+                                                    uint32_t* __restrict__ vslot, uint32_t* __restrict__ status) {
+  constexpr unsigned long long kNone = ~0ull;  // no brick key is all ones
+  __shared__ unsigned long long lkey[kInsertSlots];
+  __shared__ unsigned long long lmask[kInsertSlots];
+  __shared__ uint32_t lslot[kInsertSlots];
+  for (int e = threadIdx.x; e < kInsertSlots; e += 256) {
+    lkey[e] = kNone;
+    lmask[e] = 0ull;
+  }
+  __syncthreads();
+  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  const bool in = i < n;
+  const int4 c = in ? coords[i] : make_int4(0, 0, 0, 0);
+  const bool ok = in && coord_ok(c.x, c.y, c.z, c.w, B, X, Y, Z);
+  if (in && !ok) atomicOr(status, kBitCoordRange);
+  int mine = 0;
+  bool first = false, dup = false;
+  if (ok) {
+    const unsigned long long key = brick_key(c.x, c.y, c.z, c.w, X, Y, Z);
+    uint32_t h = mix_hash(KeyT(key)) & uint32_t(kInsertSlots - 1);
+    // at most 256 distinct keys in kInsertSlots slots: the walk ends
+    for (;;) {
+      const unsigned long long was = atomicCAS(&lkey[h], kNone, key);
+      if (was == kNone) {
+        first = true;
+        break;
+      }
+      if (was == key) break;
+      h = (h + 1) & uint32_t(kInsertSlots - 1);
+    }
+    mine = int(h);
+    const unsigned long long bit = 1ull << brick_bit(c.y, c.z, c.w);
+    if (atomicOr(&lmask[h], bit) & bit) dup = true;
+  }
+  __syncthreads();
+  const uint64_t cm = capacity - 1;
+  for (int e = threadIdx.x; e < kInsertSlots; e += 256) {
+    const unsigned long long key = lkey[e];
+    if (key == kNone) continue;
+    uint64_t slot = mix_hash(KeyT(key)) & cm;
+    uint32_t created = 0;
+    uint64_t probe = 0;
+    for (; probe < capacity; ++probe) {
+      const unsigned long long was = cas_key(&table[slot].key, (unsigned long long)empty_key<KeyT>(), key);
+      if (was == (unsigned long long)empty_key<KeyT>()) {
+        created = kCreator;
+        break;
+      }
+      if (was == key) break;
+      slot = (slot + 1) & cm;
+    }
+    if (probe == capacity) {
+      atomicOr(status, kBitHashFull);
+      lslot[e] = kSentinel;
+      continue;
+    }
+    const unsigned long long m = lmask[e];
+    if (atomicOr(&table[slot].mask, m) & m) dup = true;
+    lslot[e] = uint32_t(slot) | created;
+  }
+  __syncthreads();
+  if (dup) atomicOr(status, kBitDuplicate);
+  if (in) {
+    uint32_t v = kSentinel;
+    if (ok) {
+      const uint32_t g = lslot[mine];
+      if (g != kSentinel) v = first ? g : (g & ~kCreator);
+    }
+    vslot[i] = v;
+  }
+}
+
+// Entries a voxel allocates in brows: its brick's voxel count if it inserted
+// the brick, else none.
+template <typename KeyT>
+__device__ __forceinline__ uint32_t brick_alloc(const uint32_t* __restrict__ vslot,
+                                                const BrickSlot<KeyT>* __restrict__ table, int64_t i, int64_t n,
+                                                uint32_t* slot) {
+  const uint32_t v = i < n ? vslot[i] : kSentinel;
+  *slot = v & ~kCreator;
+  if (v == kSentinel || !(v & kCreator)) return 0u;
+  return uint32_t(__popcll(table[v & ~kCreator].mask));
+}
+
+// Per block of kTableBlock voxels: the entries it allocates in brows
+// (bcnt[b]) and the bricks it inserted (bcnt[nb + b]); bcnt[2 nb] = 0, so one
+// exclusive scan over the 2 nb + 1 words gives both prefix sums (the second
+// offset by the total of the first).  Inside a block the two counts share one
+// word (entries in the low 16 bits: at most 256 x 64).
+template <typename KeyT>
+__global__ void __launch_bounds__(kTableBlock) brick_count(const uint32_t* __restrict__ vslot, int64_t n,
+                                                           const BrickSlot<KeyT>* __restrict__ table,
+                                                           uint32_t* __restrict__ bcnt, int64_t nb) {
+  __shared__ uint32_t waves[kTableBlock / 64];
+  uint32_t slot, excl;
+  const uint32_t c = brick_alloc<KeyT>(vslot, table, int64_t(blockIdx.x) * kTableBlock + threadIdx.x, n, &slot);
+  const uint32_t total = block_exclusive_scan(c ? (1u << 16) | c : 0u, waves, &excl);
+  if (threadIdx.x == 0) {
+    bcnt[blockIdx.x] = total & 0xFFFFu;
+    bcnt[nb + blockIdx.x] = total >> 16;
+    if (blockIdx.x == 0) bcnt[2 * nb] = 0;
+  }
+}
+
+// Each inserting voxel: its brick's first entry in brows, and the brick's
+// place in the list of bricks (slot and brick coordinates), both in voxel
+// order.
+template <typename KeyT>
+__global__ void __launch_bounds__(kTableBlock) brick_base(const int4* __restrict__ coords,
+                                                          const uint32_t* __restrict__ vslot, int64_t n,
+                                                          const BrickSlot<KeyT>* __restrict__ table,
+                                                          const uint32_t* __restrict__ bcnt, int64_t nb,
+                                                          uint32_t* __restrict__ bbase, uint32_t* __restrict__ blist,
+                                                          int4* __restrict__ bcoord) {
+  __shared__ uint32_t waves[kTableBlock / 64];
+  uint32_t slot, excl;
+  const int64_t i = int64_t(blockIdx.x) * kTableBlock + threadIdx.x;
+  const uint32_t c = brick_alloc<KeyT>(vslot, table, i, n, &slot);
+  block_exclusive_scan(c ? (1u << 16) | c : 0u, waves, &excl);
+  if (c) {
+    bbase[slot] = bcnt[blockIdx.x] + (excl & 0xFFFFu);
+    const uint32_t id = bcnt[nb + blockIdx.x] - bcnt[nb] + (excl >> 16);
+    blist[id] = slot;
+    const int4 v = coords[i];
+    bcoord[id] = make_int4(v.x, v.y >> kBrickShift, v.z >> kBrickShift, v.w >> kBrickShift);
+  }
+}
+
+// every voxel: its row at its brick's base + the rank of its cell bit
+template <typename KeyT>
+__global__ void __launch_bounds__(256) brick_rows(const int4* __restrict__ coords, const uint32_t* __restrict__ vslot,
+                                                  int64_t n, const BrickSlot<KeyT>* __restrict__ table,
+                                                  const uint32_t* __restrict__ bbase, uint32_t* __restrict__ brows) {
+  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const uint32_t v = vslot[i];
+  if (v == kSentinel) return;
+  const uint32_t slot = v & ~kCreator;
   const int4 c = coords[i];
-  if (!coord_ok(c.x, c.y, c.z, c.w, B, X, Y, Z)) return;
-  if (k == 0) nmap[i * kV + kCentre] = uint32_t(i);
-  const int px = c.y + k / 9 - 1;
-  const int py = c.z + (k / 3) % 3 - 1;
-  const int pz = c.w + k % 3 - 1;
-  if (px < 0 || px >= X || py < 0 || py >= Y || pz < 0 || pz >= Z) return;
-  const uint32_t j = hash_lookup<KeyT>(table, capacity, KeyT(pack_key(c.x, px, py, pz, X, Y, Z)));
-  if (j == kSentinel) return;
-  nmap[i * kV + k] = j;
-  nmap[int64_t(j) * kV + (kV - 1 - k)] = uint32_t(i);
+  const unsigned long long m = table[slot].mask;
+  const int bit = brick_bit(c.y, c.z, c.w);
+  brows[bbase[slot] + uint32_t(__popcll(m & ((1ull << bit) - 1ull)))] = uint32_t(i);
+}
+
+// Position of the q-th set bit (q < popcount(m)) of m.
+__device__ __forceinline__ int nth_set_bit(unsigned long long m, int q) {
+  int pos = 0;
+#pragma unroll
+  for (int w = 32; w >= 1; w >>= 1) {
+    const int c = __popcll(m & ((1ull << w) - 1ull));
+    if (q >= c) {
+      q -= c;
+      m >>= w;
+      pos += w;
+    }
+  }
+  return pos;
+}
+
+// The neighbour map brick by brick.  A wave takes two listed bricks at a time:
+// in each half, lanes 0..26 look up the 3x3x3 bricks around its brick (lane 13
+// is the brick itself) and keep their masks and row bases in registers.  Then
+// the wave walks each brick's items (occupied cell q, offset k), 64 per round
+// and kUnroll rounds at once: the neighbour cell's brick and bit follow from
+// the cell's place in the brick, that brick's mask and base come from the lane
+// holding it, and the row from the grouped rows.  A voxel's 27 entries are
+// written by consecutive lanes, so whole map rows are stored at once and the
+// map needs no fill beforehand.
+constexpr int kProbeUnroll = 4;
+template <typename KeyT>
+__global__ void __launch_bounds__(256) probe_bricks(int X, int Y, int Z, const VoxelTable<KeyT> t,
+                                                    const uint32_t* __restrict__ blist,
+                                                    const int4* __restrict__ bcoord,
+                                                    const uint32_t* __restrict__ bcnt, int64_t nb,
+                                                    uint32_t* __restrict__ nmap) {
+  const int lane = int(__lane_id());
+  const int half = lane >> 5, hl = lane & 31;
+  const int64_t nw = int64_t(gridDim.x) * (blockDim.x / 64);
+  const int64_t nbricks = int64_t(bcnt[2 * nb]) - int64_t(bcnt[nb]);
+  const int BX = (X + 3) >> kBrickShift, BY = (Y + 3) >> kBrickShift, BZ = (Z + 3) >> kBrickShift;
+  const int ox = hl / 9 - 1, oy = (hl / 3) % 3 - 1, oz = hl % 3 - 1;
+  for (int64_t b = 2 * (int64_t(blockIdx.x) * (blockDim.x / 64) + threadIdx.x / 64); b < nbricks; b += 2 * nw) {
+    // set-up of this half's brick
+    const int64_t hb = b + half;
+    unsigned long long nm = 0ull;
+    uint32_t nbase = 0u;
+    if (hb < nbricks && hl < kV) {
+      if (hl == 13) {
+        const uint32_t slot = blist[hb];
+        nm = t.slots[slot].mask;
+        nbase = t.base[slot];
+      } else {
+        const int4 bc = bcoord[hb];
+        const int nx = bc.y + ox, ny = bc.z + oy, nz = bc.w + oz;
+        if (nx >= 0 && nx < BX && ny >= 0 && ny < BY && nz >= 0 && nz < BZ) {
+          unsigned long long m;
+          const uint32_t s =
+              find_brick<KeyT>(t.slots, t.capacity, KeyT(pack_key(bc.x, nx, ny, nz, BX, BY, BZ)), &m);
+          if (s != kSentinel) {
+            nm = m;
+            nbase = t.base[s];
+          }
+        }
+      }
+    }
+    const uint32_t nm_lo = uint32_t(nm), nm_hi = uint32_t(nm >> 32);
+#pragma unroll 1
+    for (int h = 0; h < 2; ++h) {
+      if (b + h >= nbricks) break;
+      const int src = 32 * h;
+      const unsigned long long m0 = (unsigned long long)__shfl(nm_lo, src + 13, 64) |
+                                    ((unsigned long long)__shfl(nm_hi, src + 13, 64) << 32);
+      const uint32_t base0 = __shfl(nbase, src + 13, 64);
+      const int total = __popcll(m0) * kV;
+#pragma unroll 1
+      for (int t0 = 0; t0 < total; t0 += 64 * kProbeUnroll) {
+        uint32_t ri[kProbeUnroll], rj[kProbeUnroll], jok[kProbeUnroll];
+        int kk[kProbeUnroll];
+#pragma unroll
+        for (int u = 0; u < kProbeUnroll; ++u) {
+          const int it = t0 + 64 * u + lane;
+          const int item = it < total ? it : 0;
+          const int q = item / kV, k = item - q * kV;
+          const int cell = nth_set_bit(m0, q);
+          const int nx = (cell >> 4) + k / 9 - 1, ny = ((cell >> 2) & 3) + (k / 3) % 3 - 1, nz = (cell & 3) + k % 3 - 1;
+          // each of nx, ny, nz lies in -1..4: the brick among the 27, then the cell in it
+          const int d = src + ((nx >> 2) + 1) * 9 + ((ny >> 2) + 1) * 3 + ((nz >> 2) + 1);
+          const unsigned long long m = (unsigned long long)__shfl(nm_lo, d, 64) |
+                                       ((unsigned long long)__shfl(nm_hi, d, 64) << 32);
+          const uint32_t nbs = __shfl(nbase, d, 64);
+          const int bit = brick_bit(nx & 3, ny & 3, nz & 3);
+          jok[u] = uint32_t((m >> bit) & 1ull);
+          // both loads unconditional (a present row, or this brick's first one)
+          ri[u] = base0 + uint32_t(q);
+          rj[u] = jok[u] ? nbs + uint32_t(__popcll(m & ((1ull << bit) - 1ull))) : base0;
+          kk[u] = it < total ? k : -1;
+        }
+        uint32_t vi[kProbeUnroll], vj[kProbeUnroll];
+#pragma unroll
+        for (int u = 0; u < kProbeUnroll; ++u) {
+          vi[u] = t.rows[ri[u]];
+          vj[u] = t.rows[rj[u]];
+        }
+#pragma unroll
+        for (int u = 0; u < kProbeUnroll; ++u)
+          if (kk[u] >= 0) nmap[int64_t(vi[u]) * kV + kk[u]] = jok[u] ? vj[u] : kSentinel;
+      }
+    }
+  }
+}
+
+// Rows no brick wrote (coordinates out of range, a full table, the second of
+// two voxels on one cell) become all sentinel.  Runs only when the build
+// flagged such a voxel.
+template <typename KeyT>
+__global__ void __launch_bounds__(256) fill_orphans(const int4* __restrict__ coords, const uint32_t* __restrict__ vslot,
+                                                    int64_t n, const VoxelTable<KeyT> t,
+                                                    const uint32_t* __restrict__ status, uint32_t* __restrict__ nmap) {
+  if ((*status & (kBitCoordRange | kBitDuplicate | kBitHashFull)) == 0u) return;
+  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const uint32_t v = vslot[i];
+  bool orphan = v == kSentinel;
+  if (!orphan) {
+    const uint32_t slot = v & ~kCreator;
+    const int4 c = coords[i];
+    orphan = brick_row(t.base, t.rows, slot, t.slots[slot].mask, brick_bit(c.y, c.z, c.w)) != uint32_t(i);
+  }
+  if (orphan)
+    for (int k = 0; k < kV; ++k) nmap[i * kV + k] = kSentinel;
 }
 
 // Rows of nmap in blocks of kPairRows, read cooperatively through LDS so the
@@ -781,26 +1025,41 @@ void prepare_region(char* base, const PlanLayout& L, int64_t n, int B, int X, in
   const unsigned prep = prep_blocks < 2048 ? prep_blocks : 2048;
   if (kb == 64)
     plan_prepare<uint64_t><<<prep, 256, 0, s>>>(h, n, B, X, Y, Z, kb, zbits, L.capacity, map,
-                                                reinterpret_cast<Slot<uint64_t>*>(base + L.table), zrow, h0,
-                                                h0_len);
+                                                reinterpret_cast<BrickSlot<uint64_t>*>(base + L.table), zrow,
+                                                h0, h0_len);
   else
     plan_prepare<uint32_t><<<prep, 256, 0, s>>>(h, n, B, X, Y, Z, kb, zbits, L.capacity, map,
-                                                reinterpret_cast<Slot<uint32_t>*>(base + L.table), zrow, h0,
-                                                h0_len);
+                                                reinterpret_cast<BrickSlot<uint32_t>*>(base + L.table), zrow,
+                                                h0, h0_len);
+}
+
+template <typename KeyT>
+static void build_table(const int4* c4, int64_t n, int B, int X, int Y, int Z, char* base, const PlanLayout& L,
+                        bool lookups, hipStream_t s) {
+  PlanHeader* h = reinterpret_cast<PlanHeader*>(base + L.header);
+  BrickSlot<KeyT>* table = reinterpret_cast<BrickSlot<KeyT>*>(base + L.table);
+  uint32_t* vslot = reinterpret_cast<uint32_t*>(base + L.vslot);
+  brick_insert<KeyT><<<grid1d(n, 256), 256, 0, s>>>(c4, n, B, X, Y, Z, table, L.capacity, vslot, &h->status_bits);
+  if (!lookups) return;
+  uint32_t* bcnt = reinterpret_cast<uint32_t*>(base + L.bcnt);
+  uint32_t* bbase = reinterpret_cast<uint32_t*>(base + L.bbase);
+  const int64_t nb = (n + kTableBlock - 1) / kTableBlock;
+  brick_count<KeyT><<<unsigned(nb), kTableBlock, 0, s>>>(vslot, n, table, bcnt, nb);
+  launch_scan(bcnt, 2 * nb + 1, reinterpret_cast<uint32_t*>(base + L.scan_tmp), s);
+  brick_base<KeyT><<<unsigned(nb), kTableBlock, 0, s>>>(c4, vslot, n, table, bcnt, nb, bbase,
+                                                        reinterpret_cast<uint32_t*>(base + L.blist),
+                                                        reinterpret_cast<int4*>(base + L.bcoord));
+  brick_rows<KeyT><<<grid1d(n, 256), 256, 0, s>>>(c4, vslot, n, table, bbase,
+                                                  reinterpret_cast<uint32_t*>(base + L.brows));
 }
 
 void insert_coords(const int4* c4, int64_t n, int B, int X, int Y, int Z, int kb, char* base,
-                   const PlanLayout& L, hipStream_t s) {
+                   const PlanLayout& L, bool lookups, hipStream_t s) {
   if (n == 0) return;
-  PlanHeader* h = reinterpret_cast<PlanHeader*>(base + L.header);
   if (kb == 64)
-    hash_insert<uint64_t><<<grid1d(n, 256), 256, 0, s>>>(c4, n, B, X, Y, Z,
-                                                         reinterpret_cast<Slot<uint64_t>*>(base + L.table),
-                                                         L.capacity, &h->status_bits);
+    build_table<uint64_t>(c4, n, B, X, Y, Z, base, L, lookups, s);
   else
-    hash_insert<uint32_t><<<grid1d(n, 256), 256, 0, s>>>(c4, n, B, X, Y, Z,
-                                                         reinterpret_cast<Slot<uint32_t>*>(base + L.table),
-                                                         L.capacity, &h->status_bits);
+    build_table<uint32_t>(c4, n, B, X, Y, Z, base, L, lookups, s);
 }
 
 void order_rows(const int4* c4, const uint32_t* nmap, int64_t n, int B, int X, int Y, int Z, int32_t* perm,
@@ -951,18 +1210,32 @@ extern "C" int ssc_build_neighbor_map(const int32_t* coords, int64_t n, int32_t 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* base = static_cast<char*>(plan);
   (void)hipGetLastError();
-  // header, zero row, first histogram, sentinel fill of nmap, empty table
-  prepare_region(base, L, n, B, X, Y, Z, kb, zbits, n > 0 ? nmap : nullptr, s);
+  // header, zero row, first histogram, empty table (the probe writes every map entry)
+  prepare_region(base, L, n, B, X, Y, Z, kb, zbits, nullptr, s);
   if (n == 0) return hipGetLastError() == hipSuccess ? SSC_OK : SSC_ERR_HIP;
 
   const int4* c4 = reinterpret_cast<const int4*>(coords);
-  insert_coords(c4, n, B, X, Y, Z, kb, base, L, s);
-  if (kb == 64)
-    probe_half<uint64_t><<<grid1d(n * kCentre, 256), 256, 0, s>>>(
-        c4, n, B, X, Y, Z, reinterpret_cast<const Slot<uint64_t>*>(base + L.table), L.capacity, nmap);
-  else
-    probe_half<uint32_t><<<grid1d(n * kCentre, 256), 256, 0, s>>>(
-        c4, n, B, X, Y, Z, reinterpret_cast<const Slot<uint32_t>*>(base + L.table), L.capacity, nmap);
+  insert_coords(c4, n, B, X, Y, Z, kb, base, L, true, s);
+  {
+    PlanHeader* h = reinterpret_cast<PlanHeader*>(base + L.header);
+    const uint32_t* blist = reinterpret_cast<const uint32_t*>(base + L.blist);
+    const int4* bcoord = reinterpret_cast<const int4*>(base + L.bcoord);
+    const uint32_t* bcnt = reinterpret_cast<const uint32_t*>(base + L.bcnt);
+    const uint32_t* vslot = reinterpret_cast<const uint32_t*>(base + L.vslot);
+    const int64_t nb = (n + kTableBlock - 1) / kTableBlock;
+    // two bricks per wave and round: at most one wave per 32 voxels, at most 8192 workgroups of 4 waves
+    const int64_t want = (n + 127) / 128;
+    const unsigned bgrid = unsigned(want < 8192 ? want : 8192);
+    if (kb == 64) {
+      const VoxelTable<uint64_t> t = voxel_table<uint64_t>(base, L, X, Y, Z);
+      probe_bricks<uint64_t><<<bgrid, 256, 0, s>>>(X, Y, Z, t, blist, bcoord, bcnt, nb, nmap);
+      fill_orphans<uint64_t><<<grid1d(n, 256), 256, 0, s>>>(c4, vslot, n, t, &h->status_bits, nmap);
+    } else {
+      const VoxelTable<uint32_t> t = voxel_table<uint32_t>(base, L, X, Y, Z);
+      probe_bricks<uint32_t><<<bgrid, 256, 0, s>>>(X, Y, Z, t, blist, bcoord, bcnt, nb, nmap);
+      fill_orphans<uint32_t><<<grid1d(n, 256), 256, 0, s>>>(c4, vslot, n, t, &h->status_bits, nmap);
+    }
+  }
   order_rows(c4, nmap, n, B, X, Y, Z, perm, base, L, true, true, s);
   if (parts) order_parts(c4, nmap, perm, n, B, X, Y, Z, base, L, s);
   return hipGetLastError() == hipSuccess ? SSC_OK : SSC_ERR_HIP;

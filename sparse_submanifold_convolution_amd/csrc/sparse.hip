@@ -157,8 +157,8 @@ __global__ void __launch_bounds__(256) os_emit(const uint32_t* __restrict__ bits
 template <typename KeyT>
 __global__ void __launch_bounds__(256) sparse_probe(const int4* __restrict__ coords_out, int64_t n_out, int B,
                                                     int Xo, int Yo, int Zo, int X, int Y, int Z, int ks,
-                                                    int stride, int pad, const Slot<KeyT>* __restrict__ table,
-                                                    uint64_t capacity, uint32_t* __restrict__ nmap,
+                                                    int stride, int pad, const VoxelTable<KeyT> table,
+                                                    uint32_t* __restrict__ nmap,
                                                     uint32_t* __restrict__ tmap) {
   const int V = ks * ks * ks;
   const int64_t g = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
@@ -171,7 +171,7 @@ __global__ void __launch_bounds__(256) sparse_probe(const int4* __restrict__ coo
   const int py = c.z * stride - pad + (k / ks) % ks;
   const int pz = c.w * stride - pad + k % ks;
   if (px < 0 || px >= X || py < 0 || py >= Y || pz < 0 || pz >= Z) return;
-  const uint32_t j = hash_lookup<KeyT>(table, capacity, KeyT(pack_key(c.x, px, py, pz, X, Y, Z)));
+  const uint32_t j = voxel_lookup<KeyT>(table, c.x, px, py, pz);
   if (j == kSentinel) return;
   nmap[o * kV + k] = j;
   tmap[int64_t(j) * kV + (kV - 1 - k)] = uint32_t(o);
@@ -327,18 +327,18 @@ extern "C" int ssc_build_sparse_map(const int32_t* coords_in, int64_t n_in, int3
   prepare_region(fb, S.f, n_out, od[0], od[1], od[2], od[3], kb_out, zb_out, n_out > 0 ? nmap : nullptr, s);
   prepare_region(bb, S.b, n_in, B, X, Y, Z, kb_in, zb_in, n_in > 0 ? tmap : nullptr, s);
   // output sites: range and uniqueness checks (their table is not probed); input sites: the probed table
-  insert_coords(co, n_out, od[0], od[1], od[2], od[3], kb_out, fb, S.f, s);
-  insert_coords(ci, n_in, B, X, Y, Z, kb_in, bb, S.b, s);
+  insert_coords(co, n_out, od[0], od[1], od[2], od[3], kb_out, fb, S.f, false, s);
+  insert_coords(ci, n_in, B, X, Y, Z, kb_in, bb, S.b, true, s);
   if (n_out > 0 && n_in > 0) {
     const int V = ks * ks * ks;
     if (kb_in == 64)
       sparse_probe<uint64_t><<<blocks_for(n_out * V, 256), 256, 0, s>>>(
           co, n_out, od[0], od[1], od[2], od[3], X, Y, Z, ks, stride, pad,
-          reinterpret_cast<const Slot<uint64_t>*>(bb + S.b.table), S.b.capacity, nmap, tmap);
+          voxel_table<uint64_t>(bb, S.b, X, Y, Z), nmap, tmap);
     else
       sparse_probe<uint32_t><<<blocks_for(n_out * V, 256), 256, 0, s>>>(
           co, n_out, od[0], od[1], od[2], od[3], X, Y, Z, ks, stride, pad,
-          reinterpret_cast<const Slot<uint32_t>*>(bb + S.b.table), S.b.capacity, nmap, tmap);
+          voxel_table<uint32_t>(bb, S.b, X, Y, Z), nmap, tmap);
   }
   // GEMM order, sorted maps and (forward direction) the pair lists the weight gradient walks
   order_rows(co, nmap, n_out, od[0], od[1], od[2], od[3], perm_out, fb, S.f, true, false, s);

@@ -31,6 +31,8 @@ constexpr int64_t kSortSmallKeys = int64_t(kSortDirectBlocks) * kSortThreads * k
 inline int sort_items_for(int64_t n) { return n <= kSortSmallKeys ? kSortItemsSmall : kSortItems; }
 // pair-list build: rows per workgroup
 constexpr int kPairRows = 256;
+// voxel-table build: voxels per workgroup of the allocation passes
+constexpr int kTableBlock = 256;
 static_assert((kSortThreads * kSortItemsSmall) % kPairRows == 0, "a row_scan block must lie in one sort block");
 // up to this many pair-list blocks, pair_scatter sums the block counts itself
 constexpr int kPairDirectBlocks = 256;
@@ -122,8 +124,14 @@ struct PlanLayout {
   size_t pperm = 0;   // [2][n] i32: original row at each sorted position of the part
   size_t psmask = 0;  // [2][n] u32: the part's 9-bit mask there (bit 9 holds q)
   size_t psnmap = 0;  // [2][n][9] u32: nmap columns 9q..9q+8 in the part's order
-  // build-only scratch
-  size_t table = 0;  // hash slots: {key, row} pairs, 8 bytes (32-bit keys) or 16 (64-bit)
+  // the voxel table (read by the build's probe and by grid sampling) and build-only scratch
+  size_t table = 0;  // [capacity] brick slots: {key, 64-bit occupancy mask}, 16 bytes
+  size_t bbase = 0;  // [capacity] u32: first entry of each occupied brick in brows
+  size_t brows = 0;  // [n] u32: voxel rows grouped by brick, cells in mask-bit order
+  size_t vslot = 0;  // [n] u32: each voxel's brick slot (kCreator set on the voxel that inserted it)
+  size_t bcnt = 0;   // [2 (n / 256 + 1) + 1] u32: entries and bricks of each block of 256 voxels, then their scan
+  size_t blist = 0;  // [n] u32: slot of each occupied brick, in the order of the voxels that inserted them
+  size_t bcoord = 0; // [n] int4: (batch, x / 4, y / 4, z / 4) of each listed brick
   size_t key0 = 0, key1 = 0, val0 = 0, val1 = 0, hist = 0, pcnt = 0, scan_tmp = 0;
   size_t total = 0;
   uint64_t capacity = 0;
@@ -164,16 +172,21 @@ inline PlanLayout plan_layout(int64_t n, int key_bits, bool parts = false) {
     off = align_up(off + bytes, 256);
     return o;
   };
-  // load factor at most 1/4: half of the probes miss, and a miss walks to the next empty slot
-  // (measured on MI355X: 2n -> 4n slots took config 4's plan 3.75 -> 3.66 ms, config 2's 94 -> 90 us;
-  // 1.6n slots, small enough for the 256 MB MALL, took them to 4.68 ms and 117 us)
-  uint64_t want = uint64_t(n) * 4 < 1024 ? 1024 : uint64_t(n) * 4;
+  // a brick slot per voxel at most: load factor at most 1/2 when every voxel has
+  // a brick of its own, far less when bricks hold many voxels
+  uint64_t want = uint64_t(n) * 2 < 1024 ? 1024 : uint64_t(n) * 2;
   L.capacity = uint64_t(1) << ceil_log2_u64(want);
   L.key_bytes = key_bits == 64 ? 8 : 4;
   L.sort_items = sort_items_for(n);
   L.sort_blocks = (n + kSortThreads * L.sort_items - 1) / (kSortThreads * L.sort_items);
   L.pair_blocks = (n + kPairRows - 1) / kPairRows;
-  L.table = take(L.capacity * (L.key_bytes == 8 ? 16 : 8));
+  L.table = take(L.capacity * 16);
+  L.bbase = take(L.capacity * 4);
+  L.brows = take(size_t(n) * 4);
+  L.vslot = take(size_t(n) * 4);
+  L.bcnt = take((2 * (size_t(n) / kTableBlock + 2)) * 4);
+  L.blist = take(size_t(n) * 4);
+  L.bcoord = take(size_t(n) * 16);
   const size_t nkeys = size_t(n) * (parts ? kOwnOrderParts : 1);
   L.key0 = take(nkeys * 8);
   L.key1 = take(nkeys * 8);
@@ -200,6 +213,7 @@ inline PlanLayout plan_layout(int64_t n, int key_bits, bool parts = false) {
     if (pb * 256 + 1 > scan_len) scan_len = pb * 256 + 1;
   }
   if (size_t(L.pair_blocks) * kV + 1 > scan_len) scan_len = size_t(L.pair_blocks) * kV + 1;
+  if (2 * (size_t(n) / kTableBlock + 2) > scan_len) scan_len = 2 * (size_t(n) / kTableBlock + 2);
   L.scan_tmp = take(((scan_len + kScanBlock - 1) / kScanBlock + 1) * 4);
   L.total = off;
   return L;
@@ -217,6 +231,13 @@ inline void sort_key_bits(int32_t B, int32_t X, int32_t Y, int32_t Z, int* axis_
 // Moves a plan layout's build-only scratch by delta bytes (its conv regions stay).
 inline PlanLayout relocate_scratch(PlanLayout L, size_t delta) {
   L.table += delta;
+  L.bbase += delta;
+  L.brows += delta;
+  L.vslot += delta;
+  L.bcnt += delta;
+  L.blist += delta;
+  L.bcoord += delta;
+
   L.key0 += delta;
   L.key1 += delta;
   L.val0 += delta;
@@ -277,9 +298,11 @@ inline SparseLayout sparse_layout(int64_t n_in, int64_t n_out, int kb_in, int kb
 // hash keys of one region
 void prepare_region(char* base, const PlanLayout& L, int64_t n, int B, int X, int Y, int Z, int kb, int zbits,
                     uint32_t* map, hipStream_t s);
-// coordinate check and hash insert of n rows into the region's table
+// coordinate checks and the voxel table of n rows in the region (lookups: also
+// group the rows by brick, which the lookups need; without it only the range
+// and duplicate checks are made)
 void insert_coords(const int4* c4, int64_t n, int B, int X, int Y, int Z, int kb, char* base,
-                   const PlanLayout& L, hipStream_t s);
+                   const PlanLayout& L, bool lookups, hipStream_t s);
 // masks, (mask, z-order) sort -> perm and sorted masks, and (want_pairs) the
 // per-offset pair lists, of a [n][27] map whose rows sit at coords in grid
 // (B, X, Y, Z); centre: every row has its centre offset (a submanifold map),
