@@ -144,7 +144,7 @@ __global__ void __launch_bounds__(kScanThreads) scan_apply(uint32_t* __restrict_
   }
   uint32_t excl;
   block_exclusive_scan(s, waves, &excl);
-  uint32_t run = tmp[blockIdx.x] + excl;
+  uint32_t run = (tmp ? tmp[blockIdx.x] : 0u) + excl;
 #pragma unroll
   for (int e = 0; e < kScanItems; ++e) {
     int64_t idx = base + e;
@@ -156,6 +156,11 @@ __global__ void __launch_bounds__(kScanThreads) scan_apply(uint32_t* __restrict_
 void launch_scan(uint32_t* data, int64_t len, uint32_t* tmp, hipStream_t s, const uint32_t* gate) {
   if (len <= 0) return;
   const int64_t nb = (len + kScanBlock - 1) / kScanBlock;
+  if (nb == 1) {
+    // one workgroup's worth: a single launch with no block offsets
+    scan_apply<<<dim3(1), dim3(kScanThreads), 0, s>>>(data, len, nullptr, gate);
+    return;
+  }
   scan_reduce<<<dim3(unsigned(nb)), dim3(kScanThreads), 0, s>>>(data, len, tmp, gate);
   scan_top<<<dim3(1), dim3(kScanThreads), 0, s>>>(tmp, nb, gate);
   scan_apply<<<dim3(unsigned(nb)), dim3(kScanThreads), 0, s>>>(data, len, tmp, gate);
