@@ -188,6 +188,23 @@ __device__ __forceinline__ void gemm_store(const f32x16 (&acc)[FM][FN], const in
                                            int n0, int N, const T* __restrict__ bias, T* __restrict__ out,
                                            const GemmPart& gp) {
   using E = Elt<T>;
+  if (gp.emode == 0) {
+    // a whole GEMM: bias, round once, scatter rows to perm
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int c = n0 + c0 + j * 32 + (lane & 31);
+      if (c >= N) continue;
+      const float bv = bias ? E::load(bias[c]) : 0.f;
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int32_t p = prow[r0 + i * 32 + acc_row(lane, e)];
+          if (p >= 0) out[int64_t(p) * N + c] = E::store(acc[i][j][e] + bv);
+        }
+    }
+    return;
+  }
   if (gp.emode == 1 || gp.emode == 3) {
     // first or middle part of a split: fp32 sums by original row, no bias
 #pragma unroll
@@ -211,7 +228,7 @@ __device__ __forceinline__ void gemm_store(const f32x16 (&acc)[FM][FN], const in
     }
     return;
   }
-  // bias (and the earlier parts' sums), round once, scatter rows to perm
+  // last part: the earlier parts' sums, the bias, round once, scatter rows to perm
 #pragma unroll
   for (int j = 0; j < FN; ++j) {
     const int c = n0 + c0 + j * 32 + (lane & 31);
@@ -223,7 +240,7 @@ __device__ __forceinline__ void gemm_store(const f32x16 (&acc)[FM][FN], const in
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int32_t p = prow[r0 + i * 32 + acc_row(lane, e)];
-        prev[e] = (gp.emode == 2 && p >= 0) ? gp.pbuf[int64_t(p) * N + c] : 0.f;
+        prev[e] = p >= 0 ? gp.pbuf[int64_t(p) * N + c] : 0.f;
       }
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
@@ -234,7 +251,10 @@ __device__ __forceinline__ void gemm_store(const f32x16 (&acc)[FM][FN], const in
   }
 }
 
-template <typename T, int FM, int FN, int BK, int NWM, int NWN, int DEPTH, int KMAP, int MW>
+// GM: the map rows come from a map in original row order (gp.gmap) through
+// perm, instead of from a sorted-order map; a compile-time choice, so that
+// the sorted-map prologue issues all of its loads in one round trip.
+template <typename T, int FM, int FN, int BK, int NWM, int NWN, int DEPTH, int KMAP, int MW, bool GM>
 __global__ void __launch_bounds__(64 * NWM * NWN)
     igemm(const T* __restrict__ A, const T* __restrict__ Bt, const T* __restrict__ bias, T* __restrict__ out,
           const uint32_t* __restrict__ snmap, const int32_t* __restrict__ perm,
@@ -298,7 +318,7 @@ __global__ void __launch_bounds__(64 * NWM * NWN)
       msk = smask[g] & gp.kmask;
     }
   }
-  if (gp.gmap) {
+  if constexpr (GM) {
     static_assert(MW <= kV, "map rows");
     if (tid < BM) prow[tid] = pr;
     __syncthreads();
@@ -1266,7 +1286,7 @@ static bool channels_ok(int Ci, int Co, int dtype) {
   return Ci > 0 && Co > 0 && Ci % vec == 0 && Co % vec == 0 && Ci <= 4096 && Co <= 4096;
 }
 
-template <typename T, int MW, int FM, int FN, int BK, int NWM, int NWN, int DEPTH, int KMAP>
+template <typename T, int MW, int FM, int FN, int BK, int NWM, int NWN, int DEPTH, int KMAP, bool GM>
 static void igemm_go(const T* A, const T* Bt, const T* bias, T* out, const uint32_t* nmap, const int32_t* perm,
                      const uint32_t* smask, const T* zrow, int64_t n, int K, int N, int flip, float* partial,
                      hipStream_t s, const GemmPart& gp) {
@@ -1276,7 +1296,7 @@ static void igemm_go(const T* A, const T* Bt, const T* bias, T* out, const uint3
   const int nsplit = split_parts(n, N);
   const int tgroup = nblk * nsplit == 1 ? kTileGroup : 1;
   const unsigned grid = xcd_group_grid((ntiles + tgroup - 1) / tgroup, tgroup * nblk * nsplit);
-  igemm<T, FM, FN, BK, NWM, NWN, DEPTH, KMAP, MW><<<grid, 64 * NWM * NWN, 0, s>>>(
+  igemm<T, FM, FN, BK, NWM, NWN, DEPTH, KMAP, MW, GM><<<grid, 64 * NWM * NWN, 0, s>>>(
       A, Bt, bias, out, nmap, perm, smask, zrow, n, K, N, flip, ntiles, nblk, nsplit, partial, tgroup, gp);
   if (nsplit > 1)
     split_reduce<T><<<unsigned((n * N + 255) / 256), 256, 0, s>>>(partial, nsplit, n, N, bias, perm, out);
@@ -1289,14 +1309,15 @@ static void igemm_go(const T* A, const T* Bt, const T* bias, T* out, const uint3
 // workgroups) otherwise.  With 8 waves and a reduction of at most 128 (at most
 // two stages per offset, so the gathers dominate) the rows are gathered whole
 // (KMAP 2); wider reductions keep the register-only natural order.
-template <typename T, int MW, int FN>
+template <typename T, int MW, int FN, bool GM>
 static void igemm_pick_rows(const T* A, const T* Bt, const T* bias, T* out, const uint32_t* nmap,
                             const int32_t* perm, const uint32_t* smask, const T* zrow, int64_t n, int K, int N,
                             int flip, float* partial, hipStream_t s, const GemmPart& gp) {
   const int64_t nblk = (N + FN * 32 - 1) / (FN * 32);
   const int64_t wg256 = (n + 255) / 256 * nblk, wg128 = (n + 127) / 128 * nblk;
 #define SSC_GO(NW, BK, DEPTH, KMAP) \
-  igemm_go<T, MW, 1, FN, BK, NW, 1, DEPTH, KMAP>(A, Bt, bias, out, nmap, perm, smask, zrow, n, K, N, flip, partial, s, \
+  igemm_go<T, MW, 1, FN, BK, NW, 1, DEPTH, KMAP, GM>(A, Bt, bias, out, nmap, perm, smask, zrow, n, K, N, flip, partial, \
+                                                     s, \
                                                  gp)
 #define SSC_BK(NW, DEPTH)                                                 \
   do {                                                                    \
@@ -1329,21 +1350,25 @@ static void igemm_pick_rows(const T* A, const T* Bt, const T* bias, T* out, cons
 
 // MW: columns of the sorted-order map rows (27, or 8 for the compact map of a
 // 2x2x2 strided kernel); with flip the weight of column c is W[MW - 1 - c].
-template <typename T, int MW>
+template <typename T, int MW, bool GM>
 static void launch_igemm(const T* A, const T* Bt, const T* bias, T* out, const uint32_t* nmap,
                          const int32_t* perm, const uint32_t* smask, const T* zrow, int64_t n, int K, int N,
                          int flip, float* partial, hipStream_t s, const uint32_t* gmap) {
   // every offset, one row order; with flip, column c meets W[MW - 1 - c]
   const GemmPart gp{nullptr, 0, ~0u, 0, MW - 1, 0, nullptr, gmap};
-  if (N > 128) igemm_pick_rows<T, MW, 8>(A, Bt, bias, out, nmap, perm, smask, zrow, n, K, N, flip, partial, s, gp);
-  else if (N > 64) igemm_pick_rows<T, MW, 4>(A, Bt, bias, out, nmap, perm, smask, zrow, n, K, N, flip, partial, s, gp);
-  else if (N > 32) igemm_pick_rows<T, MW, 2>(A, Bt, bias, out, nmap, perm, smask, zrow, n, K, N, flip, partial, s, gp);
-  else igemm_pick_rows<T, MW, 1>(A, Bt, bias, out, nmap, perm, smask, zrow, n, K, N, flip, partial, s, gp);
+  if (N > 128)
+    igemm_pick_rows<T, MW, 8, GM>(A, Bt, bias, out, nmap, perm, smask, zrow, n, K, N, flip, partial, s, gp);
+  else if (N > 64)
+    igemm_pick_rows<T, MW, 4, GM>(A, Bt, bias, out, nmap, perm, smask, zrow, n, K, N, flip, partial, s, gp);
+  else if (N > 32)
+    igemm_pick_rows<T, MW, 2, GM>(A, Bt, bias, out, nmap, perm, smask, zrow, n, K, N, flip, partial, s, gp);
+  else
+    igemm_pick_rows<T, MW, 1, GM>(A, Bt, bias, out, nmap, perm, smask, zrow, n, K, N, flip, partial, s, gp);
 }
 
 // One gated part of a possibly split GEMM: wide layers only (parts_possible),
 // so always 8 waves of 32 rows and 256 channels.
-template <typename T, int MW>
+template <typename T, int MW, bool GM>
 static void igemm_part_go(const T* A, const T* Bt, const T* bias, T* out, const uint32_t* nmap, const int32_t* perm,
                           const uint32_t* smask, const T* zrow, int64_t n, int K, int N, int flip, hipStream_t s,
                           const GemmPart& gp) {
@@ -1353,11 +1378,14 @@ static void igemm_part_go(const T* A, const T* Bt, const T* bias, T* out, const 
   // random occupancy: 16.9 ms against 17.4 ms per input-gradient pass).
   if constexpr (sizeof(T) == 2) {
     if (K % 64 == 0)
-      igemm_go<T, MW, 1, 8, 64, 8, 1, 1, 1>(A, Bt, bias, out, nmap, perm, smask, zrow, n, K, N, flip, nullptr, s, gp);
+      igemm_go<T, MW, 1, 8, 64, 8, 1, 1, 1, GM>(A, Bt, bias, out, nmap, perm, smask, zrow, n, K, N, flip, nullptr, s,
+                                                gp);
     else if (K % 32 == 0)
-      igemm_go<T, MW, 1, 8, 32, 8, 1, 1, 1>(A, Bt, bias, out, nmap, perm, smask, zrow, n, K, N, flip, nullptr, s, gp);
+      igemm_go<T, MW, 1, 8, 32, 8, 1, 1, 1, GM>(A, Bt, bias, out, nmap, perm, smask, zrow, n, K, N, flip, nullptr, s,
+                                                gp);
     else
-      igemm_go<T, MW, 1, 8, 16, 8, 1, 1, 1>(A, Bt, bias, out, nmap, perm, smask, zrow, n, K, N, flip, nullptr, s, gp);
+      igemm_go<T, MW, 1, 8, 16, 8, 1, 1, 1, GM>(A, Bt, bias, out, nmap, perm, smask, zrow, n, K, N, flip, nullptr, s,
+                                                gp);
   }
 }
 
@@ -1376,13 +1404,13 @@ static void launch_igemm_split(const T* A, const T* Bt, const T* bias, T* out, c
   const uint32_t* snmap = reinterpret_cast<const uint32_t*>(region + L.snmap);
   const uint32_t* smask = reinterpret_cast<const uint32_t*>(region + L.smask);
   const T* zrow = reinterpret_cast<const T*>(region + L.zrow);
-  igemm_part_go<T, kV>(A, Bt, bias, out, snmap, perm, smask, zrow, n, K, N, flip, s,
-                       GemmPart{h, 2, ~0u, 0, kV - 1, 0, nullptr, gmap});
-  igemm_part_go<T, kV>(A, Bt, bias, out, snmap, perm, smask, zrow, n, K, N, flip, s,
-                       GemmPart{h, 1, kTopPartMask, 0, kV - 1, 1, pbuf, gmap});
+  igemm_part_go<T, kV, true>(A, Bt, bias, out, snmap, perm, smask, zrow, n, K, N, flip, s,
+                             GemmPart{h, 2, ~0u, 0, kV - 1, 0, nullptr, gmap});
+  igemm_part_go<T, kV, true>(A, Bt, bias, out, snmap, perm, smask, zrow, n, K, N, flip, s,
+                             GemmPart{h, 1, kTopPartMask, 0, kV - 1, 1, pbuf, gmap});
   for (int q = kOwnOrderParts - 1; q >= 0; --q) {
     const int lo = q * kPartCols;
-    igemm_part_go<T, kPartCols>(A, Bt, bias, out,
+    igemm_part_go<T, kPartCols, false>(A, Bt, bias, out,
                                 reinterpret_cast<const uint32_t*>(region + L.psnmap) + int64_t(q) * n * kPartCols,
                                 reinterpret_cast<const int32_t*>(region + L.pperm) + int64_t(q) * n,
                                 reinterpret_cast<const uint32_t*>(region + L.psmask) + int64_t(q) * n, zrow, n, K, N,
@@ -1395,9 +1423,12 @@ static void launch_igemm_w(int mw, const T* A, const T* Bt, const T* bias, T* ou
                            const int32_t* perm, const uint32_t* smask, const T* zrow, int64_t n, int K, int N,
                            int flip, float* partial, hipStream_t s, const uint32_t* gmap) {
   if (mw == kCompactCols)
-    launch_igemm<T, kCompactCols>(A, Bt, bias, out, nmap, perm, smask, zrow, n, K, N, flip, partial, s, nullptr);
+    launch_igemm<T, kCompactCols, false>(A, Bt, bias, out, nmap, perm, smask, zrow, n, K, N, flip, partial, s,
+                                         nullptr);
+  else if (gmap)
+    launch_igemm<T, kV, true>(A, Bt, bias, out, nmap, perm, smask, zrow, n, K, N, flip, partial, s, gmap);
   else
-    launch_igemm<T, kV>(A, Bt, bias, out, nmap, perm, smask, zrow, n, K, N, flip, partial, s, gmap);
+    launch_igemm<T, kV, false>(A, Bt, bias, out, nmap, perm, smask, zrow, n, K, N, flip, partial, s, nullptr);
 }
 
 // dbias stage 1 geometry: column vectors (16 bytes) per work item, all of them
