@@ -183,6 +183,36 @@ struct GemmPart {
 // Epilogue of a GEMM tile (see GemmPart): each wave holds FM x FN 32x32
 // accumulator blocks for tile rows r0.. and channels n0 + c0..; prow maps tile
 // rows to original rows (-1 past the end).
+// Whole-GEMM epilogue of 16-bit layers through LDS: a wave rounds one 32 x 32
+// block of its outputs (with the bias) into its own 2 KB of LDS, then writes
+// the block's rows as 16-byte vectors, four lanes a row: two store
+// instructions per block instead of sixteen two-byte ones.  `stage` is the
+// wave's 2 KB, free to overwrite (the caller has passed a workgroup barrier).
+// The wave's LDS writes and reads complete in program order.
+template <typename T, int FN>
+__device__ __forceinline__ void gemm_store_rows(const f32x16 (&acc)[1][FN], const int32_t* prow, int r0, int lane,
+                                                int n0, int N, const T* __restrict__ bias, T* __restrict__ out,
+                                                T* stage) {
+  using E = Elt<T>;
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    const int cb = n0 + j * 32;  // the block's first column
+    if (cb >= N) break;
+    const int c = cb + (lane & 31);
+    const float bv = (bias && c < N) ? E::load(bias[c]) : 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) stage[acc_row(lane, e) * 32 + (lane & 31)] = E::store(acc[0][j][e] + bv);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int idx = q * 64 + lane, row = idx >> 2, cv = idx & 3;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(stage + row * 32 + cv * 8);
+      const int32_t p = prow[r0 + row];
+      const int col = cb + cv * 8;
+      if (p >= 0 && col < N) *reinterpret_cast<u32x4*>(out + int64_t(p) * N + col) = v;
+    }
+  }
+}
+
 template <typename T, int FM, int FN>
 __device__ __forceinline__ void gemm_store(const f32x16 (&acc)[FM][FN], const int32_t* prow, int r0, int c0, int lane,
                                            int n0, int N, const T* __restrict__ bias, T* __restrict__ out,
@@ -569,6 +599,13 @@ __global__ void __launch_bounds__(64 * NWM * NWN)
     return;
   }
 
+  if constexpr (sizeof(T) == 2 && FM == 1 && NWN == 1 && 2 * C::kLdsB >= size_t(NWM) * 2048) {
+    if (gp.emode == 0) {
+      __syncthreads();  // every wave is past its last stage: the weight buffers are free
+      gemm_store_rows<T, FN>(acc, prow, wm * 32, lane, n0, N, bias, out, reinterpret_cast<T*>(lds_b) + wave * 1024);
+      return;
+    }
+  }
   gemm_store<T, FM, FN>(acc, prow, wm * FM * 32, wn * FN * 32, lane, n0, N, bias, out, gp);
 }
 

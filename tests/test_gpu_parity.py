@@ -146,6 +146,37 @@ def test_device_errors_are_reported(ssc):
     assert e.value.code == 5
 
 
+def test_failed_build_map_stays_valid(ssc):
+    """After a device-detected error (duplicate voxels, coordinates out of range) the build still
+    writes every map entry, as a row index or the sentinel, and perm is still a permutation, so a
+    caller that ignores the status reads no index past the rows.  The map starts out filled with
+    an invalid index, so an entry the build skipped would show."""
+    from sparse_submanifold_convolution_amd import binding as b
+    rng = np.random.default_rng(5)
+    shape = (1, 24, 24, 24)
+    cells = rng.choice(24 ** 3, 3000, replace=False)
+    c = np.stack([np.zeros_like(cells), cells // 576, (cells // 24) % 24, cells % 24], 1).astype(np.int32)
+    dup = np.concatenate([c, c[rng.choice(len(c), 50, replace=False)]])
+    bad = c.copy()
+    bad[::97, 1] = 30
+    for coords, code in ((dup, 6), (bad, 5)):
+        t = torch.from_numpy(coords).to(DEV)
+        n = int(t.shape[0])
+        nb = b.plan_bytes(n, shape, 0)
+        buf = torch.empty(nb, dtype=torch.uint8, device=DEV)
+        nmap = torch.full((n, 27), 0x7FFFFFF0, dtype=torch.int32, device=DEV)
+        perm = torch.empty(n, dtype=torch.int32, device=DEV)
+        rc = b.lib().ssc_build_neighbor_map(b._ptr(t), n, *shape, 0, b._ptr(nmap), b._ptr(perm), b._ptr(buf), nb,
+                                           b._stream(DEV))
+        assert rc == 0
+        st = ssc.plan_status(b.Plan(nmap, perm, buf, n, shape, 0))
+        print(f"[case] failed build n={n} status={st}", flush=True)
+        assert st == code
+        m = _u32(nmap)
+        assert ((m == O.SENTINEL) | (m < n)).all()
+        assert np.array_equal(np.sort(perm.cpu().numpy()), np.arange(n))
+
+
 # ---------------------------------------------------------------------------
 # floats: small cases, every element
 # ---------------------------------------------------------------------------
