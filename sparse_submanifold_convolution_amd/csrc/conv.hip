@@ -213,6 +213,56 @@ __device__ __forceinline__ void gemm_store_rows(const f32x16 (&acc)[1][FN], cons
   }
 }
 
+// The same for the offset parts of a split GEMM: a wave stages one 32 x 32
+// block of fp32 sums in its own 4 KB of LDS, then moves the block's rows as
+// 16-byte vectors of four sums, eight lanes a row: the first part writes its
+// sums, the middle part adds them to the handed-over sums, the last adds
+// them, the bias (in that order, as the direct epilogue does) and rounds.
+template <typename T, int FN>
+__device__ __forceinline__ void gemm_store_parts(const f32x16 (&acc)[1][FN], const int32_t* prow, int r0, int lane,
+                                                 int n0, int N, const T* __restrict__ bias, T* __restrict__ out,
+                                                 const GemmPart& gp, float* stage) {
+  using E = Elt<T>;
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  // a lane always moves the same four columns of a block (lane % 8)
+  const int cv = lane & 7;
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    const int cb = n0 + j * 32;
+    if (cb >= N) break;
+    const int col = cb + cv * 4;
+    float bv[4] = {0.f, 0.f, 0.f, 0.f};
+    if (gp.emode == 2 && bias && col < N) {
+      const uint2 braw = *reinterpret_cast<const uint2*>(bias + col);
+      const T* bt = reinterpret_cast<const T*>(&braw);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) bv[u] = E::load(bt[u]);
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) stage[acc_row(lane, e) * 32 + (lane & 31)] = acc[0][j][e];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int row = (q * 64 + lane) >> 3;
+      const f32x4 v = *reinterpret_cast<const f32x4*>(stage + row * 32 + cv * 4);
+      const int32_t p = prow[r0 + row];
+      if (p < 0 || col >= N) continue;
+      f32x4* pb = reinterpret_cast<f32x4*>(gp.pbuf + int64_t(p) * N + col);
+      if (gp.emode == 1) {
+        *pb = v;
+      } else if (gp.emode == 3) {
+        const f32x4 o = *pb;
+        *pb = o + v;
+      } else {
+        const f32x4 o = *pb;
+        T r[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) r[u] = E::store(v[u] + o[u] + bv[u]);
+        *reinterpret_cast<uint2*>(out + int64_t(p) * N + col) = *reinterpret_cast<const uint2*>(r);
+      }
+    }
+  }
+}
+
 template <typename T, int FM, int FN>
 __device__ __forceinline__ void gemm_store(const f32x16 (&acc)[FM][FN], const int32_t* prow, int r0, int c0, int lane,
                                            int n0, int N, const T* __restrict__ bias, T* __restrict__ out,
@@ -599,11 +649,22 @@ __global__ void __launch_bounds__(64 * NWM * NWN)
     return;
   }
 
-  if constexpr (sizeof(T) == 2 && FM == 1 && NWN == 1 && 2 * C::kLdsB >= size_t(NWM) * 2048) {
-    if (gp.emode == 0) {
-      __syncthreads();  // every wave is past its last stage: the weight buffers are free
-      gemm_store_rows<T, FN>(acc, prow, wm * 32, lane, n0, N, bias, out, reinterpret_cast<T*>(lds_b) + wave * 1024);
-      return;
+  if constexpr (sizeof(T) == 2 && FM == 1 && NWN == 1) {
+    // every wave is past its last stage (barrier below): the weight buffers are free
+    if constexpr (2 * C::kLdsB >= size_t(NWM) * 2048) {
+      if (gp.emode == 0) {
+        __syncthreads();
+        gemm_store_rows<T, FN>(acc, prow, wm * 32, lane, n0, N, bias, out, reinterpret_cast<T*>(lds_b) + wave * 1024);
+        return;
+      }
+    }
+    if constexpr (2 * C::kLdsB >= size_t(NWM) * 4096) {
+      if (gp.emode != 0) {
+        __syncthreads();
+        gemm_store_parts<T, FN>(acc, prow, wm * 32, lane, n0, N, bias, out, gp,
+                                reinterpret_cast<float*>(lds_b) + wave * 1024);
+        return;
+      }
     }
   }
   gemm_store<T, FM, FN>(acc, prow, wm * FM * 32, wn * FN * 32, lane, n0, N, bias, out, gp);
