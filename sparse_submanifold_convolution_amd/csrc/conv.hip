@@ -557,7 +557,7 @@ __global__ void __launch_bounds__(64 * NWM * NWN)
 #pragma unroll
     for (int v = 0; v < C::kBV; ++v) {
       const int idx = tid + v * NT;
-      if (idx < BN * VPR) {
+      if (C::kBV * NT == BN * VPR || idx < BN * VPR) {
         const int r = idx / VPR, cv = idx % VPR;
         *reinterpret_cast<u32x4*>(sb + r * C::kLd + cv * C::kVec) = rb[v];
       }
@@ -604,17 +604,90 @@ __global__ void __launch_bounds__(64 * NWM * NWN)
     if constexpr (KMAP == 2) __builtin_amdgcn_wave_barrier();
   };
 
+  // One stage of prefetch in the natural order: the gathered piece of MFMA
+  // step q is reloaded for the next stage right after that step's MFMAs, so
+  // each gather has most of a stage to arrive (with a whole-stage refill it
+  // would be issued after the last MFMA and awaited right after the next
+  // barrier) and the ring costs no more registers.
+  constexpr bool kRoll = DEPTH == 1 && KMAP == 1 && FM == 1 && sizeof(T) == 2 && !RAG && C::kSteps == NV;
+
+  // the row pieces of the gather cursor's stage (the zero row past the last
+  // stage); advances the cursor
+  auto a_src = [&]() {
+    const int64_t zoff = reinterpret_cast<const char*>(zrow) - reinterpret_cast<const char*>(A);
+    const uint32_t live = a_rem != 0 ? ~0u : 0u;
+    const uint32_t j = jtab[(wm * 32 + (lane & 31)) * MW + a_k] | ~live;
+    const int64_t off = j != kSentinel ? (int64_t(j) * K + a_ks * BK + half * C::kVec) * int64_t(sizeof(T)) : zoff;
+    advance(a_rem, a_k, a_ks);
+    return reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(A) + off);
+  };
+
   // prologue loads: both operands DEPTH stages deep
 #pragma unroll
-  for (int d = 0; d < DEPTH; ++d) {
+  for (int d = 0; !kRoll && d < DEPTH; ++d) {
     load_a(abuf[d]);
     load_b(bbuf[d]);
+  }
+
+  if constexpr (kRoll) {
+    // Stage s: barrier (B(s) is in LDS and every wave is past stage s - 1),
+    // B(s + 1) loads, the MFMAs of stage s with A(s + 1) loads between
+    // their steps, then B(s + 1) to the other LDS buffer.  The weight slice
+    // gets a whole stage to arrive, and each wait sees the same loads in
+    // flight on every path into it.
+    load_b(bbuf[0]);
+    {
+      const u32x4* src = a_src();
+#pragma unroll
+      for (int q = 0; q < C::kSteps; ++q) {
+        abuf[0][q] = src[2 * q];
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    store_b(0, bbuf[0]);
+    for (int s = 0; s < nstages; ++s) {
+      const int buf = s & 1;
+      __syncthreads();
+      load_b(bbuf[0]);
+      const u32x4* src = a_src();  // the next stage's pieces
+      // A wave whose rows all lack the stage's offset skips its MFMAs.  The
+      // skip tests sit around each step's LDS reads and MFMAs only; the
+      // gathers between them are issued on every path, so the compiler sees
+      // one sequence of loads and waits only for the pieces each step needs.
+      const bool run = (wuni >> c_k) & 1u;
+      const T* sb = reinterpret_cast<const T*>(lds_b + buf * C::kLdsB);
+      auto read_b = [&](frag_t (&bfr)[FN], int q) {
+#pragma unroll
+        for (int jn = 0; jn < FN; ++jn)
+          bfr[jn] = *reinterpret_cast<const frag_t*>(sb + ((wn * FN + jn) * 32 + (lane & 31)) * C::kLd +
+                                                     (2 * q + half) * E::kFrag);
+      };
+      frag_t bcur[FN], bnext[FN];
+      if (run) read_b(bcur, 0);
+#pragma unroll
+      for (int q = 0; q < C::kSteps; ++q) {
+        if (run) {
+          if (q + 1 < C::kSteps) read_b(bnext, q + 1);
+          const frag_t af = __builtin_bit_cast(frag_t, abuf[0][q]);
+#pragma unroll
+          for (int jn = 0; jn < FN; ++jn) acc[0][jn] = E::mfma(af, bcur[jn], acc[0][jn]);
+        }
+        abuf[0][q] = src[2 * q];
+        // keep the refill here: the scheduler would otherwise move it after
+        // the last MFMA
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int jn = 0; jn < FN; ++jn) bcur[jn] = bnext[jn];
+      }
+      advance(c_rem, c_k, c_ks);
+      store_b(buf ^ 1, bbuf[0]);
+    }
   }
 
   // Each stage refills its ring slot DEPTH stages ahead.  Only the LDS store,
   // the barrier and the MFMAs depend on the (uniform) stage bound; the loads
   // are issued on every path.
-  for (int s0 = 0; s0 < nstages; s0 += DEPTH) {
+  for (int s0 = 0; !kRoll && s0 < nstages; s0 += DEPTH) {
 #pragma unroll
     for (int d = 0; d < DEPTH; ++d) {
       const int s = s0 + d;
