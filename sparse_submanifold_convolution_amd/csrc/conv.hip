@@ -662,22 +662,20 @@ __global__ void __launch_bounds__(64 * NWM * NWN)
           bfr[jn] = *reinterpret_cast<const frag_t*>(sb + ((wn * FN + jn) * 32 + (lane & 31)) * C::kLd +
                                                      (2 * q + half) * E::kFrag);
       };
-      frag_t bcur[FN], bnext[FN];
-      if (run) read_b(bcur, 0);
+      frag_t bfr[2][FN];  // this step's weight fragments and the next step's
+      if (run) read_b(bfr[0], 0);
 #pragma unroll
       for (int q = 0; q < C::kSteps; ++q) {
         if (run) {
-          if (q + 1 < C::kSteps) read_b(bnext, q + 1);
+          if (q + 1 < C::kSteps) read_b(bfr[(q + 1) & 1], q + 1);
           const frag_t af = __builtin_bit_cast(frag_t, abuf[0][q]);
 #pragma unroll
-          for (int jn = 0; jn < FN; ++jn) acc[0][jn] = E::mfma(af, bcur[jn], acc[0][jn]);
+          for (int jn = 0; jn < FN; ++jn) acc[0][jn] = E::mfma(af, bfr[q & 1][jn], acc[0][jn]);
         }
         abuf[0][q] = src[2 * q];
         // keep the refill here: the scheduler would otherwise move it after
         // the last MFMA
         __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int jn = 0; jn < FN; ++jn) bcur[jn] = bnext[jn];
       }
       advance(c_rem, c_k, c_ks);
       store_b(buf ^ 1, bbuf[0]);
@@ -1217,7 +1215,7 @@ __global__ void __launch_bounds__(64 * NWM * NWN)
 #pragma unroll
     for (int v = 0; v < C::kIA; ++v) {
       const int idx = tid + v * NT;
-      if (idx < C::kItemsA) {
+      if (C::kIA * NT == C::kItemsA || idx < C::kItemsA) {
         const int r = idx / (BM / 8), cv = idx % (BM / 8);
         *reinterpret_cast<u32x4*>(sa + (size_t(r) * C::kLdA + cv * 8) * 2) = da[v];
       }
@@ -1225,7 +1223,7 @@ __global__ void __launch_bounds__(64 * NWM * NWN)
 #pragma unroll
     for (int v = 0; v < C::kIB; ++v) {
       const int idx = tid + v * NT;
-      if (idx < C::kItemsB) {
+      if (C::kIB * NT == C::kItemsB || idx < C::kItemsB) {
         const int r = idx / (BN / 8), cv = idx % (BN / 8);
         *reinterpret_cast<u32x4*>(sb + (size_t(r) * C::kLdB + cv * 8) * 2) = db[v];
       }
