@@ -252,6 +252,8 @@ SPLIT = [
     (62, 2, (64, 60, 64), 0.35, 256, 320, "f16", False, 3),
     (63, 1, (52, 52, 52), 1.0, 256, 256, "bf16", False, 1),
     (64, 1, (80, 80, 80), 0.3, 64, 264, "f16", False, 3),
+    # a reduction of 288 takes 32-wide slices in the forward parts
+    (65, 1, (80, 80, 80), 0.3, 288, 256, "bf16", False, 3),
 ]
 
 
